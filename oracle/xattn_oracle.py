@@ -1,0 +1,308 @@
+"""CPU oracle for XAttention-style block-sparse prefill attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import this module:
+only the tests, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` use it. It shares no code, constant or helper with the HIP library.
+
+Plain NumPy in float64. Inputs (bf16 values carried in float32, or float32) are
+upcast exactly. Every step is written the way the pages describe it, with no
+blocking or fusion beyond processing one query-block row at a time so memory
+stays O(block * M).
+
+Sources (page title, section):
+  [XA-abs]  "XAttention: Block Sparse Attention with Antidiagonal Scoring",
+            arXiv abstract as shown on fugumt.com (2503.16428v1).
+  [XA-sum]  "XAttention: Block Sparse Attention with Antidiagonal Scoring",
+            AI-written summary on atlas.scime.ai: sections "Approach",
+            "Key results", "Limitations".
+  [DuSA]    "DuSA: Fast and Accurate Dual-Stage Sparse Attention Mechanism
+            Accelerating Both Training and Inference", rebuttal on paperhub.cn,
+            section "Response to Q2" (the reshape formulation of XAttention).
+  [Flex]    "FlexPrefill: A Context-Aware Sparse Attention Mechanism for
+            Efficient Long-Sequence Inference", rebuttal on paperhub.cn,
+            section "R Q3" (minimal |S| under a cumulative-mass constraint).
+
+Notation: Q is (B, Hq, M, C); K, V are (B, Hkv, M, C); query head h reads KV
+head h // (Hq // Hkv). Block size Bk, stride S, r = Bk // S strided rows per
+block, NB = M // Bk blocks, R = M // S strided rows.
+
+Readings taken where the pages are silent (each one is listed in the design doc):
+  * score temperature: the caller passes ``score_scale`` explicitly;
+  * the antidiagonal pairs query row i*S+s with key row j*S+S-1-s;
+  * causal masking of the strided scores is at the strided level (j <= i);
+  * softmax runs over keys for each strided query row, before the block sum;
+  * block scores are divided by r so each query-block row sums to 1;
+  * ties in the sort are broken by ascending block index;
+  * tau >= 1 keeps every candidate; the diagonal block is always added after
+    the threshold cut;
+  * sparse attention is exact softmax attention renormalised over the
+    selected keys only.
+
+Pins: every function here is checked in tests/test_oracle_pins.py against
+something other than itself (brute force, closed forms, library routines).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "strided_query_rows",
+    "reversed_key_rows",
+    "strided_logits",
+    "block_score_row",
+    "block_scores",
+    "minimal_set",
+    "select_row",
+    "select",
+    "mask_to_index",
+    "attend_row",
+    "attend",
+    "dense",
+    "prefill",
+    "density",
+]
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _kv_head(h: int, hq: int, hkv: int) -> int:
+    # GQA: consecutive query heads share one KV head.
+    if hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return h // (hq // hkv)
+
+
+# ---------------------------------------------------------------------------
+# Stage 1: strided antidiagonal scoring.
+# [DuSA] Response to Q2: Q and K of shape (B, H, M, C) are reshaped to
+# (B, H, M // stride, stride * C) and an attention is computed on them.
+# [XA-abs]: the antidiagonal runs from the lower-left to the upper-right
+# corner of each stride x stride tile, so query row i*S + s meets key row
+# j*S + (S - 1 - s). Reversing the S key rows inside each stride group before
+# the reshape turns the reshape-matmul into exactly that antidiagonal sum.
+# ---------------------------------------------------------------------------
+
+def strided_query_rows(qh: np.ndarray, stride: int) -> np.ndarray:
+    """Q' (R, S*C): row i concatenates q[i*S], ..., q[i*S+S-1]."""
+    m, c = qh.shape
+    if m % stride:
+        raise ValueError("M must be a multiple of the stride")
+    return _f64(qh).reshape(m // stride, stride * c)
+
+
+def reversed_key_rows(kh: np.ndarray, stride: int) -> np.ndarray:
+    """K~' (R, S*C): row j concatenates k[j*S+S-1], ..., k[j*S]."""
+    m, c = kh.shape
+    if m % stride:
+        raise ValueError("M must be a multiple of the stride")
+    return _f64(kh).reshape(m // stride, stride, c)[:, ::-1, :].reshape(m // stride, stride * c)
+
+
+def strided_logits(qh, kh, stride: int, score_scale: float, causal: bool,
+                   rows: slice | None = None) -> np.ndarray:
+    """Scaled strided antidiagonal logits for strided query ``rows`` vs all keys.
+
+    Entries with key j > query i are -inf when ``causal`` (strided level).
+    """
+    qs = strided_query_rows(qh, stride)
+    ks = reversed_key_rows(kh, stride)
+    if rows is None:
+        rows = slice(0, qs.shape[0])
+    lo = rows.start
+    a = qs[rows] @ ks.T
+    a *= score_scale
+    if causal:
+        i = np.arange(lo, lo + a.shape[0])[:, None]
+        j = np.arange(ks.shape[0])[None, :]
+        a[j > i] = -np.inf
+    return a
+
+
+# ---------------------------------------------------------------------------
+# Stage 2: softmax-normalised block importance.
+# [XA-sum] Approach: the strided antidiagonal values inside each attention
+# block are summed after softmax normalisation. [DuSA] Response to Q2: the
+# softmax runs on the final two dimensions of the reshaped tensors, i.e. over
+# keys for each strided query row.
+# ---------------------------------------------------------------------------
+
+def block_score_row(qh, kh, big_i: int, block: int, stride: int,
+                    score_scale: float, causal: bool) -> np.ndarray:
+    """Block scores S^[I, :] (length NB) for query block ``big_i`` of one head."""
+    if block % stride:
+        raise ValueError("block must be a multiple of the stride")
+    m = qh.shape[0]
+    r = block // stride
+    nb = m // block
+    logits = strided_logits(qh, kh, stride, score_scale, causal,
+                            rows=slice(big_i * r, (big_i + 1) * r))
+    # row softmax over keys
+    mx = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - mx)
+    p /= p.sum(axis=1, keepdims=True)
+    # sum each (r x r) tile: columns grouped into NB blocks of r strided keys
+    per_block = p.reshape(r, nb, r).sum(axis=2).sum(axis=0)
+    return per_block / r
+
+
+def block_scores(q, k, block: int, stride: int, score_scale: float, causal: bool,
+                 heads=None, qblocks=None) -> np.ndarray:
+    """Block scores (B, Hq, NB, NB), float64. Rows not in ``qblocks`` stay 0."""
+    b_, hq, m, _ = q.shape
+    hkv = k.shape[1]
+    nb = m // block
+    heads = range(hq) if heads is None else heads
+    qblocks = range(nb) if qblocks is None else qblocks
+    out = np.zeros((b_, hq, nb, nb))
+    for b in range(b_):
+        for h in heads:
+            g = _kv_head(h, hq, hkv)
+            for big_i in qblocks:
+                out[b, h, big_i] = block_score_row(q[b, h], k[b, g], big_i, block,
+                                                   stride, score_scale, causal)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Stage 3: minimal-set threshold selection.
+# [XA-sum] Approach: keep the minimal set of blocks whose softmax-normalised
+# antidiagonal mass exceeds a (per-head) threshold. [Flex] R Q3: minimising
+# |S| subject to the cumulative-mass constraint is solved by taking entries in
+# descending order until the constraint holds.
+# ---------------------------------------------------------------------------
+
+def minimal_set(cand: np.ndarray, tau: float) -> np.ndarray:
+    """Indices of the smallest candidate set whose mass reaches tau * total.
+
+    Candidates are taken in descending score order (ties: ascending index) and
+    the prefix stops at the first k with cumulative mass >= tau * total
+    (k = 0 when tau <= 0). tau >= 1 keeps every candidate.
+    """
+    cand = _f64(cand)
+    n = cand.shape[0]
+    if tau >= 1.0:
+        return np.arange(n)
+    idx = np.arange(n)
+    order = np.lexsort((idx, -cand))          # score descending, index ascending
+    csum = np.concatenate([[0.0], np.cumsum(cand[order])])
+    total = csum[-1]
+    kstar = int(np.argmax(csum >= tau * total))  # first k with mass >= tau * total
+    return order[:kstar]
+
+
+def select_row(scores_row: np.ndarray, big_i: int, tau: float, causal: bool) -> np.ndarray:
+    """Boolean keep-mask (length NB) for one query-block row."""
+    nb = scores_row.shape[0]
+    n_cand = big_i + 1 if causal else nb
+    keep = np.zeros(nb, dtype=bool)
+    keep[minimal_set(scores_row[:n_cand], tau)] = True
+    keep[big_i] = True                               # diagonal block, added after the cut
+    return keep
+
+
+def select(scores: np.ndarray, tau, causal: bool, heads=None, qblocks=None) -> np.ndarray:
+    """Mask (B, Hq, NB, NB) uint8 from block scores and per-head ``tau`` (len Hq)."""
+    b_, hq, nb, _ = scores.shape
+    tau = np.broadcast_to(np.asarray(tau, dtype=np.float64), (hq,))
+    heads = range(hq) if heads is None else heads
+    qblocks = range(nb) if qblocks is None else qblocks
+    mask = np.zeros(scores.shape, dtype=np.uint8)
+    for b in range(b_):
+        for h in heads:
+            for big_i in qblocks:
+                mask[b, h, big_i] = select_row(scores[b, h, big_i], big_i, float(tau[h]), causal)
+    return mask
+
+
+def mask_to_index(mask: np.ndarray):
+    """Ascending per-row block lists: kv_idx (.., NB) int32 padded with -1, kv_cnt int32."""
+    nb = mask.shape[-1]
+    cnt = mask.astype(bool).sum(axis=-1).astype(np.int32)
+    idx = np.full(mask.shape, -1, dtype=np.int32)
+    flat_m = mask.reshape(-1, nb).astype(bool)
+    flat_i = idx.reshape(-1, nb)
+    for row in range(flat_m.shape[0]):
+        sel = np.nonzero(flat_m[row])[0]
+        flat_i[row, :sel.size] = sel
+    return idx, cnt
+
+
+# ---------------------------------------------------------------------------
+# Stage 4: block-sparse attention.
+# [XA-abs]: block-sparse attention computes only on the critical blocks.
+# Plain definition: exact softmax attention over the selected keys only
+# (causal: key index <= query index), scale sm_scale.
+# ---------------------------------------------------------------------------
+
+def attend_row(qh, kh, vh, keep_row: np.ndarray, big_i: int, block: int,
+               sm_scale: float, causal: bool):
+    """Output (Bk, C) and natural-log LSE (Bk,) for query block ``big_i``."""
+    qb = _f64(qh[big_i * block:(big_i + 1) * block])
+    blocks = np.nonzero(keep_row)[0]
+    keys = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    kk = _f64(kh[keys])
+    vv = _f64(vh[keys])
+    s = (qb @ kk.T) * sm_scale
+    if causal:
+        qi = big_i * block + np.arange(block)[:, None]
+        s[keys[None, :] > qi] = -np.inf
+    mx = s.max(axis=1, keepdims=True)
+    p = np.exp(s - mx)
+    den = p.sum(axis=1, keepdims=True)
+    out = (p @ vv) / den
+    lse = (mx + np.log(den))[:, 0]
+    return out, lse
+
+
+def attend(q, k, v, mask, block: int, sm_scale: float, causal: bool,
+           heads=None, qblocks=None):
+    """Block-sparse attention with a block mask (B, Hq, NB, NB): (out, lse) float64."""
+    b_, hq, m, c = q.shape
+    hkv = k.shape[1]
+    nb = m // block
+    heads = range(hq) if heads is None else heads
+    qblocks = range(nb) if qblocks is None else qblocks
+    out = np.zeros((b_, hq, m, c))
+    lse = np.zeros((b_, hq, m))
+    for b in range(b_):
+        for h in heads:
+            g = _kv_head(h, hq, hkv)
+            for big_i in qblocks:
+                o, l = attend_row(q[b, h], k[b, g], v[b, g], mask[b, h, big_i], big_i,
+                                  block, sm_scale, causal)
+                out[b, h, big_i * block:(big_i + 1) * block] = o
+                lse[b, h, big_i * block:(big_i + 1) * block] = l
+    return out, lse
+
+
+def dense(q, k, v, block: int, sm_scale: float, causal: bool, heads=None, qblocks=None):
+    """Dense attention: every candidate block kept."""
+    b_, hq, m, _ = q.shape
+    nb = m // block
+    full = np.ones((b_, hq, nb, nb), dtype=np.uint8)
+    if causal:
+        full = np.broadcast_to(np.tril(np.ones((nb, nb), dtype=np.uint8)), full.shape).copy()
+    return attend(q, k, v, full, block, sm_scale, causal, heads, qblocks)
+
+
+def prefill(q, k, v, block: int, stride: int, tau, score_scale: float, sm_scale: float,
+            causal: bool, heads=None, qblocks=None):
+    """All three stages: (block_scores, mask, out, lse)."""
+    sc = block_scores(q, k, block, stride, score_scale, causal, heads, qblocks)
+    mk = select(sc, tau, causal, heads, qblocks)
+    out, lse = attend(q, k, v, mk, block, sm_scale, causal, heads, qblocks)
+    return sc, mk, out, lse
+
+
+def density(mask: np.ndarray, causal: bool, qblocks=None) -> float:
+    """Selected blocks / candidate blocks (diagonal counted as 1)."""
+    nb = mask.shape[-1]
+    rows = range(nb) if qblocks is None else list(qblocks)
+    sel = 0
+    cand = 0
+    for big_i in rows:
+        sel += int(mask[..., big_i, :].astype(bool).sum())
+        cand += (big_i + 1 if causal else nb) * int(np.prod(mask.shape[:-2]))
+    return sel / cand

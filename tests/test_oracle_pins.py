@@ -1,0 +1,277 @@
+"""Pins for the CPU oracle: each check rests on something other than the oracle.
+
+* brute force over the full attention matrix (antidiagonal tile sums);
+* a hand-worked example stored under tests/golden/;
+* the stride-1 closed form (textbook per-block attention mass via scipy softmax);
+* exhaustive subset enumeration for the minimal set;
+* torch's scaled_dot_product_attention (CPU, float64) with an element mask;
+* invariants: non-negative scores, rows summing to 1, tau=1 keeps every
+  candidate and equals dense attention, monotonicity in tau, diagonal kept.
+"""
+import itertools
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _read_golden(name):
+    rows = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            rows[key] = np.array([float(x) for x in vals])
+    return rows
+
+
+# ----------------------------------------------------------------- scoring
+
+@pytest.mark.parametrize("stride,m,c", [(2, 16, 3), (4, 32, 5), (8, 64, 2), (1, 8, 4)])
+def test_strided_logits_equal_bruteforce_antidiagonal(stride, m, c):
+    rng = _rng(stride)
+    q = rng.standard_normal((m, c))
+    k = rng.standard_normal((m, c))
+    full = q @ k.T
+    r = m // stride
+    brute = np.zeros((r, r))
+    for i in range(r):
+        for j in range(r):
+            # walk the tile's antidiagonal from its lower-left to its upper-right corner
+            for a in range(stride):
+                brute[i, j] += full[i * stride + stride - 1 - a, j * stride + a]
+    got = oracle.strided_logits(q, k, stride, 1.0, causal=False)
+    np.testing.assert_allclose(got, brute, rtol=1e-12, atol=1e-12)
+
+
+def test_strided_logits_are_not_the_diagonal_sums():
+    # A dropped reversal would give the main-diagonal tile sums instead.
+    rng = _rng(7)
+    q = rng.standard_normal((32, 4))
+    k = rng.standard_normal((32, 4))
+    full = q @ k.T
+    s = 4
+    diag = np.array([[sum(full[i * s + a, j * s + a] for a in range(s)) for j in range(8)]
+                     for i in range(8)])
+    got = oracle.strided_logits(q, k, s, 1.0, causal=False)
+    assert np.abs(got - diag).max() > 1e-3
+
+
+def test_strided_logits_causal_mask_and_scale():
+    rng = _rng(3)
+    q = rng.standard_normal((32, 4))
+    k = rng.standard_normal((32, 4))
+    a = oracle.strided_logits(q, k, 4, 0.25, causal=True)
+    b = oracle.strided_logits(q, k, 4, 1.0, causal=False)
+    r = 8
+    for i in range(r):
+        for j in range(r):
+            if j > i:
+                assert a[i, j] == -np.inf
+            else:
+                assert a[i, j] == pytest.approx(0.25 * b[i, j], rel=1e-14)
+
+
+def test_golden_hand_example():
+    g = _read_golden("antidiag_hand_example.txt")
+    q = np.array([[1.0], [2.0], [3.0], [4.0]])
+    k = np.array([[1.0], [1.0], [2.0], [2.0]])
+    a = oracle.strided_logits(q, k, 2, 1.0, causal=False)
+    np.testing.assert_array_equal(a.reshape(-1), g["strided_scores"])
+    sc = oracle.block_scores(q[None, None], k[None, None], 2, 2, 1.0, causal=True)[0, 0]
+    np.testing.assert_allclose(sc[0], g["block_scores_row0"], rtol=1e-15, atol=0)
+    np.testing.assert_allclose(sc[1], g["block_scores_row1"], rtol=1e-14, atol=0)
+    m9 = oracle.select(sc[None, None], [0.9], causal=True)[0, 0, 1]
+    np.testing.assert_array_equal(m9, g["mask_row1_tau0.9"])
+    m99 = oracle.select(sc[None, None], [0.9995], causal=True)[0, 0, 1]
+    np.testing.assert_array_equal(m99, g["mask_row1_tau0.9995"])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_stride_one_equals_textbook_block_attention_mass(causal):
+    # With S=1 each strided cell is a single logit, so the block score is the
+    # per-block attention mass averaged over the block's query rows.
+    rng = _rng(11)
+    m, c, block = 64, 8, 16
+    q = rng.standard_normal((m, c))
+    k = rng.standard_normal((m, c))
+    scale = 0.7
+    logits = scale * (q @ k.T)
+    if causal:
+        logits = np.where(np.tril(np.ones((m, m), dtype=bool)), logits, -np.inf)
+    p = scipy.special.softmax(logits, axis=1)
+    nb = m // block
+    expect = np.zeros((nb, nb))
+    for big_i in range(nb):
+        for big_j in range(nb):
+            expect[big_i, big_j] = p[big_i * block:(big_i + 1) * block,
+                                     big_j * block:(big_j + 1) * block].sum() / block
+    got = oracle.block_scores(q[None, None], k[None, None], block, 1, scale, causal)[0, 0]
+    np.testing.assert_allclose(got, expect, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_score_invariants(causal):
+    rng = _rng(5)
+    q = rng.standard_normal((1, 4, 256, 16))
+    k = rng.standard_normal((1, 2, 256, 16))
+    sc = oracle.block_scores(q, k, 32, 4, 0.3, causal)
+    assert (sc >= 0).all()
+    np.testing.assert_allclose(sc.sum(axis=-1), 1.0, rtol=1e-12)
+    if causal:
+        nb = sc.shape[-1]
+        upper = np.triu(np.ones((nb, nb), dtype=bool), k=1)
+        assert (sc[..., upper] == 0).all()
+
+
+def test_block_scores_gqa_reads_shared_kv_head():
+    rng = _rng(9)
+    q = rng.standard_normal((1, 4, 128, 8))
+    k = rng.standard_normal((1, 2, 128, 8))
+    sc = oracle.block_scores(q, k, 32, 4, 0.5, True)
+    # repeat-KV MHA must give the same scores
+    k_rep = np.repeat(k, 2, axis=1)
+    sc2 = oracle.block_scores(q, k_rep, 32, 4, 0.5, True)
+    np.testing.assert_array_equal(sc, sc2)
+    # and head 1 must differ from using KV head 1 instead of 0
+    wrong = oracle.block_scores(q[:, 1:2], k[:, 1:2], 32, 4, 0.5, True)
+    assert np.abs(wrong[0, 0] - sc[0, 1]).max() > 1e-6
+
+
+# --------------------------------------------------------------- selection
+
+def test_minimal_set_matches_exhaustive_search():
+    rng = _rng(21)
+    for trial in range(200):
+        n = int(rng.integers(1, 11))
+        cand = rng.dirichlet(np.full(n, 0.5))
+        if trial % 5 == 0:                       # force ties
+            cand = np.round(cand * 4) / 4
+        tau = float(rng.choice([0.0, 0.3, 0.5, 0.8, 0.9, 0.95, 0.999, 1.0]))
+        total = cand.sum()
+        kept = oracle.minimal_set(cand, tau)
+        if tau >= 1.0:
+            assert len(kept) == n
+            continue
+        best = None
+        for size in range(0, n + 1):
+            for sub in itertools.combinations(range(n), size):
+                if cand[list(sub)].sum() >= tau * total:
+                    best = size
+                    break
+            if best is not None:
+                break
+        assert len(kept) == best, (cand, tau, kept)
+        assert cand[kept].sum() >= tau * total
+
+
+def test_minimal_set_tie_break_by_ascending_index():
+    cand = np.array([0.25, 0.25, 0.25, 0.25])
+    np.testing.assert_array_equal(oracle.minimal_set(cand, 0.5), [0, 1])
+    cand = np.array([0.1, 0.3, 0.3, 0.3])
+    np.testing.assert_array_equal(oracle.minimal_set(cand, 0.6), [1, 2])
+
+
+def test_select_invariants():
+    rng = _rng(4)
+    q = rng.standard_normal((1, 2, 512, 16))
+    k = rng.standard_normal((1, 1, 512, 16))
+    sc = oracle.block_scores(q, k, 32, 4, 0.5, True)
+    nb = sc.shape[-1]
+    lower = np.tril(np.ones((nb, nb), dtype=bool))
+    prev = None
+    for tau in [0.0, 0.5, 0.8, 0.9, 0.99, 1.0]:
+        mk = oracle.select(sc, [tau, tau], True).astype(bool)
+        assert mk[..., np.arange(nb), np.arange(nb)].all()          # diagonal kept
+        assert not mk[..., ~lower].any()                              # causal candidates only
+        if prev is not None:
+            assert (mk >= prev).all()                                 # monotone in tau
+        prev = mk
+    assert prev[..., lower].all()                                     # tau = 1: everything
+    only_diag = oracle.select(sc, [0.0, 0.0], True).astype(bool)
+    assert only_diag.sum() == 2 * nb
+
+
+def test_tau_one_keeps_underflowed_blocks():
+    row = np.array([1.0, 0.0, 0.0, 0.0])
+    keep = oracle.select_row(row, 3, 1.0, True)
+    assert keep.all()
+
+
+def test_mask_to_index():
+    mk = np.array([[[[1, 0, 1, 0], [0, 1, 0, 0], [1, 1, 1, 0], [0, 0, 0, 1]]]], dtype=np.uint8)
+    idx, cnt = oracle.mask_to_index(mk)
+    np.testing.assert_array_equal(cnt[0, 0], [2, 1, 3, 1])
+    np.testing.assert_array_equal(idx[0, 0, 0, :2], [0, 2])
+    np.testing.assert_array_equal(idx[0, 0, 2, :3], [0, 1, 2])
+    assert idx[0, 0, 1, 1] == -1
+
+
+# --------------------------------------------------------------- attention
+
+def _sdpa_masked(q, k, v, mask, block, scale, causal):
+    """torch SDPA on the CPU in float64 with the block mask expanded to elements."""
+    hq, hkv = q.shape[1], k.shape[1]
+    kr = torch.from_numpy(np.repeat(k, hq // hkv, axis=1))
+    vr = torch.from_numpy(np.repeat(v, hq // hkv, axis=1))
+    elem = np.repeat(np.repeat(mask.astype(bool), block, axis=-2), block, axis=-1)
+    if causal:
+        m = q.shape[2]
+        elem = elem & np.tril(np.ones((m, m), dtype=bool))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), kr, vr, attn_mask=torch.from_numpy(elem), scale=scale)
+    logits = scale * torch.from_numpy(q) @ kr.transpose(-1, -2)
+    logits = logits.masked_fill(~torch.from_numpy(elem), float("-inf"))
+    return out.numpy(), torch.logsumexp(logits, dim=-1).numpy()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attend_matches_sdpa_with_element_mask(causal):
+    rng = _rng(13)
+    q = rng.standard_normal((1, 4, 128, 16))
+    k = rng.standard_normal((1, 2, 128, 16))
+    v = rng.standard_normal((1, 2, 128, 16))
+    nb = 8
+    mask = (rng.random((1, 4, nb, nb)) < 0.4).astype(np.uint8)
+    mask[..., np.arange(nb), np.arange(nb)] = 1
+    if causal:
+        mask = mask * np.tril(np.ones((nb, nb), dtype=np.uint8))
+    out, lse = oracle.attend(q, k, v, mask, 16, 0.25, causal)
+    ref, ref_lse = _sdpa_masked(q, k, v, mask, 16, 0.25, causal)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+
+
+def test_tau_one_equals_dense_causal_sdpa():
+    rng = _rng(17)
+    q = rng.standard_normal((1, 2, 128, 16))
+    k = rng.standard_normal((1, 1, 128, 16))
+    v = rng.standard_normal((1, 1, 128, 16))
+    sc, mk, out, lse = oracle.prefill(q, k, v, 16, 4, [1.0, 1.0], 0.0625, 0.25, True)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(np.repeat(k, 2, axis=1)),
+        torch.from_numpy(np.repeat(v, 2, axis=1)), is_causal=True, scale=0.25).numpy()
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+    d_out, _ = oracle.dense(q, k, v, 16, 0.25, True)
+    np.testing.assert_allclose(d_out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_density_counts_candidates():
+    nb = 4
+    mk = np.tril(np.ones((1, 1, nb, nb), dtype=np.uint8))
+    assert oracle.density(mk, True) == 1.0
+    eye = np.eye(nb, dtype=np.uint8)[None, None]
+    assert oracle.density(eye, True) == pytest.approx(4 / 10)
+    assert oracle.density(eye, False) == pytest.approx(4 / 16)

@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for the prefill-attention workloads.
+
+This module holds no arithmetic of the method itself: it only draws Q, K, V and
+the per-head thresholds. Both the CPU oracle (in the tests) and the HIP path
+read what it produces.
+
+The pages measure on RULER / LongBench prefill with Llama-3.1-8B-Instruct and on
+HunyuanVideo generation; none of that is available, so seeded synthetic tensors
+with the same shapes and the attention structures those workloads show (sinks,
+vertical stripes, slash bands, spatio-temporal locality) stand in for them.
+
+Structure terms are added as channel features: a boost ``b`` between query i
+and key j is realised by giving Q the feature ``a_h * C**0.25 * phi(i)`` and K
+the feature ``gamma * b * C**0.25 * psi(j)``, so that after the attention scale
+1/sqrt(C) the logit changes by ``a_h * gamma * b * <phi(i), psi(j)>``.
+
+All draws are float32 on the requested device in a fixed order (Q, K, V, then
+structure draws, then tau) and are cast to the workload dtype with
+round-to-nearest-even. The same seed on the same device type gives the same
+tensors.
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+import math
+
+import torch
+
+# Structure strength per family, fixed once by calibration on the oracle's
+# selection (head-mean density of the 256K layer near 7.32% at tau=0.9, and
+# of the video layer near 45.5% at tau=0.95) and never tuned against GPU time.
+GAMMA = {"tiny": 1.0, "llama": 1.0, "llama_long": 1.0, "video": 1.0}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    family: str
+    B: int
+    Hq: int
+    Hkv: int
+    M: int
+    C: int
+    block: int
+    stride: int
+    causal: bool
+    dtype: str          # "bf16" or "f32"
+    seed: int
+    tau: tuple | float  # float, or the tuple of choices drawn per head
+
+    @property
+    def nb(self) -> int:
+        return self.M // self.block
+
+    @property
+    def dense_flops(self) -> float:
+        """Dense-equivalent FLOPs: 2*B*Hq*M^2*C causal, 4*B*Hq*M^2*C otherwise."""
+        f = 2.0 * self.B * self.Hq * self.M * self.M * self.C
+        return f if self.causal else 2.0 * f
+
+    def scaled(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", "tiny", 1, 1, 1, 1024, 64, 64, 8, True, "f32", 0, 0.9),
+    "llama8k": Workload("llama8k", "llama", 1, 32, 8, 8192, 128, 128, 8, True, "bf16", 1, 0.9),
+    "llama32k": Workload("llama32k", "llama", 1, 32, 8, 32768, 128, 128, 8, True, "bf16", 2,
+                         (0.8, 0.85, 0.9, 0.95)),
+    "llama128k": Workload("llama128k", "llama_long", 1, 32, 8, 131072, 128, 128, 16, True, "bf16", 3, 0.9),
+    "llama256k": Workload("llama256k", "llama_long", 1, 32, 8, 262144, 128, 128, 16, True, "bf16", 4, 0.9),
+    "video": Workload("video", "video", 1, 24, 24, 76800, 128, 128, 8, False, "bf16", 5, 0.95),
+}
+
+
+def _cast(x: torch.Tensor, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return x.to(torch.bfloat16)
+    if dtype == "f32":
+        return x.contiguous()
+    raise ValueError(dtype)
+
+
+def _fourier_bank(pos: torch.Tensor, n_pairs: int, base: float, span: float) -> torch.Tensor:
+    """[cos, sin] features with angular rates (pi/2) * span**(-m/(n_pairs-1))."""
+    m = torch.arange(n_pairs, device=pos.device, dtype=torch.float32)
+    omega = (math.pi / 2) * torch.pow(torch.tensor(span, device=pos.device), -m / (n_pairs - 1))
+    ang = pos.to(torch.float32)[:, None] * omega[None, :] + base
+    return torch.cat([torch.cos(ang), torch.sin(ang)], dim=1)
+
+
+def _video_bank(m_tokens: int, device) -> torch.Tensor:
+    """3-axis sinusoidal position features (M, 36): frames x rows x columns = 30 x 20 x 128."""
+    n = torch.arange(m_tokens, device=device)
+    axes = [(n // 2560, 30), ((n // 128) % 20, 20), (n % 128, 128)]
+    feats = []
+    for coord, length in axes:
+        periods = []
+        p = 4
+        while p <= 4 * length:
+            periods.append(p)
+            p *= 2
+        scale = 1.0 / math.sqrt(len(periods))
+        for per in periods:
+            ang = 2 * math.pi * coord.to(torch.float32) / per
+            feats.append(scale * torch.cos(ang))
+            feats.append(scale * torch.sin(ang))
+    return torch.stack(feats, dim=1)
+
+
+def make_inputs(w: Workload, device="cpu", gamma: float | None = None):
+    """Return dict(q, k, v, tau) for workload ``w`` on ``device``.
+
+    q: (B, Hq, M, C); k, v: (B, Hkv, M, C) in the workload dtype;
+    tau: float32 CPU tensor of Hq thresholds.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed)
+    gam = GAMMA[w.family] if gamma is None else gamma
+    B, Hq, Hkv, M, C = w.B, w.Hq, w.Hkv, w.M, w.C
+    f32 = dict(device=device, dtype=torch.float32)
+    c4 = C ** 0.25
+
+    if w.family == "tiny":
+        q = torch.randn((B, Hq, M, C), generator=g, **f32)
+        k = torch.randn((B, Hkv, M, C), generator=g, **f32)
+        v = torch.randn((B, Hkv, M, C), generator=g, **f32)
+        k[:, :, :4, :] *= 4.0 * gam                      # attention sink
+        steps = torch.randn((B, Hkv, M, C), generator=g, **f32) / math.sqrt(C)
+        walk = torch.cumsum(steps, dim=2)                 # shared local random walk
+        q += 0.5 * walk.repeat_interleave(Hq // Hkv, dim=1)
+        k += 0.5 * walk
+    elif w.family in ("llama", "llama_long"):
+        q = torch.randn((B, Hq, M, C), generator=g, **f32) / math.sqrt(C)
+        k = torch.randn((B, Hkv, M, C), generator=g, **f32) / math.sqrt(C)
+        v = torch.randn((B, Hkv, M, C), generator=g, **f32)
+        a_h = 1.0 + 0.5 * (2 * torch.rand((Hq,), generator=g, **f32) - 1)
+        q[:, :, :, 0] += (a_h * c4)[None, :, None]        # reads the sink channel
+        q[:, :, :, 1] += (a_h * c4)[None, :, None]        # reads the column channel
+        k[:, :, :4, 0] += gam * 12.0 * c4                 # sink on the first 4 keys
+        if w.family == "llama":
+            j = torch.arange(M, device=device)
+            stripe = ((j % 512) < 8).to(torch.float32)    # periodic vertical stripes
+            k[:, :, :, 1] += gam * 6.0 * c4 * stripe[None, None, :]
+        else:
+            # random vertical columns on 0.5% of keys per KV head
+            n_col = max(1, int(0.005 * (M - 4)))
+            for hk in range(Hkv):
+                cols = 4 + torch.randperm(M - 4, generator=g, device=device)[:n_col]
+                amp = 4.0 * (0.5 + torch.rand((n_col,), generator=g, **f32))
+                k[:, hk, cols, 1] += gam * c4 * amp
+            # slash bands at diagonal offsets {0, 1024, 4096}: shared Fourier bank
+            n_pairs = (C - 2) // 2
+            pos = torch.arange(M, device=device)
+            psi_q = _fourier_bank(pos, n_pairs, 0.0, 8192.0)             # (M, 2*n_pairs)
+            psi_k = torch.zeros_like(psi_q)
+            for d in (0, 1024, 4096):
+                psi_k += _fourier_bank(pos + d, n_pairs, 0.0, 8192.0)
+            beta = gam * 6.0 * c4 / n_pairs
+            q[:, :, :, 2:2 + 2 * n_pairs] += (a_h[:, None, None] * c4) * psi_q[None, None]
+            k[:, :, :, 2:2 + 2 * n_pairs] += beta * psi_k[None, None]
+    elif w.family == "video":
+        q = torch.randn((B, Hq, M, C), generator=g, **f32)
+        k = torch.randn((B, Hkv, M, C), generator=g, **f32)
+        v = torch.randn((B, Hkv, M, C), generator=g, **f32)
+        phi = _video_bank(M, device)                      # (M, 36)
+        amp = math.sqrt(4.0 * gam * math.sqrt(C))
+        q[:, :, :, :phi.shape[1]] += amp * phi[None, None]
+        k[:, :, :, :phi.shape[1]] += amp * phi[None, None]
+    else:
+        raise ValueError(w.family)
+
+    if isinstance(w.tau, tuple):
+        choice = torch.randint(len(w.tau), (Hq,), generator=g, device=device).cpu()
+        tau = torch.tensor([w.tau[i] for i in choice.tolist()], dtype=torch.float32)
+    else:
+        tau = torch.full((Hq,), float(w.tau), dtype=torch.float32)
+    return {"q": _cast(q, w.dtype), "k": _cast(k, w.dtype), "v": _cast(v, w.dtype), "tau": tau}
+
+
+def default_scales(w: Workload):
+    """(score_scale, sm_scale): mean of the S antidiagonal logits, and 1/sqrt(C)."""
+    sm = 1.0 / math.sqrt(w.C)
+    return sm / w.stride, sm
+
+
+def sha256(t: torch.Tensor) -> str:
+    x = t.detach().cpu().contiguous()
+    if x.dtype == torch.bfloat16:
+        x = x.view(torch.int16)
+    return hashlib.sha256(x.numpy().tobytes()).hexdigest()[:16]
