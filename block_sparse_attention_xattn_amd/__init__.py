@@ -1,0 +1,214 @@
+"""Python binding of libxattn.so (XAttention-style block-sparse prefill attention
+on MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI
+declared in include/xattn.h. PyTorch supplies device memory and the current
+stream. If the library is missing the import fails loudly; there is no
+fallback.
+
+Functions take contiguous CUDA (HIP) tensors: q (B, Hq, M, C), k and v
+(B, Hkv, M, C), all bfloat16 or all float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libxattn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m block_sparse_attention_xattn_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+XATTN_BF16 = 0
+XATTN_F32 = 1
+ABI_VERSION = 1
+MAX_HEADS = 256
+
+EXPORTS = (
+    "xattn_abi_version", "xattn_status_string", "xattn_last_error",
+    "xattn_score_workspace_bytes", "xattn_score", "xattn_select", "bsa_fwd",
+    "dense_fwd", "xattn_prefill",
+)
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "Hq", "Hkv", "M", "C", "block", "stride", "causal", "dtype")]
+
+
+_P = ctypes.POINTER(Problem)
+_vp = ctypes.c_void_p
+_f = ctypes.c_float
+_lib.xattn_abi_version.restype = ctypes.c_int32
+_lib.xattn_status_string.restype = ctypes.c_char_p
+_lib.xattn_status_string.argtypes = [ctypes.c_int]
+_lib.xattn_last_error.restype = ctypes.c_char_p
+_lib.xattn_score_workspace_bytes.restype = ctypes.c_size_t
+_lib.xattn_score_workspace_bytes.argtypes = [_P]
+_lib.xattn_score.restype = ctypes.c_int
+_lib.xattn_score.argtypes = [_P, _vp, _vp, _f, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.xattn_select.restype = ctypes.c_int
+_lib.xattn_select.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.bsa_fwd.restype = ctypes.c_int
+_lib.bsa_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp]
+_lib.dense_fwd.restype = ctypes.c_int
+_lib.dense_fwd.argtypes = [_P, _vp, _vp, _vp, _f, _vp, _vp, _vp]
+_lib.xattn_prefill.restype = ctypes.c_int
+_lib.xattn_prefill.argtypes = [_P, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp, _vp, _vp,
+                               ctypes.c_size_t, _vp, _vp, _vp]
+
+if _lib.xattn_abi_version() != ABI_VERSION:
+    raise ImportError("libxattn.so ABI version mismatch")
+
+
+class XAttnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        msg = _lib.xattn_status_string(status).decode()
+        detail = _lib.xattn_last_error().decode()
+        super().__init__(f"xattn status {status} ({msg}): {detail}")
+
+
+def _check(status: int):
+    if status != 0:
+        raise XAttnError(status)
+
+
+def problem(B, Hq, Hkv, M, C, block, stride, causal, dtype) -> Problem:
+    """C struct for the given sizes; dtype is torch.bfloat16/torch.float32 or 0/1."""
+    if isinstance(dtype, torch.dtype):
+        dtype = {torch.bfloat16: XATTN_BF16, torch.float32: XATTN_F32}.get(dtype, 99)
+    return Problem(B, Hq, Hkv, M, C, block, stride, int(bool(causal)), dtype)
+
+
+def _problem_of(q, k, block, stride, causal) -> Problem:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be 4-D (B, H, M, C)")
+    B, Hq, M, C = q.shape
+    return problem(B, Hq, k.shape[1], M, C, block, stride, causal, q.dtype)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _same(q, *ts):
+    for t in ts:
+        if t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share dtype and device")
+
+
+def workspace_bytes(p: Problem) -> int:
+    return int(_lib.xattn_score_workspace_bytes(ctypes.byref(p)))
+
+
+def xattn_score(q, k, block, stride, score_scale, causal=True, block_scores=None, ws=None):
+    """Block scores (B, Hq, NB, NB) float32."""
+    _same(q, k)
+    p = _problem_of(q, k, block, stride, causal)
+    nb = q.shape[2] // block
+    if block_scores is None:
+        block_scores = torch.empty((q.shape[0], q.shape[1], nb, nb), dtype=torch.float32, device=q.device)
+    need = workspace_bytes(p)
+    if ws is None:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
+    _check(_lib.xattn_score(ctypes.byref(p), _ptr(q), _ptr(k), float(score_scale), _ptr(block_scores),
+                            _ptr(ws), ws.numel() * ws.element_size(), _stream(q.device)))
+    return block_scores
+
+
+def _tau_host(tau, hq):
+    t = torch.as_tensor(tau, dtype=torch.float32).reshape(-1)
+    if t.numel() == 1:
+        t = t.expand(hq)
+    if t.numel() != hq:
+        raise ValueError(f"tau must have 1 or Hq={hq} entries")
+    return t.cpu().contiguous()
+
+
+def xattn_select(block_scores, tau, block, stride, causal=True, Hkv=None, C=128, dtype=torch.bfloat16,
+                 want_mask=True):
+    """(mask u8 or None, kv_idx int32, kv_cnt int32) for block scores (B, Hq, NB, NB)."""
+    B, Hq, nb, _ = block_scores.shape
+    p = problem(B, Hq, Hkv or Hq, nb * block, C, block, stride, causal, dtype)
+    dev = block_scores.device
+    mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev) if want_mask else None
+    kv_idx = torch.empty((B, Hq, nb, nb), dtype=torch.int32, device=dev)
+    kv_cnt = torch.empty((B, Hq, nb), dtype=torch.int32, device=dev)
+    tau_h = _tau_host(tau, Hq)
+    _check(_lib.xattn_select(ctypes.byref(p), _ptr(block_scores), tau_h.data_ptr(), _ptr(mask),
+                             _ptr(kv_idx), _ptr(kv_cnt), _stream(dev)))
+    return mask, kv_idx, kv_cnt
+
+
+def bsa_fwd(q, k, v, kv_idx, kv_cnt, block, sm_scale, causal=True, out=None, want_lse=False):
+    """Block-sparse attention: (out, lse or None)."""
+    _same(q, k, v)
+    p = _problem_of(q, k, block, 0, causal)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    _check(_lib.bsa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt),
+                        float(sm_scale), _ptr(out), _ptr(lse), _stream(q.device)))
+    return out, lse
+
+
+def dense_fwd(q, k, v, block, sm_scale, causal=True, out=None, want_lse=False):
+    """Dense attention (every candidate block): (out, lse or None)."""
+    _same(q, k, v)
+    p = _problem_of(q, k, block, 0, causal)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    _check(_lib.dense_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), float(sm_scale), _ptr(out),
+                          _ptr(lse), _stream(q.device)))
+    return out, lse
+
+
+class PrefillBuffers:
+    """Reusable device buffers for xattn_prefill (allocated once per shape)."""
+
+    def __init__(self, q, k, block, stride, causal=True, want_mask=True, want_lse=False):
+        p = _problem_of(q, k, block, stride, causal)
+        B, Hq, M, C = q.shape
+        nb = M // block
+        dev = q.device
+        self.problem = p
+        self.block_scores = torch.empty((B, Hq, nb, nb), dtype=torch.float32, device=dev)
+        self.mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev) if want_mask else None
+        self.kv_idx = torch.empty((B, Hq, nb, nb), dtype=torch.int32, device=dev)
+        self.kv_cnt = torch.empty((B, Hq, nb), dtype=torch.int32, device=dev)
+        self.ws = torch.empty(max(workspace_bytes(p), 4), dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(q)
+        self.lse = torch.empty((B, Hq, M), dtype=torch.float32, device=dev) if want_lse else None
+
+
+def xattn_prefill(q, k, v, tau, block, stride, score_scale, sm_scale, causal=True, buffers=None):
+    """All three stages in one call. Returns the PrefillBuffers holding the results."""
+    _same(q, k, v)
+    bufs = buffers or PrefillBuffers(q, k, block, stride, causal)
+    tau_h = _tau_host(tau, q.shape[1])
+    b = bufs
+    _check(_lib.xattn_prefill(ctypes.byref(b.problem), _ptr(q), _ptr(k), _ptr(v), tau_h.data_ptr(),
+                              float(score_scale), float(sm_scale), _ptr(b.block_scores), _ptr(b.mask),
+                              _ptr(b.kv_idx), _ptr(b.kv_cnt), _ptr(b.ws),
+                              b.ws.numel(), _ptr(b.out), _ptr(b.lse), _stream(q.device)))
+    return b
+
+
+# The pages' names for the stages, as aliases.
+score = xattn_score
+select = xattn_select
+prefill = xattn_prefill

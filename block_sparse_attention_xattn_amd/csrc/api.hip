@@ -1,0 +1,206 @@
+// C ABI of libxattn.so: argument validation on the host, then kernel launches
+// on the caller's stream. Nothing is allocated and no state is kept, apart
+// from a per-thread message for the last failure.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/xattn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+xattn_status fail(xattn_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+xattn_status fail(xattn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// need_stride: the scoring stages use the stride; attention ignores it.
+xattn_status check_problem(const xattn_problem* p, bool need_stride = true) {
+  if (!p) return fail(XATTN_ERR_NULL, "problem pointer is NULL");
+  if (p->dtype != XATTN_BF16 && p->dtype != XATTN_F32)
+    return fail(XATTN_ERR_DTYPE, "dtype %d is neither XATTN_BF16 nor XATTN_F32", p->dtype);
+  if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->M < 1 || p->C < 1 || p->block < 1 ||
+      (need_stride && p->stride < 1))
+    return fail(XATTN_ERR_SHAPE, "B, Hq, Hkv, M, C, block and stride must be positive");
+  if (p->causal != 0 && p->causal != 1) return fail(XATTN_ERR_ARG, "causal must be 0 or 1");
+  if (p->Hq % p->Hkv) return fail(XATTN_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
+  if (p->Hq > XATTN_MAX_HEADS) return fail(XATTN_ERR_UNSUPPORTED, "Hq=%d exceeds %d", p->Hq, XATTN_MAX_HEADS);
+  if (p->M % p->block) return fail(XATTN_ERR_SHAPE, "M=%d is not a multiple of block=%d", p->M, p->block);
+  if (need_stride && p->block % p->stride)
+    return fail(XATTN_ERR_SHAPE, "block=%d is not a multiple of stride=%d", p->block, p->stride);
+  if (p->C != 64 && p->C != 128) return fail(XATTN_ERR_UNSUPPORTED, "head dim C=%d (supported: 64, 128)", p->C);
+  if (p->block != 64 && p->block != 128) return fail(XATTN_ERR_UNSUPPORTED, "block=%d (supported: 64, 128)", p->block);
+  const int r = need_stride ? p->block / p->stride : 2;
+  if (!pow2(r) || r < 2 || r > 32)
+    return fail(XATTN_ERR_UNSUPPORTED, "block/stride=%d (supported: 2, 4, 8, 16, 32)", r);
+  if (p->M / p->block > XATTN_MAX_BLOCKS)
+    return fail(XATTN_ERR_UNSUPPORTED, "NB=%d exceeds %d blocks", p->M / p->block, XATTN_MAX_BLOCKS);
+  const size_t per_head = (size_t)p->M * p->C;
+  if ((size_t)p->B * p->Hq * per_head > ((size_t)1 << 40))
+    return fail(XATTN_ERR_UNSUPPORTED, "problem too large");
+  return XATTN_OK;
+}
+
+xattn::Shape shape_of(const xattn_problem* p) {
+  return xattn::Shape{p->B, p->Hq, p->Hkv, p->M, p->C, p->block, p->stride, p->causal};
+}
+
+xattn_status check_scale(float x, const char* name) {
+  if (!(x > 0.f) || !std::isfinite(x)) return fail(XATTN_ERR_ARG, "%s=%g must be positive and finite", name, (double)x);
+  return XATTN_OK;
+}
+
+xattn_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return XATTN_OK;
+  return fail(XATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+xattn_status check_tau(const xattn_problem* p, const float* tau, xattn::TauArray* out) {
+  if (!tau) return fail(XATTN_ERR_NULL, "tau is NULL");
+  std::memset(out, 0, sizeof(*out));
+  for (int h = 0; h < p->Hq; ++h) {
+    const float t = tau[h];
+    if (!(t >= 0.f && t <= 1.f)) return fail(XATTN_ERR_ARG, "tau[%d]=%g is outside [0, 1]", h, (double)t);
+    out->v[h] = t;
+  }
+  return XATTN_OK;
+}
+
+xattn_status do_score(const xattn_problem* p, const void* q, const void* k, float score_scale,
+                      float* block_scores, void* ws, size_t ws_bytes, hipStream_t st) {
+  const xattn::Shape s = shape_of(p);
+  hipError_t e;
+  if (p->dtype == XATTN_BF16)
+    e = xattn::launch_score_partials_bf16(s, static_cast<const uint16_t*>(q),
+                                          static_cast<const uint16_t*>(k), score_scale,
+                                          static_cast<float*>(ws), st);
+  else
+    e = xattn::launch_score_partials_f32(s, static_cast<const float*>(q), static_cast<const float*>(k),
+                                         score_scale, static_cast<float*>(ws), st);
+  if (e != hipSuccess) return hip_status(e, "score partials launch");
+  return hip_status(xattn::launch_score_finalize(s, static_cast<const float*>(ws), block_scores, st),
+                    "score finalize launch");
+}
+
+xattn_status do_attn(const xattn_problem* p, const void* q, const void* k, const void* v,
+                     const int32_t* kv_idx, const int32_t* kv_cnt, float sm_scale, void* out,
+                     float* lse, hipStream_t st) {
+  const xattn::Shape s = shape_of(p);
+  hipError_t e;
+  if (p->dtype == XATTN_BF16)
+    e = xattn::launch_attn_bf16(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                static_cast<const uint16_t*>(v), kv_idx, kv_cnt, sm_scale,
+                                static_cast<uint16_t*>(out), lse, st);
+  else
+    e = xattn::launch_attn_f32(s, static_cast<const float*>(q), static_cast<const float*>(k),
+                               static_cast<const float*>(v), kv_idx, kv_cnt, sm_scale,
+                               static_cast<float*>(out), lse, st);
+  return hip_status(e, "attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t xattn_abi_version(void) { return XATTN_ABI_VERSION; }
+
+const char* xattn_status_string(xattn_status s) {
+  switch (s) {
+    case XATTN_OK: return "ok";
+    case XATTN_ERR_NULL: return "null pointer";
+    case XATTN_ERR_SHAPE: return "inconsistent shape";
+    case XATTN_ERR_DTYPE: return "unknown dtype";
+    case XATTN_ERR_ARG: return "argument out of range";
+    case XATTN_ERR_UNSUPPORTED: return "unsupported configuration";
+    case XATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case XATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* xattn_last_error(void) { return g_err; }
+
+size_t xattn_score_workspace_bytes(const xattn_problem* p) {
+  if (check_problem(p) != XATTN_OK) return 0;
+  return (size_t)p->B * p->Hq * (size_t)(p->M / p->block) * (size_t)(p->M / p->stride) * sizeof(float);
+}
+
+xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k, float score_scale,
+                         float* block_scores, void* ws, size_t ws_bytes, void* stream) {
+  xattn_status s = check_problem(p);
+  if (s != XATTN_OK) return s;
+  if (!q || !k || !block_scores) return fail(XATTN_ERR_NULL, "q, k and block_scores must be non-NULL");
+  if ((s = check_scale(score_scale, "score_scale")) != XATTN_OK) return s;
+  const size_t need = xattn_score_workspace_bytes(p);
+  if (!ws || ws_bytes < need)
+    return fail(XATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  return do_score(p, q, k, score_scale, block_scores, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+xattn_status xattn_select(const xattn_problem* p, const float* block_scores, const float* tau,
+                          uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, void* stream) {
+  xattn_status s = check_problem(p);
+  if (s != XATTN_OK) return s;
+  if (!block_scores || !kv_idx || !kv_cnt)
+    return fail(XATTN_ERR_NULL, "block_scores, kv_idx and kv_cnt must be non-NULL");
+  xattn::TauArray t;
+  if ((s = check_tau(p, tau, &t)) != XATTN_OK) return s;
+  return hip_status(xattn::launch_select(shape_of(p), block_scores, t, mask, kv_idx, kv_cnt,
+                                         static_cast<hipStream_t>(stream)),
+                    "select launch");
+}
+
+xattn_status bsa_fwd(const xattn_problem* p, const void* q, const void* k, const void* v,
+                     const int32_t* kv_idx, const int32_t* kv_cnt, float sm_scale, void* out,
+                     float* lse, void* stream) {
+  xattn_status s = check_problem(p, false);
+  if (s != XATTN_OK) return s;
+  if (!q || !k || !v || !kv_idx || !kv_cnt || !out)
+    return fail(XATTN_ERR_NULL, "q, k, v, kv_idx, kv_cnt and out must be non-NULL");
+  if ((s = check_scale(sm_scale, "sm_scale")) != XATTN_OK) return s;
+  return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, static_cast<hipStream_t>(stream));
+}
+
+xattn_status dense_fwd(const xattn_problem* p, const void* q, const void* k, const void* v,
+                       float sm_scale, void* out, float* lse, void* stream) {
+  xattn_status s = check_problem(p, false);
+  if (s != XATTN_OK) return s;
+  if (!q || !k || !v || !out) return fail(XATTN_ERR_NULL, "q, k, v and out must be non-NULL");
+  if ((s = check_scale(sm_scale, "sm_scale")) != XATTN_OK) return s;
+  return do_attn(p, q, k, v, nullptr, nullptr, sm_scale, out, lse, static_cast<hipStream_t>(stream));
+}
+
+xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k, const void* v,
+                           const float* tau, float score_scale, float sm_scale, float* block_scores,
+                           uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, void* ws,
+                           size_t ws_bytes, void* out, float* lse, void* stream) {
+  xattn_status s = check_problem(p);
+  if (s != XATTN_OK) return s;
+  if (!q || !k || !v || !block_scores || !kv_idx || !kv_cnt || !out)
+    return fail(XATTN_ERR_NULL, "q, k, v, block_scores, kv_idx, kv_cnt and out must be non-NULL");
+  if ((s = check_scale(score_scale, "score_scale")) != XATTN_OK) return s;
+  if ((s = check_scale(sm_scale, "sm_scale")) != XATTN_OK) return s;
+  xattn::TauArray t;
+  if ((s = check_tau(p, tau, &t)) != XATTN_OK) return s;
+  const size_t need = xattn_score_workspace_bytes(p);
+  if (!ws || ws_bytes < need)
+    return fail(XATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = do_score(p, q, k, score_scale, block_scores, ws, ws_bytes, st)) != XATTN_OK) return s;
+  if ((s = hip_status(xattn::launch_select(shape_of(p), block_scores, t, mask, kv_idx, kv_cnt, st),
+                      "select launch")) != XATTN_OK)
+    return s;
+  return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, st);
+}
+
+}  // extern "C"

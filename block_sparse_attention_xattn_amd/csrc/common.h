@@ -1,0 +1,62 @@
+// Shared device helpers for the gfx950 kernels: bf16 <-> f32, MFMA fragment
+// types, wave-level exchanges, and the launch plans the host layer hands over.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace xattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x) << 16);
+}
+
+// Round-to-nearest-even float -> bf16 (gfx950 has a native conversion; the
+// compiler selects it for this cast).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  __bf16 b = static_cast<__bf16>(f);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Exchange with the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float xor32(float v) {
+  return __shfl_xor(v, 32, 64);
+}
+
+// Read 4 bf16 from LDS with the gfx950 transposing read: within each group of
+// 16 lanes, lane t receives element (t % 4) of the 8-byte chunks addressed by
+// lanes 4c + t/4, for c = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* lds_ptr) {
+  typedef i16x4 __attribute__((address_space(3))) * lp;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds_ptr));
+}
+
+// Work-item order for XCD locality: workgroups are dispatched round-robin over
+// the 8 XCDs (workgroup w runs on XCD w % 8). This maps w to a logical index so
+// that, in each group of 32 consecutive dispatches, XCD x receives the 4
+// consecutive logical items 32a + 4x .. 32a + 4x + 3 (e.g. the 4 query heads
+// that share one KV head). The tail beyond the last full group of 32 keeps its
+// own order.
+__device__ __forceinline__ uint32_t xcd_group4(uint32_t w, uint32_t n) {
+  uint32_t full = n & ~31u;
+  if (w >= full) return w;
+  uint32_t j = w >> 3, x = w & 7u;
+  return ((j >> 2) << 5) + (x << 2) + (j & 3u);
+}
+
+}  // namespace xattn

@@ -1,0 +1,44 @@
+// Host-side launch declarations shared by the kernel sources and the C ABI
+// layer. Every launcher only enqueues on `stream` and returns the HIP status of
+// the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace xattn {
+
+struct Shape {
+  int B, Hq, Hkv, M, C, block, stride, causal;
+  int NB() const { return M / block; }
+  int R() const { return M / stride; }
+  int r() const { return block / stride; }
+};
+
+// Stage 1: per (strided row i, key block J) partial log2-sum-exp of the scaled
+// strided antidiagonal logits, written to ws as [b][h][J][i] float32.
+hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
+                                      float score_scale, float* ws, hipStream_t st);
+hipError_t launch_score_partials_f32(const Shape& s, const float* q, const float* k,
+                                     float score_scale, float* ws, hipStream_t st);
+// Stage 2: block scores from the partials (row-normalised, divided by r).
+hipError_t launch_score_finalize(const Shape& s, const float* ws, float* block_scores,
+                                 hipStream_t st);
+
+// Stage 3: per-row minimal-set selection.
+struct TauArray {
+  float v[256];
+};
+hipError_t launch_select(const Shape& s, const float* block_scores, const TauArray& tau,
+                         uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st);
+
+// Stage 4: attention over listed key blocks (kv_idx == nullptr: every candidate).
+hipError_t launch_attn_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
+                            const uint16_t* v, const int32_t* kv_idx, const int32_t* kv_cnt,
+                            float sm_scale, uint16_t* out, float* lse, hipStream_t st);
+hipError_t launch_attn_f32(const Shape& s, const float* q, const float* k, const float* v,
+                           const int32_t* kv_idx, const int32_t* kv_cnt, float sm_scale,
+                           float* out, float* lse, hipStream_t st);
+
+}  // namespace xattn

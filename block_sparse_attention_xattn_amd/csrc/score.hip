@@ -1,0 +1,383 @@
+// Stages 1-2: strided antidiagonal scoring and softmax-normalised block scores.
+//
+// Definition ("XAttention: Block Sparse Attention with Antidiagonal Scoring":
+// arXiv abstract — antidiagonal sums, lower-left to upper-right, rank block
+// importance; AI summary, "Approach" — strided sums within each block,
+// softmax-normalised; "DuSA ..." rebuttal, "Response to Q2" — Q and K are
+// reshaped to (M/stride, stride*C) and a softmax attention runs on them):
+//   A'[i][j] = sum_{s<S} q[i*S+s] . k[j*S+S-1-s],  logit = score_scale * A',
+//   causal: j <= i at the strided level; softmax over j per strided row i;
+//   block score [I][J] = (1/r) sum_{i in I, j in J} p[i][j].
+//
+// Design: the strided logits are an R x R x (S*C) GEMM per head. The
+// (M/S)^2 logit matrix never reaches HBM. Each 128 x 128 output tile
+// reduces, in registers, every (strided row i, key block J) cell to a partial
+// log2-sum-exp L[J][i]; a second kernel turns each query-block row of partials
+// into normalised block scores. Partials are written J-major so a wave's 32
+// query rows store 128 contiguous bytes.
+//
+// GEMM (bf16, gfx950 MFMA 32x32x16): S^T = K~' Q'^T, 4 waves in a 2x2 grid of
+// 64 x 64 sub-tiles, the S*C contraction streamed in 64-element chunks through
+// a double-buffered LDS tile. K~' row j, chunk c is the contiguous run
+// k[j*S + S-1 - (64c)/C][(64c)%C ...] — the stride group read in reverse, so
+// the reversal costs only address arithmetic.
+#include "common.h"
+#include "kernels.h"
+
+namespace xattn {
+
+struct ScoreArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  float* ws;
+  int B, Hq, Hkv, M, S, R, NB;
+  int T;          // strided 128-tiles per head: ceil(R / 128)
+  int pairs;      // tile pairs per head
+  float scale2;   // score_scale * log2(e)
+};
+
+constexpr int SC_TILE = 128;
+constexpr int SC_KC = 64;             // contraction chunk (elements)
+constexpr int SC_P = SC_KC + 8;       // LDS row pitch: 144 B (16 B mod 128 B)
+constexpr int SC_OP = SC_TILE * SC_P; // elements per operand buffer
+
+__device__ __forceinline__ void tile_pair(int p, bool causal, int T, int& tq, int& tk) {
+  if (!causal) {
+    tq = p / T;
+    tk = p % T;
+    return;
+  }
+  int x = (int)((sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
+  while ((x + 1) * (x + 2) / 2 <= p) ++x;
+  while (x * (x + 1) / 2 > p) --x;
+  tq = x;
+  tk = p - x * (x + 1) / 2;
+}
+
+template <int C, int RB, bool CAUSAL>
+__global__ __launch_bounds__(256) void score_partials_bf16_kernel(ScoreArgs a) {
+  static_assert(RB == 2 || RB == 4 || RB == 8 || RB == 16 || RB == 32, "r");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * SC_OP];
+  uint16_t* Ks = smem;               // [2][128][SC_P]  strided keys (A operand)
+  uint16_t* Qs = smem + 2 * SC_OP;   // [2][128][SC_P]  strided queries (B operand)
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wk = wave >> 1, wq = wave & 1;
+
+  const uint32_t n_items = (uint32_t)a.B * a.Hq * a.pairs;
+  const uint32_t item = xcd_group4(blockIdx.x, n_items);
+  const int G = a.Hq / a.Hkv;
+  const int hq_in = item % G;
+  uint32_t rest = item / G;
+  const int pair = rest % a.pairs;
+  rest /= a.pairs;
+  const int g = rest % a.Hkv;
+  const int b = rest / a.Hkv;
+  const int h = g * G + hq_in;
+  int tq, tk;
+  tile_pair(pair, CAUSAL, a.T, tq, tk);
+
+  const size_t bh = (size_t)b * a.Hq + h, bg = (size_t)b * a.Hkv + g;
+  const uint16_t* qh = a.q + bh * a.M * C;
+  const uint16_t* kh = a.k + bg * a.M * C;
+  const int i0 = tq * SC_TILE, j0 = tk * SC_TILE;  // strided row / key origin
+  const int S = a.S;
+  const int n_chunks = S * C / SC_KC;
+
+  // global -> register staging: 128 rows x 128 B per operand = 1024 x 16 B
+  u32x4 kreg[4], qreg[4];
+  auto load_chunk = [&](int c) {
+    const int srow = (SC_KC * c) / C, col0 = (SC_KC * c) % C;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int id = tid + 256 * p;
+      const int row = id >> 3, col = col0 + (id & 7) * 8;
+      const int j = j0 + row, i = i0 + row;
+      kreg[p] = (j < a.R) ? *reinterpret_cast<const u32x4*>(kh + (size_t)(j * S + S - 1 - srow) * C + col)
+                          : u32x4{0u, 0u, 0u, 0u};
+      qreg[p] = (i < a.R) ? *reinterpret_cast<const u32x4*>(qh + (size_t)(i * S + srow) * C + col)
+                          : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int id = tid + 256 * p;
+      const int row = id >> 3, col = (id & 7) * 8;
+      *reinterpret_cast<u32x4*>(Ks + buf * SC_OP + row * SC_P + col) = kreg[p];
+      *reinterpret_cast<u32x4*>(Qs + buf * SC_OP + row * SC_P + col) = qreg[p];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  for (int c = 0; c < n_chunks; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < n_chunks;
+    if (more) load_chunk(c + 1);
+    const uint16_t* Kb = Ks + buf * SC_OP + (64 * wk + l32) * SC_P + 8 * hh;
+    const uint16_t* Qb = Qs + buf * SC_OP + (64 * wq + l32) * SC_P + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < SC_KC / 16; ++ks) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        af[x] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Kb + 32 * x * SC_P + 16 * ks));
+        bfr[x] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Qb + 32 * x * SC_P + 16 * ks));
+      }
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
+    }
+    if (more) store_chunk(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: acc[x][y][r] is strided key j = j0 + 64wk + 32x + 8(r/4) + 4hh + r%4,
+  //      strided query i = i0 + 64wq + 32y + l32. Reduce each run of RB keys.
+  float* wsh = a.ws + bh * (size_t)a.NB * a.R;
+#pragma unroll
+  for (int y = 0; y < 2; ++y) {
+    const int i = i0 + 64 * wq + 32 * y + l32;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int jb = j0 + 64 * wk + 32 * x;  // first strided key of this 32-key sub-tile
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = jb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        float xv = acc[x][y][r] * a.scale2;
+        if ((CAUSAL && j > i) || j >= a.R) xv = -INFINITY;
+        v[r] = xv;
+      }
+      if constexpr (RB <= 4) {
+        // each run of RB keys lies inside one lane's group of 4 registers
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += RB) {
+          float m = v[r0];
+#pragma unroll
+          for (int u = 1; u < RB; ++u) m = fmaxf(m, v[r0 + u]);
+          float s = 0.f;
+          if (m != -INFINITY) {
+#pragma unroll
+            for (int u = 0; u < RB; ++u) s += exp2f(v[r0 + u] - m);
+          }
+          const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
+          const int j = jb + 8 * (r0 >> 2) + 4 * hh + (r0 & 3);
+          const int J = j / RB;
+          if (i < a.R && j < a.R) wsh[(size_t)J * a.R + i] = Lv;
+        }
+      } else {
+        // a run of RB >= 8 keys = registers [4q .. 4q + RB/2) in both wave halves
+        constexpr int NR = RB / 2;  // registers per half per run
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += NR) {
+          float m = v[r0];
+#pragma unroll
+          for (int u = 1; u < NR; ++u) m = fmaxf(m, v[r0 + u]);
+          m = fmaxf(m, xor32(m));
+          float s = 0.f;
+          if (m != -INFINITY) {
+#pragma unroll
+            for (int u = 0; u < NR; ++u) s += exp2f(v[r0 + u] - m);
+          }
+          s += xor32(s);
+          const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
+          const int j = jb + 8 * (r0 >> 2);
+          const int J = j / RB;
+          if (hh == 0 && i < a.R && j < a.R) wsh[(size_t)J * a.R + i] = Lv;
+        }
+      }
+    }
+  }
+}
+
+// fp32 inputs: one thread per (strided row i, key block J), plain FMA.
+struct ScoreArgsF32 {
+  const float* q;
+  const float* k;
+  float* ws;
+  int B, Hq, Hkv, M, C, S, R, NB, r, causal;
+  float scale2;
+};
+
+__global__ __launch_bounds__(256) void score_partials_f32_kernel(ScoreArgsF32 a) {
+  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t per_head = (size_t)a.R * a.NB;
+  const size_t total = per_head * a.B * a.Hq;
+  if (gid >= total) return;
+  const size_t bh = gid / per_head;
+  const int rem = (int)(gid % per_head);
+  const int J = rem / a.R, i = rem % a.R;
+  const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
+  const int g = h / (a.Hq / a.Hkv);
+  if (a.causal && J > i / a.r) return;   // never read by the finalize pass
+  const float* qh = a.q + bh * (size_t)a.M * a.C;
+  const float* kh = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.M * a.C;
+  float m = -INFINITY, s = 0.f;
+  for (int u = 0; u < a.r; ++u) {
+    const int j = J * a.r + u;
+    if (a.causal && j > i) break;
+    float dot = 0.f;
+    for (int st = 0; st < a.S; ++st) {
+      const float* qr = qh + (size_t)(i * a.S + st) * a.C;
+      const float* kr = kh + (size_t)(j * a.S + a.S - 1 - st) * a.C;
+      for (int c = 0; c < a.C; ++c) dot = fmaf(qr[c], kr[c], dot);
+    }
+    const float x = dot * a.scale2;
+    const float mn = fmaxf(m, x);
+    s = s * exp2f(m - mn) + exp2f(x - mn);
+    m = mn;
+  }
+  a.ws[bh * per_head + (size_t)J * a.R + i] = (m == -INFINITY) ? -INFINITY : m + log2f(s);
+}
+
+// Block scores from partials: one workgroup per (b, h, I).
+struct FinalizeArgs {
+  const float* ws;
+  float* out;
+  int B, Hq, R, NB, r, causal;
+};
+
+template <int RB>
+__global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
+  __shared__ float red_m[4][32], red_s[4][32];
+  __shared__ float lse[32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const size_t row = blockIdx.x;  // bh * NB + I
+  const int I = (int)(row % a.NB);
+  const size_t bh = row / a.NB;
+  const int n_cand = a.causal ? I + 1 : a.NB;
+  const float* L = a.ws + bh * (size_t)a.NB * a.R + (size_t)I * a.r;
+  constexpr int r = RB;
+
+  // pass 1: per strided row t, log2-sum-exp over candidate blocks
+  float m[RB], s[RB];
+#pragma unroll
+  for (int t = 0; t < r; ++t) { m[t] = -INFINITY; s[t] = 0.f; }
+  for (int J = tid; J < n_cand; J += 256) {
+    const float* p = L + (size_t)J * a.R;
+#pragma unroll
+    for (int t = 0; t < r; ++t) {
+      const float x = p[t];
+      const float mn = fmaxf(m[t], x);
+      if (mn != -INFINITY) {
+        s[t] = s[t] * exp2f(m[t] - mn) + exp2f(x - mn);
+        m[t] = mn;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < r; ++t) {
+    float mt = m[t], stv = s[t];
+    for (int off = 32; off > 0; off >>= 1) {
+      const float mo = __shfl_xor(mt, off, 64), so = __shfl_xor(stv, off, 64);
+      const float mn = fmaxf(mt, mo);
+      if (mn != -INFINITY) {
+        stv = stv * exp2f(mt - mn) + so * exp2f(mo - mn);
+        mt = mn;
+      }
+    }
+    if (lane == 0) { red_m[wave][t] = mt; red_s[wave][t] = stv; }
+  }
+  __syncthreads();
+  if (tid < r) {
+    float mt = -INFINITY, stv = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const float mo = red_m[w][tid], so = red_s[w][tid];
+      const float mn = fmaxf(mt, mo);
+      if (mn != -INFINITY) {
+        stv = stv * exp2f(mt - mn) + so * exp2f(mo - mn);
+        mt = mn;
+      }
+    }
+    lse[tid] = mt + log2f(stv);
+  }
+  __syncthreads();
+
+  // pass 2: block score = (1/r) sum_t 2^(L[J][t] - lse_t)
+  float* orow = a.out + row * a.NB;
+  const float inv_r = 1.f / (float)r;
+  for (int J = tid; J < a.NB; J += 256) {
+    float sc = 0.f;
+    if (J < n_cand) {
+      const float* p = L + (size_t)J * a.R;
+#pragma unroll
+      for (int t = 0; t < r; ++t) sc += exp2f(p[t] - lse[t]);
+      sc *= inv_r;
+    }
+    orow[J] = sc;
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+
+template <int C, int RB>
+static hipError_t launch_partials_cr(const Shape& s, const ScoreArgs& a, hipStream_t st) {
+  const unsigned grid = (unsigned)((size_t)s.B * s.Hq * a.pairs);
+  if (s.causal)
+    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, true>), dim3(grid), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, false>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int C>
+static hipError_t launch_partials_c(const Shape& s, const ScoreArgs& a, hipStream_t st) {
+  switch (s.r()) {
+    case 2: return launch_partials_cr<C, 2>(s, a, st);
+    case 4: return launch_partials_cr<C, 4>(s, a, st);
+    case 8: return launch_partials_cr<C, 8>(s, a, st);
+    case 16: return launch_partials_cr<C, 16>(s, a, st);
+    case 32: return launch_partials_cr<C, 32>(s, a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
+                                      float score_scale, float* ws, hipStream_t st) {
+  const int R = s.R();
+  const int T = (R + SC_TILE - 1) / SC_TILE;
+  const int pairs = s.causal ? T * (T + 1) / 2 : T * T;
+  ScoreArgs a{q, k, ws, s.B, s.Hq, s.Hkv, s.M, s.stride, R, s.NB(), T, pairs,
+              score_scale * kLog2e};
+  if (s.C == 128) return launch_partials_c<128>(s, a, st);
+  if (s.C == 64) return launch_partials_c<64>(s, a, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_score_partials_f32(const Shape& s, const float* q, const float* k,
+                                     float score_scale, float* ws, hipStream_t st) {
+  ScoreArgsF32 a{q, k, ws, s.B, s.Hq, s.Hkv, s.M, s.C, s.stride, s.R(), s.NB(), s.r(),
+                 s.causal, score_scale * kLog2e};
+  const size_t total = (size_t)s.R() * s.NB() * s.B * s.Hq;
+  hipLaunchKernelGGL(score_partials_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_finalize(const Shape& s, const float* ws, float* block_scores,
+                                 hipStream_t st) {
+  FinalizeArgs a{ws, block_scores, s.B, s.Hq, s.R(), s.NB(), s.r(), s.causal};
+  const dim3 grid((unsigned)((size_t)s.B * s.Hq * s.NB()));
+  switch (s.r()) {
+    case 2: hipLaunchKernelGGL(score_finalize_kernel<2>, grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(score_finalize_kernel<4>, grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(score_finalize_kernel<8>, grid, dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL(score_finalize_kernel<16>, grid, dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(score_finalize_kernel<32>, grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace xattn

@@ -1,0 +1,186 @@
+/*
+ * xattn.h — C ABI of the MI355X (gfx950) XAttention-style block-sparse
+ * prefill attention library (libxattn.so).
+ *
+ * The method (sources are web pages; cited by page title and section):
+ *   [XA-abs] "XAttention: Block Sparse Attention with Antidiagonal Scoring",
+ *            arXiv abstract: the sum of antidiagonal values (lower-left to
+ *            upper-right) of the attention matrix ranks block importance;
+ *            block-sparse attention then runs on the important blocks.
+ *   [XA-sum] same title, AI summary page, "Approach": strided antidiagonal sums
+ *            inside each block, softmax-normalised, then the minimal set of
+ *            blocks whose mass reaches a per-head threshold.
+ *   [DuSA]   "DuSA: Fast and Accurate Dual-Stage Sparse Attention Mechanism
+ *            Accelerating Both Training and Inference", rebuttal, "Response to
+ *            Q2": Q and K of shape (B, H, M, C) are reshaped to
+ *            (B, H, M/stride, stride*C) and a softmax attention is computed on
+ *            the reshaped tensors.
+ *   [Flex]   "FlexPrefill: ...", rebuttal, "R Q2: Integration Feasibility":
+ *            a single function call replacing standard attention.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Q is (B, Hq, M, C); K and V are (B, Hkv, M, C); O has Q's shape. All are
+ *    contiguous row-major DEVICE buffers of the problem dtype. Query head h
+ *    reads KV head h / (Hq / Hkv) (grouped-query attention).
+ *  - Block size Bk = p->block, stride S = p->stride, NB = M / Bk blocks,
+ *    R = M / S strided rows, r = Bk / S strided rows per block.
+ *  - Block tensors are (B, Hq, NB, NB) row-major, indexed [b][h][I][J]
+ *    (query block I, key block J).
+ *  - The caller owns and allocates every buffer. The library keeps no state,
+ *    never allocates, and is re-entrant; scratch memory comes only through
+ *    the workspace argument.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *    call only enqueues work on it and returns without synchronising.
+ *  - Arguments are validated on the host before anything is enqueued. On any
+ *    error the call returns a non-zero status and enqueues nothing; a failed
+ *    kernel launch returns XATTN_ERR_HIP. xattn_last_error() gives a message
+ *    for the calling thread's last failure. No C++ exception crosses the ABI.
+ *  - NaN or Inf inside Q/K/V gives unspecified values in the outputs; the
+ *    kernels still terminate and stay within the buffers.
+ *
+ * Supported shapes: dtype XATTN_BF16 or XATTN_F32; C in {64, 128};
+ * block in {64, 128}; r = block/stride in {2, 4, 8, 16, 32};
+ * M a positive multiple of block with NB <= 4096; 1 <= Hq <= 256;
+ * Hq a multiple of Hkv; causal in {0, 1}.
+ */
+#ifndef XATTN_H
+#define XATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define XATTN_ABI_VERSION 1
+#define XATTN_MAX_HEADS 256
+#define XATTN_MAX_BLOCKS 4096
+
+typedef enum {
+  XATTN_OK = 0,
+  XATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  XATTN_ERR_SHAPE = 2,       /* sizes inconsistent (divisibility, ranges) */
+  XATTN_ERR_DTYPE = 3,       /* unknown dtype */
+  XATTN_ERR_ARG = 4,         /* a scalar argument is out of range (tau, scales) */
+  XATTN_ERR_UNSUPPORTED = 5, /* valid but not implemented (C, block, r) */
+  XATTN_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+  XATTN_ERR_HIP = 7          /* the HIP runtime reported an error at launch */
+} xattn_status;
+
+typedef enum { XATTN_BF16 = 0, XATTN_F32 = 1 } xattn_dtype;
+
+/* Problem description. All fields are plain int32. */
+typedef struct {
+  int32_t B;      /* batch */
+  int32_t Hq;     /* query heads */
+  int32_t Hkv;    /* key/value heads, divides Hq */
+  int32_t M;      /* sequence length (queries = keys) */
+  int32_t C;      /* head dimension */
+  int32_t block;  /* block size Bk (queries and keys) */
+  int32_t stride; /* antidiagonal stride S, divides block */
+  int32_t causal; /* 1: key j visible to query i iff j <= i; 0: all keys */
+  int32_t dtype;  /* xattn_dtype of Q, K, V and O */
+} xattn_problem;
+
+/* ABI version of the loaded library (XATTN_ABI_VERSION). */
+int32_t xattn_abi_version(void);
+
+/* Static description of a status code. */
+const char* xattn_status_string(xattn_status s);
+
+/* Message describing the calling thread's most recent failed call. */
+const char* xattn_last_error(void);
+
+/* Device workspace bytes xattn_score (and xattn_prefill) need for problem p;
+ * 0 if p is invalid. The workspace holds per-(strided row, key block) partial
+ * log-sum-exp values: B*Hq*NB*R float32. */
+size_t xattn_score_workspace_bytes(const xattn_problem* p);
+
+/*
+ * Stage 1+2 — strided antidiagonal block scores ([XA-abs]; [XA-sum] Approach;
+ * [DuSA] Response to Q2).
+ *
+ * For strided query row i and strided key row j (i, j < R):
+ *   A'[i][j] = sum_{s<S} dot(q[i*S+s], k[j*S+S-1-s]),  logit = score_scale*A'.
+ * Causal problems keep j <= i. Each strided row is softmax-normalised over its
+ * keys, and the probabilities are summed over each r x r tile:
+ *   block_scores[b][h][I][J] = (1/r) * sum_{i in I, j in J} softmax_j(logit[i][j]).
+ * Every row of block_scores sums to 1; causal entries with J > I are 0.
+ *
+ *  q, k          device, problem dtype, layouts above.
+ *  score_scale   > 0 and finite (e.g. 1/(S*sqrt(C)): the mean antidiagonal logit).
+ *  block_scores  device float32 (B, Hq, NB, NB), fully written.
+ *  ws, ws_bytes  device scratch of at least xattn_score_workspace_bytes(p).
+ */
+xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k,
+                         float score_scale, float* block_scores, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * Stage 3 — minimal-set threshold selection ([XA-sum] Approach: the minimal
+ * set of blocks whose normalised mass exceeds the per-head threshold;
+ * [Flex] R Q3: minimal |S| under the cumulative-mass constraint).
+ *
+ * Per row (b, h, I): candidates are J <= I (causal) or all J. They are ordered
+ * by score descending, ties by J ascending; with prefix masses c_k (float64)
+ * and total T = c_n, the kept set is the first k* = min{k >= 0 : c_k >= tau_h*T}
+ * candidates (tau_h >= 1 keeps all). The diagonal block J = I is then added.
+ *
+ *  block_scores  device float32 (B, Hq, NB, NB), as written by xattn_score.
+ *  tau           HOST array of Hq floats, each in [0, 1] (copied at the call).
+ *  mask          device uint8 (B, Hq, NB, NB) or NULL; 1 = kept.
+ *  kv_idx        device int32 (B, Hq, NB, NB): per row the kept J in ascending
+ *                order; only the first kv_cnt entries of a row are written.
+ *  kv_cnt        device int32 (B, Hq, NB): kept blocks per row (>= 1).
+ */
+xattn_status xattn_select(const xattn_problem* p, const float* block_scores,
+                          const float* tau, uint8_t* mask, int32_t* kv_idx,
+                          int32_t* kv_cnt, void* stream);
+
+/*
+ * Stage 4 — block-sparse attention forward ([XA-abs]: block-sparse attention
+ * computes only on the important blocks).
+ *
+ * For query i in block I of head h:
+ *   O[i] = sum_{j in A(i)} softmax_j(sm_scale * q_i . k_j) v_j,
+ *   A(i) = union of key blocks kv_idx[b][h][I][0 .. kv_cnt-1], intersected
+ *          with j <= i when causal.
+ *
+ *  kv_idx, kv_cnt  device int32 as produced by xattn_select; each listed J
+ *                  must be in [0, NB) (and <= I when causal), kv_cnt in
+ *                  [1, NB], and for causal problems the list must hold J = I.
+ *  sm_scale        > 0 and finite (usually 1/sqrt(C)).
+ *  out             device, problem dtype, (B, Hq, M, C).
+ *  lse             device float32 (B, Hq, M), natural-log log-sum-exp of the
+ *                  scaled logits over A(i); may be NULL.
+ */
+xattn_status bsa_fwd(const xattn_problem* p, const void* q, const void* k,
+                     const void* v, const int32_t* kv_idx, const int32_t* kv_cnt,
+                     float sm_scale, void* out, float* lse, void* stream);
+
+/*
+ * Dense attention forward: bsa_fwd with every candidate block kept (all
+ * J <= I when causal, all J otherwise). The reference point for speedups.
+ */
+xattn_status dense_fwd(const xattn_problem* p, const void* q, const void* k,
+                       const void* v, float sm_scale, void* out, float* lse,
+                       void* stream);
+
+/*
+ * The three stages in one call ([Flex] R Q2: one call in place of standard
+ * attention): xattn_score, then xattn_select, then bsa_fwd, all enqueued on
+ * `stream`. Arguments as in those calls; mask and lse may be NULL.
+ */
+xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
+                           const void* v, const float* tau, float score_scale,
+                           float sm_scale, float* block_scores, uint8_t* mask,
+                           int32_t* kv_idx, int32_t* kv_cnt, void* ws,
+                           size_t ws_bytes, void* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XATTN_H */

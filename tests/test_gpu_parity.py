@@ -1,0 +1,270 @@
+"""GPU parity: every stage of the HIP path against the CPU oracle, element by
+element, through the C ABI (via the thin ctypes binding).
+
+Tolerances (from the method's acceptance bar):
+  block scores |g - o| <= 1e-4 |o| + 1e-7;  bf16 outputs max-abs <= 2e-2;
+  fp32 outputs max-abs <= 1e-3;  masks identical up to near-tau blocks.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests.gpu_util import check_index, f64, mask_mismatches, score_tol
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def xa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_xattn_amd as x
+    return x
+
+
+def _rand(shape, seed, dtype, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    t = torch.randn(shape, generator=g) * scale
+    return t.to(dtype)
+
+
+def _inputs(B, Hq, Hkv, M, C, dtype, seed, structured=False):
+    if structured:
+        fam = "llama" if dtype == torch.bfloat16 else "tiny"
+        w = wl.WORKLOADS["llama8k" if fam == "llama" else "tiny"].scaled(B=B, Hq=Hq, Hkv=Hkv, M=M, C=C)
+        x = wl.make_inputs(w)
+        return x["q"], x["k"], x["v"]
+    q = _rand((B, Hq, M, C), seed, dtype)
+    k = _rand((B, Hkv, M, C), seed + 1, dtype)
+    v = _rand((B, Hkv, M, C), seed + 2, dtype)
+    return q, k, v
+
+
+def _bf16_tol(dtype):
+    return 2e-2 if dtype == torch.bfloat16 else 1e-3
+
+
+# ------------------------------------------------------------------ attention
+
+ATTN_CASES = [
+    # B, Hq, Hkv, M, C, block, causal, dtype
+    (1, 4, 2, 512, 128, 128, True, torch.bfloat16),
+    (1, 4, 4, 384, 128, 128, False, torch.bfloat16),
+    (2, 2, 1, 256, 64, 64, True, torch.bfloat16),
+    (1, 2, 2, 256, 64, 128, False, torch.bfloat16),
+    (1, 8, 2, 128, 128, 128, True, torch.bfloat16),   # a single block
+    (1, 2, 1, 256, 128, 64, True, torch.bfloat16),
+    (1, 1, 1, 512, 64, 64, True, torch.float32),
+    (1, 2, 1, 256, 128, 128, False, torch.float32),
+]
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "-".join(map(str, c[:7])) + str(c[7])[-4:])
+def test_dense_fwd_matches_oracle(xa, case):
+    B, Hq, Hkv, M, C, block, causal, dtype = case
+    q, k, v = _inputs(B, Hq, Hkv, M, C, dtype, 100 + M)
+    scale = 1.0 / math.sqrt(C)
+    out, lse = xa.dense_fwd(q.to(DEV), k.to(DEV), v.to(DEV), block, scale, causal, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.dense(f64(q), f64(k), f64(v), block, scale, causal)
+    err = np.abs(f64(out) - ref).max()
+    assert err <= _bf16_tol(dtype), err
+    assert np.abs(f64(lse) - ref_lse).max() <= 2e-3
+
+
+@pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "-".join(map(str, c[:7])) + str(c[7])[-4:])
+def test_bsa_fwd_matches_oracle_with_given_mask(xa, case):
+    B, Hq, Hkv, M, C, block, causal, dtype = case
+    q, k, v = _inputs(B, Hq, Hkv, M, C, dtype, 200 + M)
+    nb = M // block
+    rng = np.random.default_rng(M + Hq)
+    mask = (rng.random((B, Hq, nb, nb)) < 0.35).astype(np.uint8)
+    mask[..., np.arange(nb), np.arange(nb)] = 1
+    if causal:
+        mask *= np.tril(np.ones((nb, nb), dtype=np.uint8))
+    idx, cnt = oracle.mask_to_index(mask)
+    scale = 1.0 / math.sqrt(C)
+    out, lse = xa.bsa_fwd(q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(idx).to(DEV),
+                          torch.from_numpy(cnt).to(DEV), block, scale, causal, want_lse=True)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.attend(f64(q), f64(k), f64(v), mask, block, scale, causal)
+    err = np.abs(f64(out) - ref).max()
+    assert err <= _bf16_tol(dtype), err
+    assert np.abs(f64(lse) - ref_lse).max() <= 2e-3
+
+
+# ------------------------------------------------------------------ scoring
+
+SCORE_CASES = [
+    # B, Hq, Hkv, M, C, block, stride, causal, dtype, structured
+    (1, 4, 1, 2048, 128, 128, 8, True, torch.bfloat16, True),
+    (1, 4, 2, 2048, 128, 128, 16, True, torch.bfloat16, True),
+    (1, 2, 2, 1280, 128, 128, 8, False, torch.bfloat16, False),
+    (1, 2, 1, 1024, 64, 64, 8, True, torch.bfloat16, False),
+    (1, 2, 1, 512, 128, 128, 4, True, torch.bfloat16, False),    # r = 32
+    (1, 2, 1, 512, 64, 64, 32, True, torch.bfloat16, False),     # r = 2
+    (1, 1, 1, 256, 128, 128, 32, False, torch.bfloat16, False),  # r = 4, R < one tile
+    (1, 1, 1, 1024, 64, 64, 8, True, torch.float32, True),       # the tiny fp32 workload
+    (1, 2, 1, 512, 128, 128, 16, False, torch.float32, False),
+]
+
+
+@pytest.mark.parametrize("case", SCORE_CASES, ids=lambda c: "-".join(map(str, c[:8])) + str(c[8])[-4:])
+def test_score_matches_oracle(xa, case):
+    B, Hq, Hkv, M, C, block, stride, causal, dtype, structured = case
+    q, k, _ = _inputs(B, Hq, Hkv, M, C, dtype, 300 + M, structured)
+    sscale = 1.0 / (stride * math.sqrt(C))
+    got = xa.xattn_score(q.to(DEV), k.to(DEV), block, stride, sscale, causal)
+    torch.cuda.synchronize()
+    ref = oracle.block_scores(f64(q), f64(k), block, stride, sscale, causal)
+    g = got.cpu().numpy().astype(np.float64)
+    assert (g >= 0).all()
+    viol = np.abs(g - ref) > score_tol(ref)
+    assert not viol.any(), (np.argwhere(viol)[:5], np.abs(g - ref).max())
+    np.testing.assert_allclose(g.sum(-1), 1.0, rtol=1e-4)
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.5, 0.9, 0.95, 1.0])
+@pytest.mark.parametrize("causal", [True, False])
+def test_select_matches_oracle_on_same_scores(xa, tau, causal):
+    B, Hq, nb = 1, 3, 40
+    rng = np.random.default_rng(int(tau * 100) + causal)
+    raw = rng.gamma(0.3, size=(B, Hq, nb, nb))
+    raw[..., :, 3] *= 0.0       # exact zeros
+    raw[..., :, 5] = raw[..., :, 6]  # exact ties
+    if causal:
+        raw *= np.tril(np.ones((nb, nb)))
+    raw /= raw.sum(-1, keepdims=True)
+    scores = torch.from_numpy(raw.astype(np.float32))
+    taus = [tau, min(1.0, tau + 0.03), max(0.0, tau - 0.2)]
+    mask, idx, cnt = xa.xattn_select(scores.to(DEV), taus, 128, 8, causal, Hkv=Hq)
+    torch.cuda.synchronize()
+    s64 = scores.numpy().astype(np.float64)
+    ref = oracle.select(s64, taus, causal)
+    m = mask.cpu().numpy()
+    n_diff, bad = mask_mismatches(m, ref, s64, np.array(taus), causal, 1e-5)
+    assert not bad, bad[:5]
+    check_index(m, idx.cpu().numpy(), cnt.cpu().numpy())
+
+
+# ------------------------------------------------------------------ end to end
+
+E2E_CASES = [
+    # workload name, overrides
+    ("tiny", {}),
+    ("llama8k", dict(M=2048, Hq=8, Hkv=2)),
+    ("llama32k", dict(M=2048, Hq=8, Hkv=2)),
+    ("llama128k", dict(M=4096, Hq=4, Hkv=1)),
+    ("video", dict(M=2560, Hq=2, Hkv=2)),
+]
+
+
+@pytest.mark.parametrize("name,over", E2E_CASES, ids=[c[0] for c in E2E_CASES])
+def test_prefill_end_to_end(xa, name, over):
+    w = wl.WORKLOADS[name].scaled(**over)
+    x = wl.make_inputs(w)
+    sscale, smscale = wl.default_scales(w)
+    qd, kd, vd = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    bufs = xa.xattn_prefill(qd, kd, vd, x["tau"], w.block, w.stride, sscale, smscale, w.causal)
+    torch.cuda.synchronize()
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    tau = x["tau"].numpy().astype(np.float64)
+    ref_sc = oracle.block_scores(q, k, w.block, w.stride, sscale, w.causal)
+    g_sc = bufs.block_scores.cpu().numpy().astype(np.float64)
+    assert not (np.abs(g_sc - ref_sc) > score_tol(ref_sc)).any()
+    g_mask = bufs.mask.cpu().numpy()
+    # selection parity on the GPU's own scores
+    same = oracle.select(g_sc, tau, w.causal)
+    _, bad = mask_mismatches(g_mask, same, g_sc, tau, w.causal, 1e-5)
+    assert not bad, bad[:5]
+    # end to end: differences only where the score tolerance can move the cut
+    ref_mask = oracle.select(ref_sc, tau, w.causal)
+    band = 1e-5 + 1e-4 + w.nb * 1e-7
+    _, bad = mask_mismatches(g_mask, ref_mask, ref_sc, tau, w.causal, band)
+    assert not bad, bad[:5]
+    check_index(g_mask, bufs.kv_idx.cpu().numpy(), bufs.kv_cnt.cpu().numpy())
+    # attention parity with the GPU's mask (isolates the attention stage)
+    ref_out, _ = oracle.attend(q, k, v, g_mask, w.block, smscale, w.causal)
+    err = np.abs(f64(bufs.out) - ref_out).max()
+    assert err <= (2e-2 if w.dtype == "bf16" else 1e-3), err
+    # invariants
+    nb = w.nb
+    assert g_mask[..., np.arange(nb), np.arange(nb)].all()
+    if w.causal:
+        assert not g_mask[..., np.triu(np.ones((nb, nb), dtype=bool), 1)].any()
+
+
+def test_tau_one_selects_all_and_equals_dense(xa):
+    w = wl.WORKLOADS["llama8k"].scaled(M=1024, Hq=4, Hkv=1)
+    x = wl.make_inputs(w)
+    sscale, smscale = wl.default_scales(w)
+    qd, kd, vd = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    bufs = xa.xattn_prefill(qd, kd, vd, [1.0] * 4, w.block, w.stride, sscale, smscale, True)
+    dense, _ = xa.dense_fwd(qd, kd, vd, w.block, smscale, True)
+    torch.cuda.synchronize()
+    nb = w.nb
+    assert (bufs.mask.cpu().numpy() == np.tril(np.ones((nb, nb), dtype=np.uint8))).all()
+    assert torch.equal(bufs.out, dense)
+
+
+def test_repeat_runs_are_bitwise_identical(xa):
+    w = wl.WORKLOADS["llama32k"].scaled(M=2048, Hq=8, Hkv=2)
+    x = wl.make_inputs(w)
+    sscale, smscale = wl.default_scales(w)
+    qd, kd, vd = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    a = xa.xattn_prefill(qd, kd, vd, x["tau"], w.block, w.stride, sscale, smscale, True)
+    b = xa.xattn_prefill(qd, kd, vd, x["tau"], w.block, w.stride, sscale, smscale, True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.block_scores, b.block_scores)
+    assert torch.equal(a.mask, b.mask)
+    assert torch.equal(a.out, b.out)
+
+
+def test_outputs_stay_inside_buffers(xa):
+    # guard regions around every output must be untouched
+    B, Hq, Hkv, M, C, block = 1, 4, 1, 1024, 128, 128
+    q, k, v = _inputs(B, Hq, Hkv, M, C, torch.bfloat16, 7)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    nb = M // block
+    guard = 4096
+    def guarded(n, dtype, fill):
+        t = torch.full((n + 2 * guard,), fill, dtype=dtype, device=DEV)
+        return t, t[guard:guard + n]
+    sc_all, sc = guarded(B * Hq * nb * nb, torch.float32, -7.0)
+    mk_all, mk = guarded(B * Hq * nb * nb, torch.uint8, 0xAB)
+    ix_all, ix = guarded(B * Hq * nb * nb, torch.int32, -5)
+    ct_all, ct = guarded(B * Hq * nb, torch.int32, -5)
+    out_all, out = guarded(B * Hq * M * C, torch.bfloat16, 3.0)
+    lse_all, lse = guarded(B * Hq * M, torch.float32, -7.0)
+    p = xa.problem(B, Hq, Hkv, M, C, block, 8, 1, torch.bfloat16)
+    ws = torch.empty(xa.workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    tau = torch.full((Hq,), 0.9)
+    import ctypes
+    st = torch.cuda.current_stream().cuda_stream
+    rc = xa._lib.xattn_prefill(ctypes.byref(p), qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), tau.data_ptr(),
+                               1 / (8 * math.sqrt(C)), 1 / math.sqrt(C), sc.data_ptr(), mk.data_ptr(),
+                               ix.data_ptr(), ct.data_ptr(), ws.data_ptr(), ws.numel(), out.data_ptr(),
+                               lse.data_ptr(), st)
+    assert rc == 0
+    torch.cuda.synchronize()
+    for full, fill in ((sc_all, -7.0), (mk_all, 0xAB), (ix_all, -5), (ct_all, -5), (out_all, 3.0),
+                       (lse_all, -7.0)):
+        assert (full[:guard] == fill).all() and (full[-guard:] == fill).all()
+
+
+def test_nonfinite_inputs_terminate(xa):
+    B, Hq, Hkv, M, C, block = 1, 2, 1, 512, 128, 128
+    q, k, v = _inputs(B, Hq, Hkv, M, C, torch.bfloat16, 9)
+    q[0, 0, 5, 3] = float("nan")
+    k[0, 0, 17, 0] = float("inf")
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    bufs = xa.xattn_prefill(qd, kd, vd, [0.9, 0.9], block, 8, 0.01, 0.08, True)
+    torch.cuda.synchronize()
+    assert bufs.kv_cnt.min().item() >= 1
+    assert bufs.kv_cnt.max().item() <= M // block
