@@ -141,14 +141,17 @@ def _tau_host(tau, hq):
 
 
 def xattn_select(block_scores, tau, block, stride, causal=True, Hkv=None, C=128, dtype=torch.bfloat16,
-                 want_mask=True):
+                 want_mask=True, mask=None, kv_idx=None, kv_cnt=None):
     """(mask u8 or None, kv_idx int32, kv_cnt int32) for block scores (B, Hq, NB, NB)."""
     B, Hq, nb, _ = block_scores.shape
     p = problem(B, Hq, Hkv or Hq, nb * block, C, block, stride, causal, dtype)
     dev = block_scores.device
-    mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev) if want_mask else None
-    kv_idx = torch.empty((B, Hq, nb, nb), dtype=torch.int32, device=dev)
-    kv_cnt = torch.empty((B, Hq, nb), dtype=torch.int32, device=dev)
+    if mask is None and want_mask:
+        mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev)
+    if kv_idx is None:
+        kv_idx = torch.empty((B, Hq, nb, nb), dtype=torch.int32, device=dev)
+    if kv_cnt is None:
+        kv_cnt = torch.empty((B, Hq, nb), dtype=torch.int32, device=dev)
     tau_h = _tau_host(tau, Hq)
     _check(_lib.xattn_select(ctypes.byref(p), _ptr(block_scores), tau_h.data_ptr(), _ptr(mask),
                              _ptr(kv_idx), _ptr(kv_cnt), _stream(dev)))

@@ -37,15 +37,28 @@ struct AttnArgs {
 
 template <int C>
 struct AttnLds {
-  static constexpr int KT = 64;          // keys per sub-tile
-  static constexpr int KP = C + 8;       // K row pitch (elements): 16 B mod 128 B
-  static constexpr int VP = C + 16;      // V row pitch (elements): 32 B mod 128 B
-  static constexpr int K_ELEMS = KT * KP;
-  static constexpr int V_ELEMS = KT * VP;
-  static constexpr int BYTES = 2 * (K_ELEMS + V_ELEMS) * 2;
+  static constexpr int KT = 64;               // keys per sub-tile
+  static constexpr int ROW_B = 2 * C;         // bytes per K or V row (no padding)
+  static constexpr int TILE_B = KT * ROW_B;   // bytes per K (or V) sub-tile
+  static constexpr int ROWS_PER_256 = 256 / ROW_B;
+  static constexpr int IDX_MAX = 4096;        // block-index row cached as uint16
+  static constexpr int BYTES = 2 * 2 * TILE_B + 2 * IDX_MAX;
+  // LDS serves 256 B per clock in 64 banks of 4 B. Rows are stored unpadded and
+  // the 16-byte chunks (K) or 64-byte segments (V) of each row are XOR-permuted
+  // by the row index so that
+  //  * K fragment reads (16 lanes x 16 B, 16 consecutive rows, same column) and
+  //  * V transposing reads (32 lanes x 8 B over 4 consecutive rows x 64 B)
+  // each cover 256 distinct bytes of the bank window, while row-major 16-byte
+  // tile writes stay conflict-free.
+  __device__ static int k_off(int row, int chunk16) {
+    return row * ROW_B + 16 * (chunk16 ^ ((row / ROWS_PER_256) % (C / 8)));
+  }
+  __device__ static int v_off(int row, int byte_in_row) {
+    return row * ROW_B + (byte_in_row ^ (64 * ((row / ROWS_PER_256) % (C / 32))));
+  }
 };
 
-template <int C, int BLK, bool CAUSAL>
+template <int C, int BLK, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   using L = AttnLds<C>;
   constexpr int NT = BLK * 2;                 // threads: BLK/32 waves of 64
@@ -56,9 +69,10 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int DN = C / 32;                  // 32-wide d tiles of O^T
   static_assert(CHUNKS % NT == 0, "tile load must divide evenly");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[L::BYTES / 2];
-  uint16_t* Ks = smem;                          // [2][KT][KP]
-  uint16_t* Vs = smem + 2 * L::K_ELEMS;         // [2][KT][VP]
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
+  unsigned char* Ks = smem;                      // [2][KT rows][2C bytes], swizzled
+  unsigned char* Vs = smem + 2 * L::TILE_B;      // [2][KT rows][2C bytes], swizzled
+  uint16_t* idx_s = reinterpret_cast<uint16_t*>(smem + 4 * L::TILE_B);  // kept key blocks
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -85,11 +99,18 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const uint16_t* vh = a.v + bg * a.M * C;
 
   int cnt;
-  const int32_t* idx = nullptr;
-  if (a.kv_idx) {
+  constexpr bool sparse = SPARSE;
+  if constexpr (SPARSE) {
     cnt = a.kv_cnt[bh * a.NB + I];
     cnt = cnt < 0 ? 0 : (cnt > a.NB ? a.NB : cnt);
-    idx = a.kv_idx + (bh * a.NB + I) * a.NB;
+    // cache the row's block list in LDS once, so no dependent global load sits
+    // in front of each tile fetch; out-of-range entries are clamped
+    const int32_t* idx = a.kv_idx + (bh * a.NB + I) * a.NB;
+    for (int t = tid; t < cnt; t += NT) {
+      int jb = idx[t];
+      jb = jb < 0 ? 0 : (jb >= a.NB ? a.NB - 1 : jb);
+      idx_s[t] = (uint16_t)jb;
+    }
   } else {
     cnt = CAUSAL ? I + 1 : a.NB;
   }
@@ -112,8 +133,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   float l_run = 0.f;
 
   auto key_start = [&](int t) -> int {
-    int jb = idx ? idx[t / SUB] : t / SUB;
-    jb = jb < 0 ? 0 : (jb >= a.NB ? a.NB - 1 : jb);
+    const int jb = sparse ? (int)idx_s[t / SUB] : t / SUB;
     return jb * BLK + (t % SUB) * L::KT;
   };
 
@@ -132,12 +152,13 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int p = 0; p < PER_T; ++p) {
       const int c = tid + p * NT;
-      const int row = c / (C / 8), col = (c % (C / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Ks + buf * L::K_ELEMS + row * L::KP + col) = kreg[p];
-      *reinterpret_cast<u32x4*>(Vs + buf * L::V_ELEMS + row * L::VP + col) = vreg[p];
+      const int row = c / (C / 8), chunk = c % (C / 8);
+      *reinterpret_cast<u32x4*>(Ks + buf * L::TILE_B + L::k_off(row, chunk)) = kreg[p];
+      *reinterpret_cast<u32x4*>(Vs + buf * L::TILE_B + L::v_off(row, 16 * chunk)) = vreg[p];
     }
   };
 
+  __syncthreads();  // block list visible
   if (n_sub > 0) {
     load_tile(0);
     store_tile(0);
@@ -152,8 +173,8 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 
     const bool skip = CAUSAL && (k0 > q0 + 31);  // whole sub-tile above this wave's rows
     if (!skip) {
-      const uint16_t* Kb = Ks + buf * L::K_ELEMS;
-      const uint16_t* Vb = Vs + buf * L::V_ELEMS;
+      const unsigned char* Kb = Ks + buf * L::TILE_B;
+      const unsigned char* Vb = Vs + buf * L::TILE_B;
       // S^T tiles n = 0, 1: keys k0 + 32n + [8(r/4) + 4hh + r%4], query q0 + l32
       f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
@@ -161,7 +182,7 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           const bf16x8 ka = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(Kb + (32 * n + l32) * L::KP + 16 * kk + 8 * hh));
+              bf16x8, *reinterpret_cast<const u32x4*>(Kb + L::k_off(32 * n + l32, 2 * kk + hh)));
           s[n] = mfma32x32x16(ka, qf[kk], s[n]);
         }
       }
@@ -181,15 +202,25 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[n][r]);
       mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx * a.scale_log2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
-      m_run = m_new;
-      l_run *= alpha;
+      // Lazy rescaling (exact): O and l share the reference m_run, so the
+      // reference may lag the true running max as long as 2^(s*c - m_run) stays
+      // small. It is raised only when the tile max exceeds it by more than
+      // 2^8, which bounds P by 256 (fine for bf16 and fp32); the final O / l
+      // is unchanged. The branch is uniform per wave.
+      const float m_tile = mx * a.scale_log2;
+      const bool raise = m_tile > m_run + 8.f;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = fmaxf(m_run, m_tile);
+        // 0 on a lane's first visible tile; 1 while a lane has seen no key
+        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int d = 0; d < DN; ++d)
+        for (int d = 0; d < DN; ++d)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
       bf16x8 pb[4];
 #pragma unroll
@@ -208,9 +239,9 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
         const int vrow = 16 * tc + 4 * (G16 >> 1) + (s16 >> 2);
 #pragma unroll
         for (int d = 0; d < DN; ++d) {
-          const int vcol = 32 * d + 16 * (G16 & 1) + 4 * (s16 & 3);
-          const i16x4 lo = lds_read_tr16(Vb + vrow * L::VP + vcol);
-          const i16x4 hi = lds_read_tr16(Vb + (vrow + 8) * L::VP + vcol);
+          const int vbyte = 2 * (32 * d + 16 * (G16 & 1) + 4 * (s16 & 3));
+          const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow, vbyte)));
+          const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow + 8, vbyte)));
           typedef short i16x8 __attribute__((ext_vector_type(8)));
           const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           o[d] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pb[tc], o[d]);
@@ -311,11 +342,16 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgsF32 a) {
 
 template <int C, int BLK>
 static hipError_t launch_bf16_cb(const Shape& s, const AttnArgs& a, hipStream_t st) {
-  const unsigned grid = (unsigned)((size_t)s.B * s.Hq * s.NB());
-  if (s.causal)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true>), dim3(grid), dim3(BLK * 2), 0, st, a);
+  const dim3 grid((unsigned)((size_t)s.B * s.Hq * s.NB())), block(BLK * 2);
+  const bool sp = a.kv_idx != nullptr;
+  if (s.causal && sp)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, true>), grid, block, 0, st, a);
+  else if (s.causal)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, false>), grid, block, 0, st, a);
+  else if (sp)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false>), dim3(grid), dim3(BLK * 2), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 

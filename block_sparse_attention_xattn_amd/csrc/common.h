@@ -46,17 +46,20 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* lds_ptr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds_ptr));
 }
 
-// Work-item order for XCD locality: workgroups are dispatched round-robin over
-// the 8 XCDs (workgroup w runs on XCD w % 8). This maps w to a logical index so
-// that, in each group of 32 consecutive dispatches, XCD x receives the 4
-// consecutive logical items 32a + 4x .. 32a + 4x + 3 (e.g. the 4 query heads
-// that share one KV head). The tail beyond the last full group of 32 keeps its
-// own order.
+// Work-item order for XCD locality and balance: workgroups are dispatched
+// round-robin over the 8 XCDs (workgroup w runs on XCD w % 8), each XCD with its
+// own L2. In every window of 32 consecutive dispatches this hands XCD x the 4
+// consecutive logical items 32a + 4((x + a) % 8) .. +3 — e.g. the 4 query heads
+// that share one KV head stay on one XCD (one L2), while the rotation by the
+// window index a spreads every group of items over all XCDs, so uneven per-head
+// work does not pile up on one XCD. The tail beyond the last full window keeps
+// its own order.
 __device__ __forceinline__ uint32_t xcd_group4(uint32_t w, uint32_t n) {
   uint32_t full = n & ~31u;
   if (w >= full) return w;
   uint32_t j = w >> 3, x = w & 7u;
-  return ((j >> 2) << 5) + (x << 2) + (j & 3u);
+  uint32_t a = j >> 2;
+  return (a << 5) + (((x + a) & 7u) << 2) + (j & 3u);
 }
 
 }  // namespace xattn
