@@ -21,6 +21,20 @@
 #include "common.h"
 #include "kernels.h"
 
+// log2 of the neighbouring query-block rows a KV group keeps on one XCD in the
+// sparse kernel (see xcd_map)
+// 1: sparse workgroups pair neighbouring rows of a head; 0: one row each
+#ifndef XATTN_SPARSE_PAIR_ROWS
+#define XATTN_SPARSE_PAIR_ROWS 0
+#endif
+// 1: the sparse workgroups of one KV group share an XCD; 0: spread them
+#ifndef XATTN_SPARSE_GROUP_ON_XCD
+#define XATTN_SPARSE_GROUP_ON_XCD 1
+#endif
+#ifndef XATTN_SPARSE_ROWS_PER_XCD_LOG2
+#define XATTN_SPARSE_ROWS_PER_XCD_LOG2 0
+#endif
+
 namespace xattn {
 
 struct AttnArgs {
@@ -42,7 +56,9 @@ struct AttnLds {
   static constexpr int TILE_B = KT * ROW_B;   // bytes per K (or V) sub-tile
   static constexpr int ROWS_PER_256 = 256 / ROW_B;
   static constexpr int IDX_MAX = 4096;        // block-index row cached as uint16
-  static constexpr int BYTES = 2 * 2 * TILE_B + 2 * IDX_MAX;
+  // K and V double buffers and the block list (u16); with several heads per
+  // workgroup also per-entry head bits and a per-block flag scratch (u8 each)
+  static constexpr int bytes(int hpw) { return 2 * 2 * TILE_B + 2 * IDX_MAX + (hpw > 1 ? 2 * IDX_MAX : 0); }
   // LDS serves 256 B per clock in 64 banks of 4 B. Rows are stored unpadded and
   // the 16-byte chunks (K) or 64-byte segments (V) of each row are XOR-permuted
   // by the row index so that
@@ -58,39 +74,70 @@ struct AttnLds {
   }
 };
 
-template <int C, int BLK, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
+// Workgroup modes: what the 4 or 8 waves of one workgroup cover.
+//   SINGLE    one (head, query block); 4 waves.
+//   SIBLINGS  two GQA sibling heads, same query block; 8 waves. Every K/V tile
+//             load serves both heads (dense attention, identical block lists).
+//   ROWS      one head, two neighbouring query blocks 2p and 2p+1; 8 waves over
+//             the union of the two block lists. Neighbouring rows of a head keep
+//             similar numbers of largely the same blocks, so the shared loads
+//             are rarely wasted and neither half idles for long (sparse).
+// The 8-wave modes hold two sub-tiles in flight (registers), SINGLE one.
+enum { MODE_SINGLE = 0, MODE_SIBLINGS = 1, MODE_ROWS = 2 };
+
+template <int C, int BLK, bool CAUSAL, bool SPARSE, int MODE>
+__global__ __launch_bounds__(BLK * 2 * (MODE == MODE_SINGLE ? 1 : 2), MODE == MODE_SINGLE ? 2 : 1)
+void attn_fwd_bf16_kernel(AttnArgs a) {
   using L = AttnLds<C>;
-  constexpr int NT = BLK * 2;                 // threads: BLK/32 waves of 64
+  constexpr int SLOTS = MODE == MODE_SINGLE ? 1 : 2;
+  constexpr int WPH = BLK / 32;               // waves per slot (32 query rows each)
+  constexpr int NT = 64 * WPH * SLOTS;        // threads
   constexpr int SUB = BLK / L::KT;            // sub-tiles per key block
   constexpr int CHUNKS = L::KT * C / 8;       // 16-byte chunks per K (or V) sub-tile
   constexpr int PER_T = CHUNKS / NT;
   constexpr int KK = C / 16;                  // MFMA k-steps over the head dim
   constexpr int DN = C / 32;                  // 32-wide d tiles of O^T
+  constexpr int DEPTH = SLOTS == 2 ? 2 : 1;   // sub-tiles in flight in registers
   static_assert(CHUNKS % NT == 0, "tile load must divide evenly");
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes(SLOTS)];
   unsigned char* Ks = smem;                      // [2][KT rows][2C bytes], swizzled
   unsigned char* Vs = smem + 2 * L::TILE_B;      // [2][KT rows][2C bytes], swizzled
-  uint16_t* idx_s = reinterpret_cast<uint16_t*>(smem + 4 * L::TILE_B);  // kept key blocks
+  // block list (union over the workgroup's slots) and, per entry, a bit per
+  // slot that selected it
+  uint16_t* idx_s = reinterpret_cast<uint16_t*>(smem + 4 * L::TILE_B);
+  uint8_t* memb_s = smem + 4 * L::TILE_B + 2 * L::IDX_MAX;
+  __shared__ int scan_s[SLOTS > 1 ? NT / 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+  const int hs = wave / WPH;                   // slot of this wave
+  const int slice = wave % WPH;                // 32-row slice of the query block
 
-  // ---- work item: heavy query blocks first, GQA siblings on one XCD
-  const uint32_t n_items = (uint32_t)a.B * a.Hq * a.NB;
-  const uint32_t item = xcd_group4(blockIdx.x, n_items);
+  // ---- work item: heavy query blocks first; the workgroups that share one KV
+  //      head are dispatched to one XCD (one L2), rotating over XCDs per row
   const int G = a.Hq / a.Hkv;
-  const int hq_in = item % G;
-  uint32_t rest = item / G;
+  const int NP = MODE == MODE_ROWS ? (a.NB + 1) / 2 : a.NB;     // rows (or row pairs)
+  const int GW = MODE == MODE_SIBLINGS ? G / 2 : G;             // workgroups per group
+  const uint32_t n_items = (uint32_t)a.B * a.Hkv * GW * NP;
+  const uint32_t item = SPARSE ? xcd_map(blockIdx.x, n_items, XATTN_SPARSE_GROUP_ON_XCD ? GW : 1,
+                                           XATTN_SPARSE_ROWS_PER_XCD_LOG2)
+                                : xcd_map(blockIdx.x, n_items, GW, 0);
+  const int pw = item % GW;
+  uint32_t rest = item / GW;
   const int g = rest % a.Hkv;
   rest /= a.Hkv;
   const int b = rest % a.B;
-  const int I = a.NB - 1 - (int)(rest / a.B);
-  const int h = g * G + hq_in;
+  const int P = NP - 1 - (int)(rest / a.B);
+  // slot s covers head slot_h(s) and query block slot_I(s)
+  auto slot_h = [&](int s2) { return g * G + (MODE == MODE_SIBLINGS ? 2 * pw + s2 : pw); };
+  auto slot_I = [&](int s2) { return MODE == MODE_ROWS ? 2 * P + s2 : P; };
+  const int h = slot_h(hs);                    // this wave's head
+  const int I = slot_I(hs);                    // this wave's query block
+  const bool live = I < a.NB;                  // the odd row count leaves a half-empty pair
 
   const size_t bh = (size_t)b * a.Hq + h;
   const size_t bg = (size_t)b * a.Hkv + g;
@@ -98,29 +145,82 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   const uint16_t* kh = a.k + bg * a.M * C;
   const uint16_t* vh = a.v + bg * a.M * C;
 
-  int cnt;
-  constexpr bool sparse = SPARSE;
+  int cnt;  // entries in the (union) block list
   if constexpr (SPARSE) {
-    cnt = a.kv_cnt[bh * a.NB + I];
-    cnt = cnt < 0 ? 0 : (cnt > a.NB ? a.NB : cnt);
     // cache the row's block list in LDS once, so no dependent global load sits
     // in front of each tile fetch; out-of-range entries are clamped
-    const int32_t* idx = a.kv_idx + (bh * a.NB + I) * a.NB;
-    for (int t = tid; t < cnt; t += NT) {
-      int jb = idx[t];
-      jb = jb < 0 ? 0 : (jb >= a.NB ? a.NB - 1 : jb);
-      idx_s[t] = (uint16_t)jb;
+    if constexpr (SLOTS == 1) {
+      cnt = a.kv_cnt[bh * a.NB + I];
+      cnt = cnt < 0 ? 0 : (cnt > a.NB ? a.NB : cnt);
+      const int32_t* idx = a.kv_idx + (bh * a.NB + I) * a.NB;
+      for (int t = tid; t < cnt; t += NT) {
+        int jb = idx[t];
+        jb = jb < 0 ? 0 : (jb >= a.NB ? a.NB - 1 : jb);
+        idx_s[t] = (uint16_t)jb;
+      }
+    } else {
+      // union of the slots' ascending lists: per-block slot bits, then an
+      // ascending compaction
+      uint8_t* flag = memb_s + L::IDX_MAX;     // [NB] scratch bits
+      for (int j = tid; j < a.NB; j += NT) flag[j] = 0;
+      __syncthreads();
+      for (int s2 = 0; s2 < SLOTS; ++s2) {
+        if (slot_I(s2) >= a.NB) continue;
+        const size_t row = ((size_t)b * a.Hq + slot_h(s2)) * a.NB + slot_I(s2);
+        int c2 = a.kv_cnt[row];
+        c2 = c2 < 0 ? 0 : (c2 > a.NB ? a.NB : c2);
+        const int32_t* idx = a.kv_idx + row * a.NB;
+        for (int t = tid; t < c2; t += NT) {
+          int jb = idx[t];
+          jb = jb < 0 ? 0 : (jb >= a.NB ? a.NB - 1 : jb);
+          // slots write distinct bits; byte-wide OR through a word atomic
+          __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(flag + (jb & ~3)),
+                                (unsigned)(1u << s2) << (8 * (jb & 3)), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+      __syncthreads();
+      const int per = (a.NB + NT - 1) / NT;
+      const int j0 = tid * per, j1 = min(j0 + per, a.NB);
+      int mine = 0;
+      for (int j = j0; j < j1; ++j) mine += flag[j] != 0;
+      int incl = mine;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+      }
+      if (lane == 63) scan_s[wave] = incl;
+      __syncthreads();
+      int pos = incl - mine;
+      int total = 0;
+      for (int w2 = 0; w2 < NT / 64; ++w2) {
+        if (w2 < wave) pos += scan_s[w2];
+        total += scan_s[w2];
+      }
+      for (int j = j0; j < j1; ++j) {
+        const uint8_t f = flag[j];
+        if (f) {
+          idx_s[pos] = (uint16_t)j;
+          memb_s[pos] = f;
+          ++pos;
+        }
+      }
+      cnt = total;
     }
   } else {
-    cnt = CAUSAL ? I + 1 : a.NB;
+    // dense: every candidate of the workgroup's (latest) row
+    const int Imax = slot_I(SLOTS - 1) < a.NB ? slot_I(SLOTS - 1) : slot_I(0);
+    cnt = CAUSAL ? Imax + 1 : a.NB;
   }
   const int n_sub = cnt * SUB;
 
   // ---- Q fragments (B operand of S^T = K Q^T): Q[q0 + l32][16kk + 8hh .. +7]
-  const int q0 = I * BLK + wave * 32;
+  const int q0 = I * BLK + slice * 32;
   bf16x8 qf[KK];
   {
-    const uint16_t* qrow = qh + (size_t)(q0 + l32) * C + 8 * hh;
+    // a dead slot reads row 0 of its head (never used) instead of past the end
+    const uint16_t* qrow = qh + (size_t)(live ? q0 + l32 : l32) * C + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * kk));
@@ -133,127 +233,153 @@ __global__ __launch_bounds__(BLK * 2, 2) void attn_fwd_bf16_kernel(AttnArgs a) {
   float l_run = 0.f;
 
   auto key_start = [&](int t) -> int {
-    const int jb = sparse ? (int)idx_s[t / SUB] : t / SUB;
+    const int jb = SPARSE ? (int)idx_s[t / SUB] : t / SUB;
     return jb * BLK + (t % SUB) * L::KT;
   };
+  auto mine_tile = [&](int t) -> bool {
+    if constexpr (SPARSE && SLOTS > 1) return (memb_s[t / SUB] >> hs) & 1;
+    return live;
+  };
 
-  u32x4 kreg[PER_T], vreg[PER_T];
-  auto load_tile = [&](int t) {
+  typedef u32x4 Stage[2 * PER_T];  // K chunks then V chunks
+  auto load_tile = [&](int t, Stage& r) {
     const int k0 = key_start(t);
 #pragma unroll
     for (int p = 0; p < PER_T; ++p) {
       const int c = tid + p * NT;
       const int row = c / (C / 8), col = (c % (C / 8)) * 8;
-      kreg[p] = *reinterpret_cast<const u32x4*>(kh + (size_t)(k0 + row) * C + col);
-      vreg[p] = *reinterpret_cast<const u32x4*>(vh + (size_t)(k0 + row) * C + col);
+      r[p] = *reinterpret_cast<const u32x4*>(kh + (size_t)(k0 + row) * C + col);
+      r[PER_T + p] = *reinterpret_cast<const u32x4*>(vh + (size_t)(k0 + row) * C + col);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, const Stage& r) {
 #pragma unroll
     for (int p = 0; p < PER_T; ++p) {
       const int c = tid + p * NT;
       const int row = c / (C / 8), chunk = c % (C / 8);
-      *reinterpret_cast<u32x4*>(Ks + buf * L::TILE_B + L::k_off(row, chunk)) = kreg[p];
-      *reinterpret_cast<u32x4*>(Vs + buf * L::TILE_B + L::v_off(row, 16 * chunk)) = vreg[p];
+      *reinterpret_cast<u32x4*>(Ks + buf * L::TILE_B + L::k_off(row, chunk)) = r[p];
+      *reinterpret_cast<u32x4*>(Vs + buf * L::TILE_B + L::v_off(row, 16 * chunk)) = r[PER_T + p];
     }
   };
 
-  __syncthreads();  // block list visible
-  if (n_sub > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < n_sub; ++t) {
-    const int buf = t & 1;
-    const bool more = t + 1 < n_sub;
+  // one sub-tile of online-softmax attention for this wave
+  auto compute = [&](int t, int buf) {
     const int k0 = key_start(t);
-    if (more) load_tile(t + 1);
-
-    const bool skip = CAUSAL && (k0 > q0 + 31);  // whole sub-tile above this wave's rows
-    if (!skip) {
-      const unsigned char* Kb = Ks + buf * L::TILE_B;
-      const unsigned char* Vb = Vs + buf * L::TILE_B;
-      // S^T tiles n = 0, 1: keys k0 + 32n + [8(r/4) + 4hh + r%4], query q0 + l32
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+    if (CAUSAL && (k0 > q0 + 31)) return;       // whole sub-tile above this wave's rows
+    if (!mine_tile(t)) return;                  // selected only by the other head
+    const unsigned char* Kb = Ks + buf * L::TILE_B;
+    const unsigned char* Vb = Vs + buf * L::TILE_B;
+    // S^T tiles n = 0, 1: keys k0 + 32n + [8(r/4) + 4hh + r%4], query q0 + l32
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const bf16x8 ka = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(Kb + L::k_off(32 * n + l32, 2 * kk + hh)));
-          s[n] = mfma32x32x16(ka, qf[kk], s[n]);
-        }
+      for (int n = 0; n < 2; ++n) {
+        const bf16x8 ka = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(Kb + L::k_off(32 * n + l32, 2 * kk + hh)));
+        sacc[n] = mfma32x32x16(ka, qf[kk], sacc[n]);
       }
-      if (CAUSAL && (k0 + L::KT - 1 > q0)) {
-        const int qi = q0 + l32;
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * n + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (key > qi) s[n][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[n][r]);
-      mx = fmaxf(mx, xor32(mx));
-      // Lazy rescaling (exact): O and l share the reference m_run, so the
-      // reference may lag the true running max as long as 2^(s*c - m_run) stays
-      // small. It is raised only when the tile max exceeds it by more than
-      // 2^8, which bounds P by 256 (fine for bf16 and fp32); the final O / l
-      // is unchanged. The branch is uniform per wave.
-      const float m_tile = mx * a.scale_log2;
-      const bool raise = m_tile > m_run + 8.f;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-        const float m_new = fmaxf(m_run, m_tile);
-        // 0 on a lane's first visible tile; 1 while a lane has seen no key
-        const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < DN; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-      bf16x8 pb[4];
+    }
+    if (CAUSAL && (k0 + L::KT - 1 > q0)) {
+      const int qi = q0 + l32;
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(fmaf(s[n][r], a.scale_log2, -m_use));
-          l_run += p;
-          pb[2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(p);
+          const int key = k0 + 32 * n + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (key > qi) sacc[n][r] = -INFINITY;
         }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[n][r]);
+    mx = fmaxf(mx, xor32(mx));
+    // Lazy rescaling (exact): O and l share the reference m_run, so the
+    // reference may lag the true running max as long as 2^(s*c - m_run) stays
+    // small. It is raised only when the tile max exceeds it by more than 8
+    // (in log2 units), which bounds P by 256 (fine for bf16 and fp32); the
+    // final O / l is unchanged. The branch is uniform per wave.
+    const float m_tile = mx * a.scale_log2;
+    const bool raise = m_tile > m_run + 8.f;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = fmaxf(m_run, m_tile);
+      // 0 on a lane's first visible tile; 1 while a lane has seen no key
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < DN; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-      // O^T[d][q] += V^T[d][key] P^T[key][q] over 16-key chunks tc
-      const int G16 = lane >> 4, s16 = lane & 15;
+    bf16x8 pb[4];
 #pragma unroll
-      for (int tc = 0; tc < 4; ++tc) {
-        const int vrow = 16 * tc + 4 * (G16 >> 1) + (s16 >> 2);
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int d = 0; d < DN; ++d) {
-          const int vbyte = 2 * (32 * d + 16 * (G16 & 1) + 4 * (s16 & 3));
-          const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow, vbyte)));
-          const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow + 8, vbyte)));
-          typedef short i16x8 __attribute__((ext_vector_type(8)));
-          const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[d] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pb[tc], o[d]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const float pr = exp2f(fmaf(sacc[n][r], a.scale_log2, -m_use));
+        l_run += pr;
+        pb[2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
+      }
+
+    // O^T[d][q] += V^T[d][key] P^T[key][q] over 16-key chunks tc
+    const int G16 = lane >> 4, s16 = lane & 15;
+#pragma unroll
+    for (int tc = 0; tc < 4; ++tc) {
+      const int vrow = 16 * tc + 4 * (G16 >> 1) + (s16 >> 2);
+#pragma unroll
+      for (int d = 0; d < DN; ++d) {
+        const int vbyte = 2 * (32 * d + 16 * (G16 & 1) + 4 * (s16 & 3));
+        const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow, vbyte)));
+        const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow + 8, vbyte)));
+        typedef short i16x8 __attribute__((ext_vector_type(8)));
+        const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[d] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pb[tc], o[d]);
       }
     }
+  };
 
-    if (more) store_tile(buf ^ 1);
+  __syncthreads();  // block list visible
+  if constexpr (DEPTH == 1) {
+    Stage r0;
+    if (n_sub > 0) {
+      load_tile(0, r0);
+      store_tile(0, r0);
+    }
     __syncthreads();
+    for (int t = 0; t < n_sub; ++t) {
+      const bool more = t + 1 < n_sub;
+      if (more) load_tile(t + 1, r0);
+      compute(t, t & 1);
+      if (more) store_tile((t + 1) & 1, r0);
+      __syncthreads();
+    }
+  } else {
+    // two sub-tiles in flight: tile t+2 is fetched while tile t is computed and
+    // tile t+1 (fetched one iteration earlier) waits in registers
+    Stage ra, rb;
+    if (n_sub > 0) load_tile(0, ra);
+    if (n_sub > 1) load_tile(1, rb);
+    if (n_sub > 0) store_tile(0, ra);
+    __syncthreads();
+    auto iter = [&](int t, Stage& ld, const Stage& st) {
+      if (t + 2 < n_sub) load_tile(t + 2, ld);
+      compute(t, t & 1);
+      if (t + 1 < n_sub) store_tile((t + 1) & 1, st);
+      __syncthreads();
+    };
+    for (int t = 0; t < n_sub; t += 2) {
+      iter(t, ra, rb);
+      if (t + 1 < n_sub) iter(t + 1, rb, ra);
+    }
   }
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) * ln 2
+  if (!live) return;
   const float l_tot = l_run + xor32(l_run);
   const float inv = 1.f / l_tot;
   const int qi = q0 + l32;
@@ -340,19 +466,37 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgsF32 a) {
 
 // ------------------------------------------------------------------ launchers
 
-template <int C, int BLK>
-static hipError_t launch_bf16_cb(const Shape& s, const AttnArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)((size_t)s.B * s.Hq * s.NB())), block(BLK * 2);
+template <int C, int BLK, int MODE>
+static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t st) {
+  const int G = s.Hq / s.Hkv;
+  const int NP = MODE == MODE_ROWS ? (s.NB() + 1) / 2 : s.NB();
+  const int GW = MODE == MODE_SIBLINGS ? G / 2 : G;
+  const dim3 grid((unsigned)((size_t)s.B * s.Hkv * GW * NP));
+  const dim3 block(BLK * 2 * (MODE == MODE_SINGLE ? 1 : 2));
   const bool sp = a.kv_idx != nullptr;
   if (s.causal && sp)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, true, MODE>), grid, block, 0, st, a);
   else if (s.causal)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, false, MODE>), grid, block, 0, st, a);
   else if (sp)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, true>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, true, MODE>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, false>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, false, MODE>), grid, block, 0, st, a);
   return hipGetLastError();
+}
+
+// 128-row blocks use the 8-wave modes: dense pairs GQA siblings (identical
+// block lists) when the group size is even, sparse pairs neighbouring rows of
+// one head (sibling heads keep very different numbers of blocks, so a sibling
+// pair would leave one half idle). 64-row blocks use one (head, row) per
+// workgroup.
+template <int C, int BLK>
+static hipError_t launch_bf16_cb(const Shape& s, const AttnArgs& a, hipStream_t st) {
+  if (BLK == 128) {
+    if (a.kv_idx == nullptr && (s.Hq / s.Hkv) % 2 == 0) return launch_bf16_cbm<C, BLK, MODE_SIBLINGS>(s, a, st);
+    if (a.kv_idx != nullptr && XATTN_SPARSE_PAIR_ROWS) return launch_bf16_cbm<C, BLK, MODE_ROWS>(s, a, st);
+  }
+  return launch_bf16_cbm<C, BLK, MODE_SINGLE>(s, a, st);
 }
 
 hipError_t launch_attn_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,

@@ -46,20 +46,25 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* lds_ptr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(lds_ptr));
 }
 
-// Work-item order for XCD locality and balance: workgroups are dispatched
+// Work-item order for XCD locality and balance. Workgroups are dispatched
 // round-robin over the 8 XCDs (workgroup w runs on XCD w % 8), each XCD with its
-// own L2. In every window of 32 consecutive dispatches this hands XCD x the 4
-// consecutive logical items 32a + 4((x + a) % 8) .. +3 — e.g. the 4 query heads
-// that share one KV head stay on one XCD (one L2), while the rotation by the
-// window index a spreads every group of items over all XCDs, so uneven per-head
-// work does not pile up on one XCD. The tail beyond the last full window keeps
-// its own order.
-__device__ __forceinline__ uint32_t xcd_group4(uint32_t w, uint32_t n) {
-  uint32_t full = n & ~31u;
+// own L2. With K items per group (e.g. the workgroups that share one KV head),
+// every window of 8K consecutive dispatches hands XCD x the K consecutive
+// logical items 8Ka + K((x + (a >> rot_shift)) % 8) .. +K-1. A group stays on
+// one XCD (one L2) for 2^rot_shift consecutive windows (e.g. neighbouring query
+// rows, which select overlapping key blocks), and the rotation then spreads the
+// groups over all XCDs, so uneven per-group work does not pile up on one XCD.
+// The tail beyond the last full window keeps its own order.
+__device__ __forceinline__ uint32_t xcd_map(uint32_t w, uint32_t n, uint32_t K,
+                                            uint32_t rot_shift = 0) {
+  const uint32_t win = 8u * K;
+  const uint32_t full = n - n % win;
   if (w >= full) return w;
-  uint32_t j = w >> 3, x = w & 7u;
-  uint32_t a = j >> 2;
-  return (a << 5) + (((x + a) & 7u) << 2) + (j & 3u);
+  const uint32_t j = w >> 3, x = w & 7u;
+  const uint32_t a = j / K;
+  return a * win + ((x + (a >> rot_shift)) & 7u) * K + j % K;
 }
+
+__device__ __forceinline__ uint32_t xcd_group4(uint32_t w, uint32_t n) { return xcd_map(w, n, 4); }
 
 }  // namespace xattn

@@ -17,7 +17,8 @@ struct Shape {
 };
 
 // Stage 1: per (strided row i, key block J) partial log2-sum-exp of the scaled
-// strided antidiagonal logits, written to ws as [b][h][J][i] float32.
+// strided antidiagonal logits, written to ws as [b][h][I][J][t] float32 with
+// I = i / r, t = i % r.
 hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
                                       float score_scale, float* ws, hipStream_t st);
 hipError_t launch_score_partials_f32(const Shape& s, const float* q, const float* k,

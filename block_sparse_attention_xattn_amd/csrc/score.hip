@@ -13,8 +13,9 @@
 // (M/S)^2 logit matrix never reaches HBM. Each 128 x 128 output tile
 // reduces, in registers, every (strided row i, key block J) cell to a partial
 // log2-sum-exp L[J][i]; a second kernel turns each query-block row of partials
-// into normalised block scores. Partials are written J-major so a wave's 32
-// query rows store 128 contiguous bytes.
+// into normalised block scores. Partials are stored [I][J][t] (query block,
+// key block, strided row within the block), so one query-block row of partials
+// is contiguous and the second pass reads it with unit stride.
 //
 // GEMM (bf16, gfx950 MFMA 32x32x16): S^T = K~' Q'^T, 4 waves in a 2x2 grid of
 // 64 x 64 sub-tiles, the S*C contraction streamed in 64-element chunks through
@@ -174,7 +175,7 @@ __global__ __launch_bounds__(256) void score_partials_bf16_kernel(ScoreArgs a) {
           const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
           const int j = jb + 8 * (r0 >> 2) + 4 * hh + (r0 & 3);
           const int J = j / RB;
-          if (i < a.R && j < a.R) wsh[(size_t)J * a.R + i] = Lv;
+          if (i < a.R && j < a.R) wsh[((size_t)(i / RB) * a.NB + J) * RB + i % RB] = Lv;
         }
       } else {
         // a run of RB >= 8 keys = registers [4q .. 4q + RB/2) in both wave halves
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(256) void score_partials_bf16_kernel(ScoreArgs a) {
           const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
           const int j = jb + 8 * (r0 >> 2);
           const int J = j / RB;
-          if (hh == 0 && i < a.R && j < a.R) wsh[(size_t)J * a.R + i] = Lv;
+          if (hh == 0 && i < a.R && j < a.R) wsh[((size_t)(i / RB) * a.NB + J) * RB + i % RB] = Lv;
         }
       }
     }
@@ -238,7 +239,8 @@ __global__ __launch_bounds__(256) void score_partials_f32_kernel(ScoreArgsF32 a)
     s = s * exp2f(m - mn) + exp2f(x - mn);
     m = mn;
   }
-  a.ws[bh * per_head + (size_t)J * a.R + i] = (m == -INFINITY) ? -INFINITY : m + log2f(s);
+  a.ws[bh * per_head + ((size_t)(i / a.r) * a.NB + J) * a.r + i % a.r] =
+      (m == -INFINITY) ? -INFINITY : m + log2f(s);
 }
 
 // Block scores from partials: one workgroup per (b, h, I).
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
   const int I = (int)(row % a.NB);
   const size_t bh = row / a.NB;
   const int n_cand = a.causal ? I + 1 : a.NB;
-  const float* L = a.ws + bh * (size_t)a.NB * a.R + (size_t)I * a.r;
+  const float* L = a.ws + (bh * (size_t)a.NB + I) * (size_t)a.NB * a.r;  // [J][t] of row I
   constexpr int r = RB;
 
   // pass 1: per strided row t, log2-sum-exp over candidate blocks
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
 #pragma unroll
   for (int t = 0; t < r; ++t) { m[t] = -INFINITY; s[t] = 0.f; }
   for (int J = tid; J < n_cand; J += 256) {
-    const float* p = L + (size_t)J * a.R;
+    const float* p = L + (size_t)J * r;
 #pragma unroll
     for (int t = 0; t < r; ++t) {
       const float x = p[t];
@@ -310,7 +312,7 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
   for (int J = tid; J < a.NB; J += 256) {
     float sc = 0.f;
     if (J < n_cand) {
-      const float* p = L + (size_t)J * a.R;
+      const float* p = L + (size_t)J * r;
 #pragma unroll
       for (int t = 0; t < r; ++t) sc += exp2f(p[t] - lse[t]);
       sc *= inv_r;

@@ -14,10 +14,13 @@ and key j is realised by giving Q the feature ``a_h * C**0.25 * phi(i)`` and K
 the feature ``gamma * b * C**0.25 * psi(j)``, so that after the attention scale
 1/sqrt(C) the logit changes by ``a_h * gamma * b * <phi(i), psi(j)>``.
 
-All draws are float32 on the requested device in a fixed order (Q, K, V, then
-structure draws, then tau) and are cast to the workload dtype with
-round-to-nearest-even. The same seed on the same device type gives the same
-tensors.
+Bulk Gaussian draws (Q, K, V, walk steps) are float32 on the requested device.
+The few structure draws (per-head strengths a_h, column positions and
+amplitudes, per-head tau) come from a separate CPU generator, so they are the
+same whichever device holds the tensors; a density calibrated with CPU tensors
+therefore carries over to GPU-generated ones. Everything is cast to the
+workload dtype with round-to-nearest-even. The same seed on the same device
+type gives the same tensors.
 """
 from __future__ import annotations
 
@@ -117,6 +120,8 @@ def make_inputs(w: Workload, device="cpu", gamma: float | None = None):
     """
     g = torch.Generator(device=device)
     g.manual_seed(w.seed)
+    gs = torch.Generator()                 # structure draws: CPU, device-independent
+    gs.manual_seed(1000003 * (w.seed + 1))
     gam = GAMMA[w.family] if gamma is None else gamma
     B, Hq, Hkv, M, C = w.B, w.Hq, w.Hkv, w.M, w.C
     f32 = dict(device=device, dtype=torch.float32)
@@ -135,7 +140,7 @@ def make_inputs(w: Workload, device="cpu", gamma: float | None = None):
         q = torch.randn((B, Hq, M, C), generator=g, **f32) / math.sqrt(C)
         k = torch.randn((B, Hkv, M, C), generator=g, **f32) / math.sqrt(C)
         v = torch.randn((B, Hkv, M, C), generator=g, **f32)
-        a_h = 1.0 + 0.5 * (2 * torch.rand((Hq,), generator=g, **f32) - 1)
+        a_h = (1.0 + 0.5 * (2 * torch.rand((Hq,), generator=gs) - 1)).to(device)
         q[:, :, :, 0] += (a_h * c4)[None, :, None]        # reads the sink channel
         q[:, :, :, 1] += (a_h * c4)[None, :, None]        # reads the column channel
         k[:, :, :4, 0] += gam * 12.0 * c4                 # sink on the first 4 keys
@@ -147,8 +152,8 @@ def make_inputs(w: Workload, device="cpu", gamma: float | None = None):
             # random vertical columns on 0.5% of keys per KV head
             n_col = max(1, int(0.005 * (M - 4)))
             for hk in range(Hkv):
-                cols = 4 + torch.randperm(M - 4, generator=g, device=device)[:n_col]
-                amp = 4.0 * (0.5 + torch.rand((n_col,), generator=g, **f32))
+                cols = (4 + torch.randperm(M - 4, generator=gs)[:n_col]).to(device)
+                amp = (4.0 * (0.5 + torch.rand((n_col,), generator=gs))).to(device)
                 k[:, hk, cols, 1] += gam * c4 * amp
             # slash bands at diagonal offsets {0, 1024, 4096}: shared Fourier bank
             n_pairs = (C - 2) // 2
@@ -172,7 +177,7 @@ def make_inputs(w: Workload, device="cpu", gamma: float | None = None):
         raise ValueError(w.family)
 
     if isinstance(w.tau, tuple):
-        choice = torch.randint(len(w.tau), (Hq,), generator=g, device=device).cpu()
+        choice = torch.randint(len(w.tau), (Hq,), generator=gs)
         tau = torch.tensor([w.tau[i] for i in choice.tolist()], dtype=torch.float32)
     else:
         tau = torch.full((Hq,), float(w.tau), dtype=torch.float32)
