@@ -23,6 +23,11 @@
 
 // log2 of the neighbouring query-block rows a KV group keeps on one XCD in the
 // sparse kernel (see xcd_map)
+// 1: software-pipelined attention loop (S(t+1) MFMAs overlap the softmax of
+// tile t); 0: the plain loop
+#ifndef XATTN_ATTN_PIPELINE
+#define XATTN_ATTN_PIPELINE 0
+#endif
 // 1: sparse workgroups pair neighbouring rows of a head; 0: one row each
 #ifndef XATTN_SPARSE_PAIR_ROWS
 #define XATTN_SPARSE_PAIR_ROWS 0
@@ -306,7 +311,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     if (__builtin_amdgcn_ballot_w64(raise) != 0) {
       const float m_new = fmaxf(m_run, m_tile);
       // 0 on a lane's first visible tile; 1 while a lane has seen no key
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -321,7 +326,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = exp2f(fmaf(sacc[n][r], a.scale_log2, -m_use));
+        const float pr = fast_exp2(fmaf(sacc[n][r], a.scale_log2, -m_use));
         l_run += pr;
         pb[2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
       }
@@ -344,7 +349,163 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   };
 
   __syncthreads();  // block list visible
-  if constexpr (DEPTH == 1) {
+  if constexpr (XATTN_ATTN_PIPELINE != 0) {
+    // Software-pipelined loop. K runs one LDS stage ahead of V: while a wave
+    // turns S(t) into P(t) (max, exp2, sum, bf16 pack — VALU work), it already
+    // issues the MFMAs of S(t+1) = K(t+1) Q^T, so the matrix pipe and the VALU
+    // overlap inside the wave; PV(t) follows. The exp2 runs against the current
+    // reference m_run; in the rare case the tile max exceeds it by more than 8
+    // (log2 units) the reference is raised, O and l rescaled and P recomputed.
+    // Iteration t reads K(t+1) from Kbuf[(t+1)&1] and V(t) from Vbuf[t&1] and,
+    // after the barrier-protected compute, stores K(t+2) -> Kbuf[t&1] and
+    // V(t+1) -> Vbuf[(t+1)&1]; each buffer was last read one iteration earlier.
+    typedef u32x4 Half[PER_T];
+    auto load_k = [&](int t, Half& r) {
+      const int k0 = key_start(t);
+#pragma unroll
+      for (int p = 0; p < PER_T; ++p) {
+        const int c = tid + p * NT;
+        r[p] = *reinterpret_cast<const u32x4*>(kh + (size_t)(k0 + c / (C / 8)) * C + (c % (C / 8)) * 8);
+      }
+    };
+    auto load_v = [&](int t, Half& r) {
+      const int k0 = key_start(t);
+#pragma unroll
+      for (int p = 0; p < PER_T; ++p) {
+        const int c = tid + p * NT;
+        r[p] = *reinterpret_cast<const u32x4*>(vh + (size_t)(k0 + c / (C / 8)) * C + (c % (C / 8)) * 8);
+      }
+    };
+    auto store_k = [&](int buf, const Half& r) {
+#pragma unroll
+      for (int p = 0; p < PER_T; ++p) {
+        const int c = tid + p * NT;
+        *reinterpret_cast<u32x4*>(Ks + buf * L::TILE_B + L::k_off(c / (C / 8), c % (C / 8))) = r[p];
+      }
+    };
+    auto store_v = [&](int buf, const Half& r) {
+#pragma unroll
+      for (int p = 0; p < PER_T; ++p) {
+        const int c = tid + p * NT;
+        *reinterpret_cast<u32x4*>(Vs + buf * L::TILE_B + L::v_off(c / (C / 8), 16 * (c % (C / 8)))) = r[p];
+      }
+    };
+    auto qk = [&](int kbuf, f32x16 (&sacc)[2]) {
+      const unsigned char* Kb = Ks + kbuf * L::TILE_B;
+      sacc[0] = f32x16{};
+      sacc[1] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const bf16x8 ka = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(Kb + L::k_off(32 * n + l32, 2 * kk + hh)));
+          sacc[n] = mfma32x32x16(ka, qf[kk], sacc[n]);
+        }
+    };
+    // P(t) from S(t), O += V(t)^T P(t); S(t+1) is issued in between
+    auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      const int k0 = key_start(t);
+      const bool mine = mine_tile(t);
+      if ((CAUSAL && (k0 + L::KT - 1 > q0)) || !mine) {
+        const int qi = q0 + l32;
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * n + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (!mine || (CAUSAL && key > qi)) sc[n][r] = -INFINITY;
+          }
+      }
+      // S(t+1): issued now, consumed next iteration (a stale buffer after the
+      // last tile; the result is then unused)
+      qk((t + 1) & 1, sn);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[n][r]);
+      mx = fmaxf(mx, xor32(mx));
+      const float m_tile = mx * a.scale_log2;
+      float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+      bf16x8 pb[4];
+      float lsum = 0.f;
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = fast_exp2(fmaf(sc[n][r], a.scale_log2, -m_use));
+          lsum += pr;
+          pb[2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
+        }
+      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.f) != 0) {
+        const float m_new = fmaxf(m_run, m_tile);
+        // 0 on a lane's first visible tile; 1 while a lane has seen no key
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int d = 0; d < DN; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+        m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        lsum = 0.f;
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pr = fast_exp2(fmaf(sc[n][r], a.scale_log2, -m_use));
+            lsum += pr;
+            pb[2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
+          }
+      }
+      l_run += lsum;
+      const unsigned char* Vb = Vs + (t & 1) * L::TILE_B;
+      const int G16 = lane >> 4, s16 = lane & 15;
+#pragma unroll
+      for (int tc = 0; tc < 4; ++tc) {
+        const int vrow = 16 * tc + 4 * (G16 >> 1) + (s16 >> 2);
+#pragma unroll
+        for (int d = 0; d < DN; ++d) {
+          const int vbyte = 2 * (32 * d + 16 * (G16 & 1) + 4 * (s16 & 3));
+          const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow, vbyte)));
+          const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow + 8, vbyte)));
+          typedef short i16x8 __attribute__((ext_vector_type(8)));
+          const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[d] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pb[tc], o[d]);
+        }
+      }
+    };
+
+    Half rk, rv;
+    f32x16 sa[2], sb[2];
+    if (n_sub > 0) {
+      load_k(0, rk);
+      load_v(0, rv);
+      store_k(0, rk);
+      store_v(0, rv);
+      if (n_sub > 1) {
+        load_k(1, rk);
+        store_k(1, rk);
+      }
+    }
+    __syncthreads();
+    if (n_sub > 0) qk(0, sa);
+    __syncthreads();  // Kbuf[0] is refilled in iteration 0
+    auto iter = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      const bool k2 = t + 2 < n_sub, v1 = t + 1 < n_sub;
+      if (k2) load_k(t + 2, rk);
+      if (v1) load_v(t + 1, rv);
+      step(t, sc, sn);
+      if (k2) store_k(t & 1, rk);
+      if (v1) store_v((t + 1) & 1, rv);
+      __syncthreads();
+    };
+    for (int t = 0; t < n_sub; t += 2) {
+      iter(t, sa, sb);
+      if (t + 1 < n_sub) iter(t + 1, sb, sa);
+    }
+  } else if constexpr (DEPTH == 1) {
     Stage r0;
     if (n_sub > 0) {
       load_tile(0, r0);
@@ -448,8 +609,8 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgsF32 a) {
       for (int c = 0; c < C; ++c) s = fmaf(qv[c], kr[c], s);
       s *= a.scale_log2;
       const float mn = fmaxf(m, s);
-      const float alpha = exp2f(m - mn);
-      const float p = exp2f(s - mn);
+      const float alpha = fast_exp2(m - mn);
+      const float p = fast_exp2(s - mn);
       l = l * alpha + p;
       const float* vr = vh + (size_t)kj * C;
 #pragma unroll

@@ -18,6 +18,14 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// 2^x on the hardware exp unit (v_exp_f32, about 1 ulp). Results below 2^-126
+// flush towards zero, which is harmless for softmax weights; the library's exp2f
+// would add a 5-instruction denormal-range fix-up around each call.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// log2 on the hardware unit (v_log_f32) for normal positive inputs.
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
   return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }

@@ -86,28 +86,37 @@ __global__ __launch_bounds__(256) void score_partials_bf16_kernel(ScoreArgs a) {
   const int S = a.S;
   const int n_chunks = S * C / SC_KC;
 
-  // global -> register staging: 128 rows x 128 B per operand = 1024 x 16 B
-  u32x4 kreg[4], qreg[4];
-  auto load_chunk = [&](int c) {
+  // global -> register staging: 128 rows x 128 B per operand = 1024 x 16 B.
+  // Row pointers are formed once; per chunk only a uniform offset changes.
+  // Rows past R (a ragged last tile) are clamped to row R-1: they load valid
+  // memory and their outputs are never stored.
+  const uint16_t* kp[4];
+  const uint16_t* qp[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int id = tid + 256 * p;
+    const int row = id >> 3, col = (id & 7) * 8;
+    const int j = min(j0 + row, a.R - 1), i = min(i0 + row, a.R - 1);
+    kp[p] = kh + (size_t)(j * S + S - 1) * C + col;   // stride group read in reverse
+    qp[p] = qh + (size_t)(i * S) * C + col;
+  }
+  typedef u32x4 Stage[8];  // 4 K chunks then 4 Q chunks
+  auto load_chunk = [&](int c, Stage& r) {
     const int srow = (SC_KC * c) / C, col0 = (SC_KC * c) % C;
+    const int koff = -srow * C + col0, qoff = srow * C + col0;
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-      const int id = tid + 256 * p;
-      const int row = id >> 3, col = col0 + (id & 7) * 8;
-      const int j = j0 + row, i = i0 + row;
-      kreg[p] = (j < a.R) ? *reinterpret_cast<const u32x4*>(kh + (size_t)(j * S + S - 1 - srow) * C + col)
-                          : u32x4{0u, 0u, 0u, 0u};
-      qreg[p] = (i < a.R) ? *reinterpret_cast<const u32x4*>(qh + (size_t)(i * S + srow) * C + col)
-                          : u32x4{0u, 0u, 0u, 0u};
+      r[p] = *reinterpret_cast<const u32x4*>(kp[p] + koff);
+      r[4 + p] = *reinterpret_cast<const u32x4*>(qp[p] + qoff);
     }
   };
-  auto store_chunk = [&](int buf) {
+  auto store_chunk = [&](int buf, const Stage& r) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int id = tid + 256 * p;
       const int row = id >> 3, col = (id & 7) * 8;
-      *reinterpret_cast<u32x4*>(Ks + buf * SC_OP + row * SC_P + col) = kreg[p];
-      *reinterpret_cast<u32x4*>(Qs + buf * SC_OP + row * SC_P + col) = qreg[p];
+      *reinterpret_cast<u32x4*>(Ks + buf * SC_OP + row * SC_P + col) = r[p];
+      *reinterpret_cast<u32x4*>(Qs + buf * SC_OP + row * SC_P + col) = r[4 + p];
     }
   };
 
@@ -117,13 +126,7 @@ __global__ __launch_bounds__(256) void score_partials_bf16_kernel(ScoreArgs a) {
 #pragma unroll
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
 
-  load_chunk(0);
-  store_chunk(0);
-  __syncthreads();
-  for (int c = 0; c < n_chunks; ++c) {
-    const int buf = c & 1;
-    const bool more = c + 1 < n_chunks;
-    if (more) load_chunk(c + 1);
+  auto mma_chunk = [&](int buf) {
     const uint16_t* Kb = Ks + buf * SC_OP + (64 * wk + l32) * SC_P + 8 * hh;
     const uint16_t* Qb = Qs + buf * SC_OP + (64 * wq + l32) * SC_P + 8 * hh;
 #pragma unroll
@@ -139,7 +142,18 @@ __global__ __launch_bounds__(256) void score_partials_bf16_kernel(ScoreArgs a) {
 #pragma unroll
         for (int y = 0; y < 2; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
     }
-    if (more) store_chunk(buf ^ 1);
+  };
+
+  // one chunk in flight: chunk c+1 is fetched while chunk c is multiplied
+  Stage rs;
+  load_chunk(0, rs);
+  store_chunk(0, rs);
+  __syncthreads();
+  for (int c = 0; c < n_chunks; ++c) {
+    const bool more = c + 1 < n_chunks;
+    if (more) load_chunk(c + 1, rs);
+    mma_chunk(c & 1);
+    if (more) store_chunk((c + 1) & 1, rs);
     __syncthreads();
   }
 
@@ -170,7 +184,7 @@ __global__ __launch_bounds__(256) void score_partials_bf16_kernel(ScoreArgs a) {
           float s = 0.f;
           if (m != -INFINITY) {
 #pragma unroll
-            for (int u = 0; u < RB; ++u) s += exp2f(v[r0 + u] - m);
+            for (int u = 0; u < RB; ++u) s += fast_exp2(v[r0 + u] - m);
           }
           const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
           const int j = jb + 8 * (r0 >> 2) + 4 * hh + (r0 & 3);
@@ -189,7 +203,7 @@ __global__ __launch_bounds__(256) void score_partials_bf16_kernel(ScoreArgs a) {
           float s = 0.f;
           if (m != -INFINITY) {
 #pragma unroll
-            for (int u = 0; u < NR; ++u) s += exp2f(v[r0 + u] - m);
+            for (int u = 0; u < NR; ++u) s += fast_exp2(v[r0 + u] - m);
           }
           s += xor32(s);
           const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
@@ -236,7 +250,7 @@ __global__ __launch_bounds__(256) void score_partials_f32_kernel(ScoreArgsF32 a)
     }
     const float x = dot * a.scale2;
     const float mn = fmaxf(m, x);
-    s = s * exp2f(m - mn) + exp2f(x - mn);
+    s = s * fast_exp2(m - mn) + fast_exp2(x - mn);
     m = mn;
   }
   a.ws[bh * per_head + ((size_t)(i / a.r) * a.NB + J) * a.r + i % a.r] =
@@ -273,7 +287,7 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
       const float x = p[t];
       const float mn = fmaxf(m[t], x);
       if (mn != -INFINITY) {
-        s[t] = s[t] * exp2f(m[t] - mn) + exp2f(x - mn);
+        s[t] = s[t] * fast_exp2(m[t] - mn) + fast_exp2(x - mn);
         m[t] = mn;
       }
     }
@@ -285,7 +299,7 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
       const float mo = __shfl_xor(mt, off, 64), so = __shfl_xor(stv, off, 64);
       const float mn = fmaxf(mt, mo);
       if (mn != -INFINITY) {
-        stv = stv * exp2f(mt - mn) + so * exp2f(mo - mn);
+        stv = stv * fast_exp2(mt - mn) + so * fast_exp2(mo - mn);
         mt = mn;
       }
     }
@@ -298,7 +312,7 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
       const float mo = red_m[w][tid], so = red_s[w][tid];
       const float mn = fmaxf(mt, mo);
       if (mn != -INFINITY) {
-        stv = stv * exp2f(mt - mn) + so * exp2f(mo - mn);
+        stv = stv * fast_exp2(mt - mn) + so * fast_exp2(mo - mn);
         mt = mn;
       }
     }
@@ -314,7 +328,7 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
     if (J < n_cand) {
       const float* p = L + (size_t)J * r;
 #pragma unroll
-      for (int t = 0; t < r; ++t) sc += exp2f(p[t] - lse[t]);
+      for (int t = 0; t < r; ++t) sc += fast_exp2(p[t] - lse[t]);
       sc *= inv_r;
     }
     orow[J] = sc;
