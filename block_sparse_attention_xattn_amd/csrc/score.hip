@@ -17,9 +17,11 @@
 // key block, strided row within the block), so one query-block row of partials
 // is contiguous and the second pass reads it with unit stride.
 //
-// GEMM (bf16, gfx950 MFMA 32x32x16): S^T = K~' Q'^T, 4 waves in a 2x2 grid of
-// 64 x 64 sub-tiles, the S*C contraction streamed in 64-element chunks through
-// a double-buffered LDS tile. K~' row j, chunk c is the contiguous run
+// GEMM (bf16, gfx950 MFMA 32x32x16): S^T = K~' Q'^T on 256 x 256 output tiles,
+// 16 waves in a 4x4 grid of 64 x 64 sub-tiles, the S*C contraction streamed in
+// 64-element chunks through a double-buffered 144 KiB LDS tile. The tile size is
+// set by L2 bandwidth: a 256 x 256 tile moves half the L2 bytes per FLOP of a
+// 128 x 128 one (128 vs 64 FLOP per byte). K~' row j, chunk c is the contiguous run
 // k[j*S + S-1 - (64c)/C][(64c)%C ...] — the stride group read in reverse, so
 // the reversal costs only address arithmetic.
 #include "common.h"
@@ -37,10 +39,27 @@ struct ScoreArgs {
   float scale2;   // score_scale * log2(e)
 };
 
-constexpr int SC_TILE = 128;
-constexpr int SC_KC = 64;             // contraction chunk (elements)
-constexpr int SC_P = SC_KC + 8;       // LDS row pitch: 144 B (16 B mod 128 B)
-constexpr int SC_OP = SC_TILE * SC_P; // elements per operand buffer
+#ifndef XATTN_SCORE_TILE
+#define XATTN_SCORE_TILE 256
+#endif
+constexpr int SC_TILE = XATTN_SCORE_TILE;   // strided keys x strided queries per tile
+constexpr int SC_WN = SC_TILE / 64;         // waves per tile side (64 x 64 per wave)
+constexpr int SC_NT = 64 * SC_WN * SC_WN;   // threads per workgroup
+#ifndef XATTN_SCORE_KC
+#define XATTN_SCORE_KC 64
+#endif
+constexpr int SC_KC = XATTN_SCORE_KC;  // contraction chunk (elements): 32 or 64
+constexpr int SC_CPR = SC_KC / 8;      // 16-byte chunks per operand row
+// LDS layout of one operand buffer (128 rows x SC_KC bf16), in elements.
+//  KC = 64: rows padded to 144 B (16 B mod 128 B).
+//  KC = 32: unpadded 64 B rows, the 4 chunks of a row XOR-permuted by
+//           (row / 4) % 4, so 16 lanes reading one chunk of 16 consecutive rows,
+//           and 16 lanes writing 4 whole rows, each touch 256 distinct bytes.
+constexpr int SC_OP = SC_KC == 64 ? SC_TILE * (SC_KC + 8) : SC_TILE * SC_KC;
+__device__ __forceinline__ int sc_off(int row, int chunk) {
+  if constexpr (SC_KC == 64) return row * (SC_KC + 8) + chunk * 8;
+  return row * SC_KC + 8 * (chunk ^ ((row >> 2) & 3));
+}
 
 __device__ __forceinline__ void tile_pair(int p, bool causal, int T, int& tq, int& tk) {
   if (!causal) {
@@ -56,15 +75,15 @@ __device__ __forceinline__ void tile_pair(int p, bool causal, int T, int& tq, in
 }
 
 template <int C, int RB, bool CAUSAL>
-__global__ __launch_bounds__(256) void score_partials_bf16_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a) {
   static_assert(RB == 2 || RB == 4 || RB == 8 || RB == 16 || RB == 32, "r");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * SC_OP];
-  uint16_t* Ks = smem;               // [2][128][SC_P]  strided keys (A operand)
-  uint16_t* Qs = smem + 2 * SC_OP;   // [2][128][SC_P]  strided queries (B operand)
+  uint16_t* Ks = smem;               // [2][SC_TILE rows] strided keys (A operand)
+  uint16_t* Qs = smem + 2 * SC_OP;   // [2][SC_TILE rows] strided queries (B operand)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int wk = wave >> 1, wq = wave & 1;
+  const int wk = wave / SC_WN, wq = wave % SC_WN;
 
   const uint32_t n_items = (uint32_t)a.B * a.Hq * a.pairs;
   const uint32_t item = xcd_group4(blockIdx.x, n_items);
@@ -86,37 +105,39 @@ __global__ __launch_bounds__(256) void score_partials_bf16_kernel(ScoreArgs a) {
   const int S = a.S;
   const int n_chunks = S * C / SC_KC;
 
-  // global -> register staging: 128 rows x 128 B per operand = 1024 x 16 B.
+  // global -> register staging: SC_TILE rows x SC_KC elements per operand.
   // Row pointers are formed once; per chunk only a uniform offset changes.
   // Rows past R (a ragged last tile) are clamped to row R-1: they load valid
   // memory and their outputs are never stored.
-  const uint16_t* kp[4];
-  const uint16_t* qp[4];
+  constexpr int LPT = SC_TILE * SC_CPR / SC_NT;  // 16-byte loads per thread per operand
+  static_assert(LPT * SC_NT == SC_TILE * SC_CPR, "tile load must divide evenly");
+  const uint16_t* kp[LPT];
+  const uint16_t* qp[LPT];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int id = tid + 256 * p;
-    const int row = id >> 3, col = (id & 7) * 8;
+  for (int p = 0; p < LPT; ++p) {
+    const int id = tid + SC_NT * p;
+    const int row = id / SC_CPR, col = (id % SC_CPR) * 8;
     const int j = min(j0 + row, a.R - 1), i = min(i0 + row, a.R - 1);
     kp[p] = kh + (size_t)(j * S + S - 1) * C + col;   // stride group read in reverse
     qp[p] = qh + (size_t)(i * S) * C + col;
   }
-  typedef u32x4 Stage[8];  // 4 K chunks then 4 Q chunks
+  typedef u32x4 Stage[2 * LPT];  // K chunks then Q chunks
   auto load_chunk = [&](int c, Stage& r) {
     const int srow = (SC_KC * c) / C, col0 = (SC_KC * c) % C;
     const int koff = -srow * C + col0, qoff = srow * C + col0;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < LPT; ++p) {
       r[p] = *reinterpret_cast<const u32x4*>(kp[p] + koff);
-      r[4 + p] = *reinterpret_cast<const u32x4*>(qp[p] + qoff);
+      r[LPT + p] = *reinterpret_cast<const u32x4*>(qp[p] + qoff);
     }
   };
   auto store_chunk = [&](int buf, const Stage& r) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int id = tid + 256 * p;
-      const int row = id >> 3, col = (id & 7) * 8;
-      *reinterpret_cast<u32x4*>(Ks + buf * SC_OP + row * SC_P + col) = r[p];
-      *reinterpret_cast<u32x4*>(Qs + buf * SC_OP + row * SC_P + col) = r[4 + p];
+    for (int p = 0; p < LPT; ++p) {
+      const int id = tid + SC_NT * p;
+      const int row = id / SC_CPR, chunk = id % SC_CPR;
+      *reinterpret_cast<u32x4*>(Ks + buf * SC_OP + sc_off(row, chunk)) = r[p];
+      *reinterpret_cast<u32x4*>(Qs + buf * SC_OP + sc_off(row, chunk)) = r[LPT + p];
     }
   };
 
@@ -127,15 +148,17 @@ __global__ __launch_bounds__(256) void score_partials_bf16_kernel(ScoreArgs a) {
     for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
 
   auto mma_chunk = [&](int buf) {
-    const uint16_t* Kb = Ks + buf * SC_OP + (64 * wk + l32) * SC_P + 8 * hh;
-    const uint16_t* Qb = Qs + buf * SC_OP + (64 * wq + l32) * SC_P + 8 * hh;
+    const uint16_t* Kb = Ks + buf * SC_OP;
+    const uint16_t* Qb = Qs + buf * SC_OP;
 #pragma unroll
     for (int ks = 0; ks < SC_KC / 16; ++ks) {
       bf16x8 af[2], bfr[2];
 #pragma unroll
       for (int x = 0; x < 2; ++x) {
-        af[x] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Kb + 32 * x * SC_P + 16 * ks));
-        bfr[x] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Qb + 32 * x * SC_P + 16 * ks));
+        af[x] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(Kb + sc_off(64 * wk + 32 * x + l32, 2 * ks + hh)));
+        bfr[x] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(Qb + sc_off(64 * wq + 32 * x + l32, 2 * ks + hh)));
       }
 #pragma unroll
       for (int x = 0; x < 2; ++x)
@@ -341,9 +364,9 @@ template <int C, int RB>
 static hipError_t launch_partials_cr(const Shape& s, const ScoreArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((size_t)s.B * s.Hq * a.pairs);
   if (s.causal)
-    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, true>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, true>), dim3(grid), dim3(SC_NT), 0, st, a);
   else
-    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, false>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, false>), dim3(grid), dim3(SC_NT), 0, st, a);
   return hipGetLastError();
 }
 

@@ -33,7 +33,7 @@ import torch
 # Structure strength per family, fixed once by calibration on the oracle's
 # selection (head-mean density of the 256K layer near 7.32% at tau=0.9, and
 # of the video layer near 45.5% at tau=0.95) and never tuned against GPU time.
-GAMMA = {"tiny": 1.0, "llama": 2.85, "llama_long": 2.85, "video": 0.82}
+GAMMA = {"tiny": 1.0, "llama": 2.7, "llama_long": 2.7, "video": 0.82}
 
 
 @dataclasses.dataclass(frozen=True)
