@@ -23,6 +23,11 @@
 
 // log2 of the neighbouring query-block rows a KV group keeps on one XCD in the
 // sparse kernel (see xcd_map)
+// 1: raise wave priority around the MFMA blocks (s_setprio), so a wave issuing
+// matrix work is preferred over one in its softmax phase on the same SIMD
+#ifndef XATTN_ATTN_SETPRIO
+#define XATTN_ATTN_SETPRIO 0
+#endif
 // 1: software-pipelined attention loop (S(t+1) MFMAs overlap the softmax of
 // tile t); 0: the plain loop
 #ifndef XATTN_ATTN_PIPELINE
@@ -276,6 +281,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     const unsigned char* Vb = Vs + buf * L::TILE_B;
     // S^T tiles n = 0, 1: keys k0 + 32n + [8(r/4) + 4hh + r%4], query q0 + l32
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);  // MFMA issue first on the SIMD
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
 #pragma unroll
@@ -285,6 +291,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
         sacc[n] = mfma32x32x16(ka, qf[kk], sacc[n]);
       }
     }
+    if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
     if (CAUSAL && (k0 + L::KT - 1 > q0)) {
       const int qi = q0 + l32;
 #pragma unroll
@@ -300,7 +307,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[n][r]);
-    mx = fmaxf(mx, xor32(mx));
+    mx = halves_max(mx);
     // Lazy rescaling (exact): O and l share the reference m_run, so the
     // reference may lag the true running max as long as 2^(s*c - m_run) stays
     // small. It is raised only when the tile max exceeds it by more than 8
@@ -333,6 +340,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
 
     // O^T[d][q] += V^T[d][key] P^T[key][q] over 16-key chunks tc
     const int G16 = lane >> 4, s16 = lane & 15;
+    if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int tc = 0; tc < 4; ++tc) {
       const int vrow = 16 * tc + 4 * (G16 >> 1) + (s16 >> 2);
@@ -346,6 +354,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
         o[d] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pb[tc], o[d]);
       }
     }
+    if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   __syncthreads();  // block list visible
@@ -425,7 +434,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[n][r]);
-      mx = fmaxf(mx, xor32(mx));
+      mx = halves_max(mx);
       const float m_tile = mx * a.scale_log2;
       float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       bf16x8 pb[4];
@@ -541,7 +550,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) * ln 2
   if (!live) return;
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = halves_sum(l_run);
   const float inv = 1.f / l_tot;
   const int qi = q0 + l32;
   uint16_t* orow = a.out + (bh * a.M + qi) * C;

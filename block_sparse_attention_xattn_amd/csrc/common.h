@@ -46,6 +46,19 @@ __device__ __forceinline__ float xor32(float v) {
   return __shfl_xor(v, 32, 64);
 }
 
+// Reductions across the two wave halves without an LDS round trip: the gfx950
+// v_permlane32_swap(a, a) returns r0 = (lo, lo) and r1 = (hi, hi), so
+// op(r0, r1) is op(v[l], v[l ^ 32]) in every lane, with identical operand order
+// in both halves.
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Read 4 bf16 from LDS with the gfx950 transposing read: within each group of
 // 16 lanes, lane t receives element (t % 4) of the 8-byte chunks addressed by
 // lanes 4c + t/4, for c = 0..3.

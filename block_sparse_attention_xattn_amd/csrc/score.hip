@@ -222,13 +222,13 @@ __global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a)
           float m = v[r0];
 #pragma unroll
           for (int u = 1; u < NR; ++u) m = fmaxf(m, v[r0 + u]);
-          m = fmaxf(m, xor32(m));
+          m = halves_max(m);
           float s = 0.f;
           if (m != -INFINITY) {
 #pragma unroll
             for (int u = 0; u < NR; ++u) s += fast_exp2(v[r0 + u] - m);
           }
-          s += xor32(s);
+          s = halves_sum(s);
           const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
           const int j = jb + 8 * (r0 >> 2);
           const int J = j / RB;
