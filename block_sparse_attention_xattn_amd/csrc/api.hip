@@ -76,6 +76,20 @@ xattn_status check_tau(const xattn_problem* p, const float* tau, xattn::TauArray
   return XATTN_OK;
 }
 
+xattn_status do_partials(const xattn_problem* p, const void* q, const void* k, float score_scale,
+                         void* ws, hipStream_t st) {
+  const xattn::Shape s = shape_of(p);
+  hipError_t e;
+  if (p->dtype == XATTN_BF16)
+    e = xattn::launch_score_partials_bf16(s, static_cast<const uint16_t*>(q),
+                                          static_cast<const uint16_t*>(k), score_scale,
+                                          static_cast<float*>(ws), st);
+  else
+    e = xattn::launch_score_partials_f32(s, static_cast<const float*>(q), static_cast<const float*>(k),
+                                         score_scale, static_cast<float*>(ws), st);
+  return hip_status(e, "score partials launch");
+}
+
 xattn_status do_score(const xattn_problem* p, const void* q, const void* k, float score_scale,
                       float* block_scores, void* ws, size_t ws_bytes, hipStream_t st) {
   const xattn::Shape s = shape_of(p);
@@ -196,9 +210,11 @@ xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
   if (!ws || ws_bytes < need)
     return fail(XATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if ((s = do_score(p, q, k, score_scale, block_scores, ws, ws_bytes, st)) != XATTN_OK) return s;
-  if ((s = hip_status(xattn::launch_select(shape_of(p), block_scores, t, mask, kv_idx, kv_cnt, st),
-                      "select launch")) != XATTN_OK)
+  // partials, then normalisation and selection fused in one launch
+  if ((s = do_partials(p, q, k, score_scale, ws, st)) != XATTN_OK) return s;
+  if ((s = hip_status(xattn::launch_score_select(shape_of(p), static_cast<const float*>(ws), block_scores,
+                                                 t, mask, kv_idx, kv_cnt, st),
+                      "score+select launch")) != XATTN_OK)
     return s;
   return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, st);
 }

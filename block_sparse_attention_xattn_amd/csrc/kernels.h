@@ -34,6 +34,11 @@ struct TauArray {
 hipError_t launch_select(const Shape& s, const float* block_scores, const TauArray& tau,
                          uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st);
 
+// Stages 2+3 fused (one launch per layer in xattn_prefill): block scores from
+// the partials, written out, then selected without re-reading them.
+hipError_t launch_score_select(const Shape& s, const float* ws, float* block_scores, const TauArray& tau,
+                               uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st);
+
 // Stage 4: attention over listed key blocks (kv_idx == nullptr: every candidate).
 hipError_t launch_attn_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, const int32_t* kv_idx, const int32_t* kv_cnt,

@@ -26,6 +26,7 @@
 // the reversal costs only address arithmetic.
 #include "common.h"
 #include "kernels.h"
+#include "score_row.h"
 
 namespace xattn {
 
@@ -289,73 +290,14 @@ struct FinalizeArgs {
 
 template <int RB>
 __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
-  __shared__ float red_m[4][32], red_s[4][32];
-  __shared__ float lse[32];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ ScoreRowLds sh;
   const size_t row = blockIdx.x;  // bh * NB + I
   const int I = (int)(row % a.NB);
   const size_t bh = row / a.NB;
   const int n_cand = a.causal ? I + 1 : a.NB;
-  const float* L = a.ws + (bh * (size_t)a.NB + I) * (size_t)a.NB * a.r;  // [J][t] of row I
-  constexpr int r = RB;
-
-  // pass 1: per strided row t, log2-sum-exp over candidate blocks
-  float m[RB], s[RB];
-#pragma unroll
-  for (int t = 0; t < r; ++t) { m[t] = -INFINITY; s[t] = 0.f; }
-  for (int J = tid; J < n_cand; J += 256) {
-    const float* p = L + (size_t)J * r;
-#pragma unroll
-    for (int t = 0; t < r; ++t) {
-      const float x = p[t];
-      const float mn = fmaxf(m[t], x);
-      if (mn != -INFINITY) {
-        s[t] = s[t] * fast_exp2(m[t] - mn) + fast_exp2(x - mn);
-        m[t] = mn;
-      }
-    }
-  }
-#pragma unroll
-  for (int t = 0; t < r; ++t) {
-    float mt = m[t], stv = s[t];
-    for (int off = 32; off > 0; off >>= 1) {
-      const float mo = __shfl_xor(mt, off, 64), so = __shfl_xor(stv, off, 64);
-      const float mn = fmaxf(mt, mo);
-      if (mn != -INFINITY) {
-        stv = stv * fast_exp2(mt - mn) + so * fast_exp2(mo - mn);
-        mt = mn;
-      }
-    }
-    if (lane == 0) { red_m[wave][t] = mt; red_s[wave][t] = stv; }
-  }
-  __syncthreads();
-  if (tid < r) {
-    float mt = -INFINITY, stv = 0.f;
-    for (int w = 0; w < 4; ++w) {
-      const float mo = red_m[w][tid], so = red_s[w][tid];
-      const float mn = fmaxf(mt, mo);
-      if (mn != -INFINITY) {
-        stv = stv * fast_exp2(mt - mn) + so * fast_exp2(mo - mn);
-        mt = mn;
-      }
-    }
-    lse[tid] = mt + log2f(stv);
-  }
-  __syncthreads();
-
-  // pass 2: block score = (1/r) sum_t 2^(L[J][t] - lse_t)
+  const float* L = a.ws + (bh * (size_t)a.NB + I) * (size_t)a.NB * RB;  // [J][t] of row I
   float* orow = a.out + row * a.NB;
-  const float inv_r = 1.f / (float)r;
-  for (int J = tid; J < a.NB; J += 256) {
-    float sc = 0.f;
-    if (J < n_cand) {
-      const float* p = L + (size_t)J * r;
-#pragma unroll
-      for (int t = 0; t < r; ++t) sc += fast_exp2(p[t] - lse[t]);
-      sc *= inv_r;
-    }
-    orow[J] = sc;
-  }
+  block_score_row<RB>(L, n_cand, a.NB, sh, [&](int J, float sc) { orow[J] = sc; });
 }
 
 // ------------------------------------------------------------------ launchers

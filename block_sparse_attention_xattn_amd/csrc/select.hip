@@ -16,6 +16,7 @@
 // ascending compaction to kv_idx.
 #include "common.h"
 #include "kernels.h"
+#include "score_row.h"
 
 namespace xattn {
 
@@ -48,33 +49,26 @@ __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
   return x;
 }
 
-__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
-  __shared__ uint64_t keys[SEL_MAX];
-  __shared__ uint8_t flags[SEL_MAX];
-  __shared__ double wsum[4];
-  __shared__ int wcnt[4];
+struct SelectLds {
+  uint64_t keys[SEL_MAX];
+  uint8_t flags[SEL_MAX];
+  double wsum[4];
+  int wcnt[4];
+};
 
+// Candidate p (score bits, index) as a descending-sortable key. Block scores
+// are non-negative, so their IEEE bits order like the values.
+__device__ __forceinline__ uint64_t sel_key(float score, int p) {
+  return ((uint64_t)__float_as_uint(score) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)p);
+}
+
+// With keys[0, npad) filled (keys[p] = 0 for p >= n), flags[0, NB) zeroed and
+// a barrier passed: sort, cut at tau, add the diagonal, write the row.
+__device__ void select_from_keys(SelectLds& sh, int n, int npad, int NB, int I, float tau, size_t row,
+                                 uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const size_t row = blockIdx.x;  // (b*Hq + h)*NB + I
-  const int I = (int)(row % a.NB);
-  const int h = (int)((row / a.NB) % a.Hq);
-  const int NB = a.NB;
-  const int n = a.causal ? I + 1 : NB;
-  int npad = 1;
-  while (npad < n) npad <<= 1;
-  const float* srow = a.scores + row * NB;
-
-  for (int p = tid; p < npad; p += 256) {
-    uint64_t key = 0;
-    if (p < n) {
-      const uint32_t bits = __float_as_uint(srow[p]);
-      key = ((uint64_t)bits << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)p);
-    }
-    keys[p] = key;
-  }
-  for (int p = tid; p < NB; p += 256) flags[p] = 0;
-  __syncthreads();
-
+  uint64_t* keys = sh.keys;
+  uint8_t* flags = sh.flags;
   // bitonic sort, descending
   for (int k = 2; k <= npad; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
@@ -92,7 +86,6 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     }
   }
 
-  const float tau = a.tau.v[h];
   int kstar;
   if (tau >= 1.f) {
     kstar = n;
@@ -104,11 +97,11 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
     double run = 0.0;
     for (int p = p0; p < p1; ++p) run += (double)__uint_as_float((uint32_t)(keys[p] >> 32));
     const double incl = wave_incl_scan(run, lane);
-    if (lane == 63) wsum[wave] = incl;
+    if (lane == 63) sh.wsum[wave] = incl;
     __syncthreads();
     double before = incl - run;
-    for (int w = 0; w < wave; ++w) before += wsum[w];
-    const double total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    for (int w = 0; w < wave; ++w) before += sh.wsum[w];
+    const double total = sh.wsum[0] + sh.wsum[1] + sh.wsum[2] + sh.wsum[3];
     const double thresh = (double)tau * total;
     int below = 0;
     double c = before;
@@ -117,17 +110,17 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
       if (c < thresh) ++below;
     }
     const int wb = wave_incl_scan_i(below, lane);
-    if (lane == 63) wcnt[wave] = wb;
+    if (lane == 63) sh.wcnt[wave] = wb;
     __syncthreads();
-    const int nbelow = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    const int nbelow = sh.wcnt[0] + sh.wcnt[1] + sh.wcnt[2] + sh.wcnt[3];
     kstar = (thresh <= 0.0) ? 0 : min(nbelow + 1, n);
   }
   for (int p = tid; p < kstar; p += 256) flags[0xFFFFFFFFu - (uint32_t)(keys[p] & 0xFFFFFFFFu)] = 1;
   if (tid == 0) flags[I] = 1;  // diagonal block
   __syncthreads();
 
-  if (a.mask) {
-    uint8_t* mrow = a.mask + row * NB;
+  if (mask) {
+    uint8_t* mrow = mask + row * NB;
     for (int p = tid; p < NB; p += 256) mrow[p] = flags[p];
   }
   // ascending compaction: per-thread contiguous runs of J
@@ -137,14 +130,84 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   for (int p = p0; p < p1; ++p) mine += flags[p];
   const int incl = wave_incl_scan_i(mine, lane);
   __syncthreads();  // wcnt reuse
-  if (lane == 63) wcnt[wave] = incl;
+  if (lane == 63) sh.wcnt[wave] = incl;
   __syncthreads();
   int pos = incl - mine;
-  for (int w = 0; w < wave; ++w) pos += wcnt[w];
-  int32_t* irow = a.kv_idx + row * NB;
+  for (int w = 0; w < wave; ++w) pos += sh.wcnt[w];
+  int32_t* irow = kv_idx + row * NB;
   for (int p = p0; p < p1; ++p)
     if (flags[p]) irow[pos++] = p;
-  if (tid == 0) a.kv_cnt[row] = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+  if (tid == 0) kv_cnt[row] = sh.wcnt[0] + sh.wcnt[1] + sh.wcnt[2] + sh.wcnt[3];
+}
+
+__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
+  __shared__ SelectLds sh;
+  const int tid = threadIdx.x;
+  const size_t row = blockIdx.x;  // (b*Hq + h)*NB + I
+  const int I = (int)(row % a.NB);
+  const int h = (int)((row / a.NB) % a.Hq);
+  const int NB = a.NB;
+  const int n = a.causal ? I + 1 : NB;
+  int npad = 1;
+  while (npad < n) npad <<= 1;
+  const float* srow = a.scores + row * NB;
+  for (int p = tid; p < npad; p += 256) sh.keys[p] = p < n ? sel_key(srow[p], p) : 0;
+  for (int p = tid; p < NB; p += 256) sh.flags[p] = 0;
+  __syncthreads();
+  select_from_keys(sh, n, npad, NB, I, a.tau.v[h], row, a.mask, a.kv_idx, a.kv_cnt);
+}
+
+// Fused stage 2 + 3: the row's block scores are computed from the partials
+// (written out as xattn_score would), kept in LDS as sort keys, and selected
+// without a round trip through HBM.
+struct FusedArgs {
+  const float* ws;
+  float* scores;
+  uint8_t* mask;
+  int32_t* kv_idx;
+  int32_t* kv_cnt;
+  int Hq, NB, causal;
+  TauArray tau;
+};
+
+template <int RB>
+__global__ __launch_bounds__(256) void score_select_kernel(FusedArgs a) {
+  __shared__ SelectLds sh;
+  __shared__ ScoreRowLds shs;
+  const int tid = threadIdx.x;
+  const size_t row = blockIdx.x;  // (b*Hq + h)*NB + I
+  const int I = (int)(row % a.NB);
+  const size_t bh = row / a.NB;
+  const int h = (int)(bh % a.Hq);
+  const int NB = a.NB;
+  const int n = a.causal ? I + 1 : NB;
+  int npad = 1;
+  while (npad < n) npad <<= 1;
+  const float* L = a.ws + (bh * (size_t)NB + I) * (size_t)NB * RB;
+  float* orow = a.scores + row * NB;
+  for (int p = tid; p < NB; p += 256) sh.flags[p] = 0;
+  for (int p = n + tid; p < npad; p += 256) sh.keys[p] = 0;
+  block_score_row<RB>(L, n, NB, shs, [&](int J, float sc) {
+    orow[J] = sc;
+    if (J < n) sh.keys[J] = sel_key(sc, J);
+  });
+  __syncthreads();
+  select_from_keys(sh, n, npad, NB, I, a.tau.v[h], row, a.mask, a.kv_idx, a.kv_cnt);
+}
+
+hipError_t launch_score_select(const Shape& s, const float* ws, float* block_scores, const TauArray& tau,
+                               uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st) {
+  FusedArgs a{ws, block_scores, mask, kv_idx, kv_cnt, s.Hq, s.NB(), s.causal, tau};
+  const dim3 grid((unsigned)((size_t)s.B * s.Hq * s.NB()));
+  switch (s.r()) {
+    case 2: hipLaunchKernelGGL(score_select_kernel<2>, grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL(score_select_kernel<4>, grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL(score_select_kernel<8>, grid, dim3(256), 0, st, a); break;
+    case 16: hipLaunchKernelGGL(score_select_kernel<16>, grid, dim3(256), 0, st, a); break;
+    case 32: hipLaunchKernelGGL(score_select_kernel<32>, grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const Shape& s, const float* block_scores, const TauArray& tau,

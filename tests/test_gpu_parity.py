@@ -268,3 +268,31 @@ def test_nonfinite_inputs_terminate(xa):
     torch.cuda.synchronize()
     assert bufs.kv_cnt.min().item() >= 1
     assert bufs.kv_cnt.max().item() <= M // block
+
+
+@pytest.mark.parametrize("name,over", [("llama32k", dict(M=4096, Hq=8, Hkv=2)),
+                                       ("llama128k", dict(M=4096, Hq=4, Hkv=1)),
+                                       ("video", dict(M=2560, Hq=2, Hkv=2)),
+                                       ("tiny", {})])
+def test_fused_prefill_equals_stagewise_calls(xa, name, over):
+    # xattn_prefill normalises and selects in one launch; it must reproduce the
+    # separate xattn_score + xattn_select + bsa_fwd calls bit for bit
+    w = wl.WORKLOADS[name].scaled(**over)
+    x = wl.make_inputs(w)
+    sscale, smscale = wl.default_scales(w)
+    qd, kd, vd = x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV)
+    fused = xa.xattn_prefill(qd, kd, vd, x["tau"], w.block, w.stride, sscale, smscale, w.causal)
+    sc = xa.xattn_score(qd, kd, w.block, w.stride, sscale, w.causal)
+    mk, idx, cnt = xa.xattn_select(sc, x["tau"], w.block, w.stride, w.causal, Hkv=w.Hkv, C=w.C,
+                                   dtype=qd.dtype)
+    out, _ = xa.bsa_fwd(qd, kd, vd, idx, cnt, w.block, smscale, w.causal)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.block_scores, sc)
+    assert torch.equal(fused.mask, mk)
+    assert torch.equal(fused.kv_cnt, cnt)
+    c = cnt.cpu().numpy().reshape(-1)
+    fi = fused.kv_idx.cpu().numpy().reshape(len(c), -1)
+    si = idx.cpu().numpy().reshape(len(c), -1)
+    for row, n in enumerate(c):
+        assert (fi[row, :n] == si[row, :n]).all()
+    assert torch.equal(fused.out, out)
