@@ -37,9 +37,13 @@ EXPORTS = (
 )
 
 
+ANTIDIAGONAL = 0
+DIAGONAL = 1
+
+
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("B", "Hq", "Hkv", "M", "C", "block", "stride", "causal", "dtype")]
+                ("B", "Hq", "Hkv", "M", "C", "block", "stride", "causal", "dtype", "pattern")]
 
 
 _P = ctypes.POINTER(Problem)
@@ -80,18 +84,18 @@ def _check(status: int):
         raise XAttnError(status)
 
 
-def problem(B, Hq, Hkv, M, C, block, stride, causal, dtype) -> Problem:
+def problem(B, Hq, Hkv, M, C, block, stride, causal, dtype, pattern=ANTIDIAGONAL) -> Problem:
     """C struct for the given sizes; dtype is torch.bfloat16/torch.float32 or 0/1."""
     if isinstance(dtype, torch.dtype):
         dtype = {torch.bfloat16: XATTN_BF16, torch.float32: XATTN_F32}.get(dtype, 99)
-    return Problem(B, Hq, Hkv, M, C, block, stride, int(bool(causal)), dtype)
+    return Problem(B, Hq, Hkv, M, C, block, stride, int(bool(causal)), dtype, pattern)
 
 
-def _problem_of(q, k, block, stride, causal) -> Problem:
+def _problem_of(q, k, block, stride, causal, pattern=ANTIDIAGONAL) -> Problem:
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be 4-D (B, H, M, C)")
     B, Hq, M, C = q.shape
-    return problem(B, Hq, k.shape[1], M, C, block, stride, causal, q.dtype)
+    return problem(B, Hq, k.shape[1], M, C, block, stride, causal, q.dtype, pattern)
 
 
 def _ptr(t):
@@ -116,10 +120,11 @@ def workspace_bytes(p: Problem) -> int:
     return int(_lib.xattn_score_workspace_bytes(ctypes.byref(p)))
 
 
-def xattn_score(q, k, block, stride, score_scale, causal=True, block_scores=None, ws=None):
+def xattn_score(q, k, block, stride, score_scale, causal=True, block_scores=None, ws=None,
+                pattern=ANTIDIAGONAL):
     """Block scores (B, Hq, NB, NB) float32."""
     _same(q, k)
-    p = _problem_of(q, k, block, stride, causal)
+    p = _problem_of(q, k, block, stride, causal, pattern)
     nb = q.shape[2] // block
     if block_scores is None:
         block_scores = torch.empty((q.shape[0], q.shape[1], nb, nb), dtype=torch.float32, device=q.device)
@@ -183,8 +188,9 @@ def dense_fwd(q, k, v, block, sm_scale, causal=True, out=None, want_lse=False):
 class PrefillBuffers:
     """Reusable device buffers for xattn_prefill (allocated once per shape)."""
 
-    def __init__(self, q, k, block, stride, causal=True, want_mask=True, want_lse=False):
-        p = _problem_of(q, k, block, stride, causal)
+    def __init__(self, q, k, block, stride, causal=True, want_mask=True, want_lse=False,
+                 pattern=ANTIDIAGONAL):
+        p = _problem_of(q, k, block, stride, causal, pattern)
         B, Hq, M, C = q.shape
         nb = M // block
         dev = q.device
@@ -198,10 +204,11 @@ class PrefillBuffers:
         self.lse = torch.empty((B, Hq, M), dtype=torch.float32, device=dev) if want_lse else None
 
 
-def xattn_prefill(q, k, v, tau, block, stride, score_scale, sm_scale, causal=True, buffers=None):
+def xattn_prefill(q, k, v, tau, block, stride, score_scale, sm_scale, causal=True, buffers=None,
+                  pattern=ANTIDIAGONAL):
     """All three stages in one call. Returns the PrefillBuffers holding the results."""
     _same(q, k, v)
-    bufs = buffers or PrefillBuffers(q, k, block, stride, causal)
+    bufs = buffers or PrefillBuffers(q, k, block, stride, causal, pattern=pattern)
     tau_h = _tau_host(tau, q.shape[1])
     b = bufs
     _check(_lib.xattn_prefill(ctypes.byref(b.problem), _ptr(q), _ptr(k), _ptr(v), tau_h.data_ptr(),

@@ -33,6 +33,8 @@ xattn_status check_problem(const xattn_problem* p, bool need_stride = true) {
       (need_stride && p->stride < 1))
     return fail(XATTN_ERR_SHAPE, "B, Hq, Hkv, M, C, block and stride must be positive");
   if (p->causal != 0 && p->causal != 1) return fail(XATTN_ERR_ARG, "causal must be 0 or 1");
+  if (p->pattern != XATTN_ANTIDIAGONAL && p->pattern != XATTN_DIAGONAL)
+    return fail(XATTN_ERR_ARG, "pattern %d is neither antidiagonal nor diagonal", p->pattern);
   if (p->Hq % p->Hkv) return fail(XATTN_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
   if (p->Hq > XATTN_MAX_HEADS) return fail(XATTN_ERR_UNSUPPORTED, "Hq=%d exceeds %d", p->Hq, XATTN_MAX_HEADS);
   if (p->M % p->block) return fail(XATTN_ERR_SHAPE, "M=%d is not a multiple of block=%d", p->M, p->block);
@@ -52,7 +54,7 @@ xattn_status check_problem(const xattn_problem* p, bool need_stride = true) {
 }
 
 xattn::Shape shape_of(const xattn_problem* p) {
-  return xattn::Shape{p->B, p->Hq, p->Hkv, p->M, p->C, p->block, p->stride, p->causal};
+  return xattn::Shape{p->B, p->Hq, p->Hkv, p->M, p->C, p->block, p->stride, p->causal, p->pattern};
 }
 
 xattn_status check_scale(float x, const char* name) {

@@ -11,6 +11,7 @@ namespace xattn {
 
 struct Shape {
   int B, Hq, Hkv, M, C, block, stride, causal;
+  int diagonal;  // 1: scoring pairs q[iS+s] with k[jS+s] instead of k[jS+S-1-s]
   int NB() const { return M / block; }
   int R() const { return M / stride; }
   int r() const { return block / stride; }

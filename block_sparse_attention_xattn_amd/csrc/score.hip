@@ -35,7 +35,8 @@ struct ScoreArgs {
   const uint16_t* k;
   float* ws;
   int B, Hq, Hkv, M, S, R, NB;
-  int T;          // strided 128-tiles per head: ceil(R / 128)
+  int diagonal;   // 1: key row j*S + s instead of j*S + S-1-s
+  int T;          // strided tiles per head: ceil(R / SC_TILE)
   int pairs;      // tile pairs per head
   float scale2;   // score_scale * log2(e)
 };
@@ -119,13 +120,15 @@ __global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a)
     const int id = tid + SC_NT * p;
     const int row = id / SC_CPR, col = (id % SC_CPR) * 8;
     const int j = min(j0 + row, a.R - 1), i = min(i0 + row, a.R - 1);
-    kp[p] = kh + (size_t)(j * S + S - 1) * C + col;   // stride group read in reverse
+    // antidiagonal: the stride group is read in reverse (row j*S + S-1-s)
+    kp[p] = kh + (size_t)(j * S + (a.diagonal ? 0 : S - 1)) * C + col;
     qp[p] = qh + (size_t)(i * S) * C + col;
   }
+  const int kdir = a.diagonal ? 1 : -1;
   typedef u32x4 Stage[2 * LPT];  // K chunks then Q chunks
   auto load_chunk = [&](int c, Stage& r) {
     const int srow = (SC_KC * c) / C, col0 = (SC_KC * c) % C;
-    const int koff = -srow * C + col0, qoff = srow * C + col0;
+    const int koff = kdir * srow * C + col0, qoff = srow * C + col0;
 #pragma unroll
     for (int p = 0; p < LPT; ++p) {
       r[p] = *reinterpret_cast<const u32x4*>(kp[p] + koff);
@@ -245,7 +248,7 @@ struct ScoreArgsF32 {
   const float* q;
   const float* k;
   float* ws;
-  int B, Hq, Hkv, M, C, S, R, NB, r, causal;
+  int B, Hq, Hkv, M, C, S, R, NB, r, causal, diagonal;
   float scale2;
 };
 
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(256) void score_partials_f32_kernel(ScoreArgsF32 a)
     float dot = 0.f;
     for (int st = 0; st < a.S; ++st) {
       const float* qr = qh + (size_t)(i * a.S + st) * a.C;
-      const float* kr = kh + (size_t)(j * a.S + a.S - 1 - st) * a.C;
+      const float* kr = kh + (size_t)(j * a.S + (a.diagonal ? st : a.S - 1 - st)) * a.C;
       for (int c = 0; c < a.C; ++c) dot = fmaf(qr[c], kr[c], dot);
     }
     const float x = dot * a.scale2;
@@ -329,7 +332,7 @@ hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const u
   const int R = s.R();
   const int T = (R + SC_TILE - 1) / SC_TILE;
   const int pairs = s.causal ? T * (T + 1) / 2 : T * T;
-  ScoreArgs a{q, k, ws, s.B, s.Hq, s.Hkv, s.M, s.stride, R, s.NB(), T, pairs,
+  ScoreArgs a{q, k, ws, s.B, s.Hq, s.Hkv, s.M, s.stride, R, s.NB(), s.diagonal, T, pairs,
               score_scale * kLog2e};
   if (s.C == 128) return launch_partials_c<128>(s, a, st);
   if (s.C == 64) return launch_partials_c<64>(s, a, st);
@@ -339,7 +342,7 @@ hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const u
 hipError_t launch_score_partials_f32(const Shape& s, const float* q, const float* k,
                                      float score_scale, float* ws, hipStream_t st) {
   ScoreArgsF32 a{q, k, ws, s.B, s.Hq, s.Hkv, s.M, s.C, s.stride, s.R(), s.NB(), s.r(),
-                 s.causal, score_scale * kLog2e};
+                 s.causal, s.diagonal, score_scale * kLog2e};
   const size_t total = (size_t)s.R() * s.NB() * s.B * s.Hq;
   hipLaunchKernelGGL(score_partials_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
                      0, st, a);

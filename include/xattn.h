@@ -82,7 +82,14 @@ typedef struct {
   int32_t stride; /* antidiagonal stride S, divides block */
   int32_t causal; /* 1: key j visible to query i iff j <= i; 0: all keys */
   int32_t dtype;  /* xattn_dtype of Q, K, V and O */
+  int32_t pattern; /* xattn_pattern of the strided scoring (0 = antidiagonal) */
 } xattn_problem;
+
+/* Which line of each stride x stride tile the scoring sums:
+ *  ANTIDIAGONAL (the method, [XA-abs]): query row i*S+s with key row j*S+S-1-s;
+ *  DIAGONAL (the older variant compared in [DuSA] Response to Q2 and in the
+ *  [XA-sum] ablation table): query row i*S+s with key row j*S+s. */
+typedef enum { XATTN_ANTIDIAGONAL = 0, XATTN_DIAGONAL = 1 } xattn_pattern;
 
 /* ABI version of the loaded library (XATTN_ABI_VERSION). */
 int32_t xattn_abi_version(void);
@@ -103,7 +110,8 @@ size_t xattn_score_workspace_bytes(const xattn_problem* p);
  * [DuSA] Response to Q2).
  *
  * For strided query row i and strided key row j (i, j < R):
- *   A'[i][j] = sum_{s<S} dot(q[i*S+s], k[j*S+S-1-s]),  logit = score_scale*A'.
+ *   A'[i][j] = sum_{s<S} dot(q[i*S+s], k[j*S+S-1-s]),  logit = score_scale*A'
+ * (k[j*S+s] instead for p->pattern = XATTN_DIAGONAL).
  * Causal problems keep j <= i. Each strided row is softmax-normalised over its
  * keys, and the probabilities are summed over each r x r tile:
  *   block_scores[b][h][I][J] = (1/r) * sum_{i in I, j in J} softmax_j(logit[i][j]).

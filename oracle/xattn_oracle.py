@@ -101,13 +101,22 @@ def reversed_key_rows(kh: np.ndarray, stride: int) -> np.ndarray:
 
 
 def strided_logits(qh, kh, stride: int, score_scale: float, causal: bool,
-                   rows: slice | None = None) -> np.ndarray:
-    """Scaled strided antidiagonal logits for strided query ``rows`` vs all keys.
+                   rows: slice | None = None, pattern: str = "antidiagonal") -> np.ndarray:
+    """Scaled strided logits for strided query ``rows`` vs all keys.
 
+    ``pattern="antidiagonal"`` (the method) reverses K inside each stride group;
+    ``pattern="diagonal"`` (the older variant the DuSA rebuttal, Response to Q2,
+    describes: plain (M/stride, stride*C) reshapes of Q and K) does not, which
+    sums the main diagonal of each stride x stride tile instead.
     Entries with key j > query i are -inf when ``causal`` (strided level).
     """
     qs = strided_query_rows(qh, stride)
-    ks = reversed_key_rows(kh, stride)
+    if pattern == "antidiagonal":
+        ks = reversed_key_rows(kh, stride)
+    elif pattern == "diagonal":
+        ks = strided_query_rows(kh, stride)
+    else:
+        raise ValueError(pattern)
     if rows is None:
         rows = slice(0, qs.shape[0])
     lo = rows.start
@@ -129,7 +138,7 @@ def strided_logits(qh, kh, stride: int, score_scale: float, causal: bool,
 # ---------------------------------------------------------------------------
 
 def block_score_row(qh, kh, big_i: int, block: int, stride: int,
-                    score_scale: float, causal: bool) -> np.ndarray:
+                    score_scale: float, causal: bool, pattern: str = "antidiagonal") -> np.ndarray:
     """Block scores S^[I, :] (length NB) for query block ``big_i`` of one head."""
     if block % stride:
         raise ValueError("block must be a multiple of the stride")
@@ -137,7 +146,7 @@ def block_score_row(qh, kh, big_i: int, block: int, stride: int,
     r = block // stride
     nb = m // block
     logits = strided_logits(qh, kh, stride, score_scale, causal,
-                            rows=slice(big_i * r, (big_i + 1) * r))
+                            rows=slice(big_i * r, (big_i + 1) * r), pattern=pattern)
     # row softmax over keys
     mx = logits.max(axis=1, keepdims=True)
     p = np.exp(logits - mx)
@@ -148,7 +157,7 @@ def block_score_row(qh, kh, big_i: int, block: int, stride: int,
 
 
 def block_scores(q, k, block: int, stride: int, score_scale: float, causal: bool,
-                 heads=None, qblocks=None) -> np.ndarray:
+                 heads=None, qblocks=None, pattern: str = "antidiagonal") -> np.ndarray:
     """Block scores (B, Hq, NB, NB), float64. Rows not in ``qblocks`` stay 0."""
     b_, hq, m, _ = q.shape
     hkv = k.shape[1]
@@ -161,7 +170,7 @@ def block_scores(q, k, block: int, stride: int, score_scale: float, causal: bool
             g = _kv_head(h, hq, hkv)
             for big_i in qblocks:
                 out[b, h, big_i] = block_score_row(q[b, h], k[b, g], big_i, block,
-                                                   stride, score_scale, causal)
+                                                   stride, score_scale, causal, pattern)
     return out
 
 
@@ -288,9 +297,9 @@ def dense(q, k, v, block: int, sm_scale: float, causal: bool, heads=None, qblock
 
 
 def prefill(q, k, v, block: int, stride: int, tau, score_scale: float, sm_scale: float,
-            causal: bool, heads=None, qblocks=None):
+            causal: bool, heads=None, qblocks=None, pattern: str = "antidiagonal"):
     """All three stages: (block_scores, mask, out, lse)."""
-    sc = block_scores(q, k, block, stride, score_scale, causal, heads, qblocks)
+    sc = block_scores(q, k, block, stride, score_scale, causal, heads, qblocks, pattern)
     mk = select(sc, tau, causal, heads, qblocks)
     out, lse = attend(q, k, v, mk, block, sm_scale, causal, heads, qblocks)
     return sc, mk, out, lse

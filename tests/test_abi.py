@@ -40,9 +40,10 @@ def test_version_and_strings(xa):
 
 
 def _p(xa, **kw):
-    base = dict(B=1, Hq=4, Hkv=2, M=1024, C=128, block=128, stride=8, causal=1, dtype=0)
+    base = dict(B=1, Hq=4, Hkv=2, M=1024, C=128, block=128, stride=8, causal=1, dtype=0, pattern=0)
     base.update(kw)
-    return xa.Problem(*[base[k] for k in ("B", "Hq", "Hkv", "M", "C", "block", "stride", "causal", "dtype")])
+    return xa.Problem(*[base[k] for k in ("B", "Hq", "Hkv", "M", "C", "block", "stride", "causal", "dtype",
+                                          "pattern")])
 
 
 FAKE = 0x1000  # never dereferenced: validation fails first
@@ -52,7 +53,7 @@ FAKE = 0x1000  # never dereferenced: validation fails first
     (dict(Hkv=3), 2), (dict(M=1000), 2), (dict(stride=3), 2), (dict(C=96), 5),
     (dict(block=32, stride=4), 5), (dict(stride=128), 5), (dict(stride=1), 5),
     (dict(dtype=7), 3), (dict(causal=2), 4), (dict(Hq=512, Hkv=1), 5), (dict(B=0), 2),
-    (dict(M=4096 * 128 * 2), 5),
+    (dict(M=4096 * 128 * 2), 5), (dict(pattern=2), 4), (dict(pattern=-1), 4),
 ])
 def test_score_rejects_bad_problems(xa, kw, status):
     p = _p(xa, **kw)

@@ -296,3 +296,43 @@ def test_fused_prefill_equals_stagewise_calls(xa, name, over):
     for row, n in enumerate(c):
         assert (fi[row, :n] == si[row, :n]).all()
     assert torch.equal(fused.out, out)
+
+
+@pytest.mark.parametrize("case", [
+    (1, 4, 1, 2048, 128, 128, 8, True, torch.bfloat16, True),
+    (1, 2, 2, 1280, 128, 128, 16, False, torch.bfloat16, False),
+    (1, 2, 1, 512, 64, 64, 4, True, torch.bfloat16, False),
+    (1, 1, 1, 1024, 64, 64, 8, True, torch.float32, True),
+], ids=["bf16-s8-causal", "bf16-s16-noncausal", "bf16-c64-s4", "f32-tiny"])
+def test_diagonal_pattern_score_matches_oracle(xa, case):
+    B, Hq, Hkv, M, C, block, stride, causal, dtype, structured = case
+    q, k, _ = _inputs(B, Hq, Hkv, M, C, dtype, 500 + M, structured)
+    sscale = 1.0 / (stride * math.sqrt(C))
+    got = xa.xattn_score(q.to(DEV), k.to(DEV), block, stride, sscale, causal, pattern=xa.DIAGONAL)
+    torch.cuda.synchronize()
+    ref = oracle.block_scores(f64(q), f64(k), block, stride, sscale, causal, pattern="diagonal")
+    g = got.cpu().numpy().astype(np.float64)
+    viol = np.abs(g - ref) > score_tol(ref)
+    assert not viol.any(), (np.argwhere(viol)[:5], np.abs(g - ref).max())
+    if not structured:   # (sink-dominated structured rows score alike under both patterns)
+        anti = oracle.block_scores(f64(q), f64(k), block, stride, sscale, causal)
+        assert np.abs(anti - ref).max() > 1e-4   # the two patterns really differ here
+
+
+def test_diagonal_pattern_prefill_end_to_end(xa):
+    w = wl.WORKLOADS["llama32k"].scaled(M=2048, Hq=4, Hkv=1)
+    x = wl.make_inputs(w)
+    sscale, smscale = wl.default_scales(w)
+    bufs = xa.xattn_prefill(x["q"].to(DEV), x["k"].to(DEV), x["v"].to(DEV), x["tau"], w.block, w.stride,
+                            sscale, smscale, w.causal, pattern=xa.DIAGONAL)
+    torch.cuda.synchronize()
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    tau = x["tau"].numpy().astype(np.float64)
+    g_sc = bufs.block_scores.cpu().numpy().astype(np.float64)
+    ref_sc = oracle.block_scores(q, k, w.block, w.stride, sscale, w.causal, pattern="diagonal")
+    assert not (np.abs(g_sc - ref_sc) > score_tol(ref_sc)).any()
+    g_mask = bufs.mask.cpu().numpy()
+    _, bad = mask_mismatches(g_mask, oracle.select(g_sc, tau, w.causal), g_sc, tau, w.causal, 1e-5)
+    assert not bad
+    ref_out, _ = oracle.attend(q, k, v, g_mask, w.block, smscale, w.causal)
+    assert np.abs(f64(bufs.out) - ref_out).max() <= 2e-2

@@ -275,3 +275,28 @@ def test_density_counts_candidates():
     eye = np.eye(nb, dtype=np.uint8)[None, None]
     assert oracle.density(eye, True) == pytest.approx(4 / 10)
     assert oracle.density(eye, False) == pytest.approx(4 / 16)
+
+
+@pytest.mark.parametrize("stride,m,c", [(2, 16, 3), (4, 32, 5), (8, 64, 2)])
+def test_diagonal_pattern_equals_bruteforce_diagonal(stride, m, c):
+    # the older diagonal variant: main diagonal of each stride x stride tile
+    rng = _rng(40 + stride)
+    q = rng.standard_normal((m, c))
+    k = rng.standard_normal((m, c))
+    full = q @ k.T
+    r = m // stride
+    brute = np.array([[sum(full[i * stride + a, j * stride + a] for a in range(stride))
+                       for j in range(r)] for i in range(r)])
+    got = oracle.strided_logits(q, k, stride, 1.0, causal=False, pattern="diagonal")
+    np.testing.assert_allclose(got, brute, rtol=1e-12, atol=1e-12)
+    anti = oracle.strided_logits(q, k, stride, 1.0, causal=False)
+    assert np.abs(anti - got).max() > 1e-3
+
+
+def test_diagonal_pattern_block_scores_are_normalised():
+    rng = _rng(44)
+    q = rng.standard_normal((1, 2, 256, 16))
+    k = rng.standard_normal((1, 1, 256, 16))
+    sc = oracle.block_scores(q, k, 32, 4, 0.3, True, pattern="diagonal")
+    np.testing.assert_allclose(sc.sum(-1), 1.0, rtol=1e-12)
+    assert (sc >= 0).all()
