@@ -89,6 +89,7 @@ def run_workload(xa, wl, torch, name, steps, warmup, dense_steps):
     nb = w.nb
     p = xa.problem(B, Hq, w.Hkv, M, C, w.block, w.stride, w.causal, q.dtype)
     ws = torch.empty(xa.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    aws = torch.empty(xa.attn_workspace_bytes(p), dtype=torch.uint8, device=dev)
     scores = torch.empty((B, Hq, nb, nb), dtype=torch.float32, device=dev)
     mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev)
     kv_idx = torch.empty((B, Hq, nb, nb), dtype=torch.int32, device=dev)
@@ -112,7 +113,7 @@ def run_workload(xa, wl, torch, name, steps, warmup, dense_steps):
         xa.xattn_select(scores, tau, w.block, w.stride, w.causal, Hkv=w.Hkv, C=C, dtype=q.dtype,
                         mask=mask, kv_idx=kv_idx, kv_cnt=kv_cnt)
         ev[2].record()
-        xa.bsa_fwd(q, k, v, kv_idx, kv_cnt, w.block, smscale, w.causal, out=out)
+        xa.bsa_fwd(q, k, v, kv_idx, kv_cnt, w.block, smscale, w.causal, out=out, ws=aws)
         ev[3].record()
 
     for _ in range(warmup):

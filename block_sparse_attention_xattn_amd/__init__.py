@@ -21,18 +21,19 @@ LIB_PATH = os.path.join(_HERE, "libxattn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m block_sparse_attention_xattn_amd.build`")
+        f"{LIB_PATH} is missing: build it with `python block_sparse_attention_xattn_amd/build.py`")
 
 _lib = ctypes.CDLL(LIB_PATH)
 
 XATTN_BF16 = 0
 XATTN_F32 = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAX_HEADS = 256
 
 EXPORTS = (
     "xattn_abi_version", "xattn_status_string", "xattn_last_error",
-    "xattn_score_workspace_bytes", "xattn_score", "xattn_select", "bsa_fwd",
+    "xattn_score_workspace_bytes", "xattn_attn_workspace_bytes",
+    "xattn_prefill_workspace_bytes", "xattn_score", "xattn_select", "bsa_fwd",
     "dense_fwd", "xattn_prefill",
 )
 
@@ -55,12 +56,16 @@ _lib.xattn_status_string.argtypes = [ctypes.c_int]
 _lib.xattn_last_error.restype = ctypes.c_char_p
 _lib.xattn_score_workspace_bytes.restype = ctypes.c_size_t
 _lib.xattn_score_workspace_bytes.argtypes = [_P]
+_lib.xattn_attn_workspace_bytes.restype = ctypes.c_size_t
+_lib.xattn_attn_workspace_bytes.argtypes = [_P]
+_lib.xattn_prefill_workspace_bytes.restype = ctypes.c_size_t
+_lib.xattn_prefill_workspace_bytes.argtypes = [_P]
 _lib.xattn_score.restype = ctypes.c_int
 _lib.xattn_score.argtypes = [_P, _vp, _vp, _f, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.xattn_select.restype = ctypes.c_int
 _lib.xattn_select.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.bsa_fwd.restype = ctypes.c_int
-_lib.bsa_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp]
+_lib.bsa_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.dense_fwd.restype = ctypes.c_int
 _lib.dense_fwd.argtypes = [_P, _vp, _vp, _vp, _f, _vp, _vp, _vp]
 _lib.xattn_prefill.restype = ctypes.c_int
@@ -117,7 +122,18 @@ def _same(q, *ts):
 
 
 def workspace_bytes(p: Problem) -> int:
+    """Workspace bytes of xattn_score."""
     return int(_lib.xattn_score_workspace_bytes(ctypes.byref(p)))
+
+
+def attn_workspace_bytes(p: Problem) -> int:
+    """Workspace bytes of bsa_fwd."""
+    return int(_lib.xattn_attn_workspace_bytes(ctypes.byref(p)))
+
+
+def prefill_workspace_bytes(p: Problem) -> int:
+    """Workspace bytes of xattn_prefill."""
+    return int(_lib.xattn_prefill_workspace_bytes(ctypes.byref(p)))
 
 
 def xattn_score(q, k, block, stride, score_scale, causal=True, block_scores=None, ws=None,
@@ -163,14 +179,17 @@ def xattn_select(block_scores, tau, block, stride, causal=True, Hkv=None, C=128,
     return mask, kv_idx, kv_cnt
 
 
-def bsa_fwd(q, k, v, kv_idx, kv_cnt, block, sm_scale, causal=True, out=None, want_lse=False):
+def bsa_fwd(q, k, v, kv_idx, kv_cnt, block, sm_scale, causal=True, out=None, want_lse=False, ws=None):
     """Block-sparse attention: (out, lse or None)."""
     _same(q, k, v)
     p = _problem_of(q, k, block, 0, causal)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
+    if ws is None:
+        ws = torch.empty(max(attn_workspace_bytes(p), 4), dtype=torch.uint8, device=q.device)
     _check(_lib.bsa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(kv_idx), _ptr(kv_cnt),
-                        float(sm_scale), _ptr(out), _ptr(lse), _stream(q.device)))
+                        float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                        _stream(q.device)))
     return out, lse
 
 
@@ -199,7 +218,7 @@ class PrefillBuffers:
         self.mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev) if want_mask else None
         self.kv_idx = torch.empty((B, Hq, nb, nb), dtype=torch.int32, device=dev)
         self.kv_cnt = torch.empty((B, Hq, nb), dtype=torch.int32, device=dev)
-        self.ws = torch.empty(max(workspace_bytes(p), 4), dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(max(prefill_workspace_bytes(p), 4), dtype=torch.uint8, device=dev)
         self.out = torch.empty_like(q)
         self.lse = torch.empty((B, Hq, M), dtype=torch.float32, device=dev) if want_lse else None
 

@@ -1,6 +1,7 @@
 """Build libxattn.so for gfx950 with hipcc (in-tree, next to this file).
 
-Usage: python -m block_sparse_attention_xattn_amd.build [--verbose]
+Usage: python block_sparse_attention_xattn_amd/build.py [--verbose]
+(run by path: the package import would load the library being rebuilt)
 """
 from __future__ import annotations
 

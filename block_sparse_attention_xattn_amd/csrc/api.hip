@@ -110,18 +110,28 @@ xattn_status do_score(const xattn_problem* p, const void* q, const void* k, floa
 
 xattn_status do_attn(const xattn_problem* p, const void* q, const void* k, const void* v,
                      const int32_t* kv_idx, const int32_t* kv_cnt, float sm_scale, void* out,
-                     float* lse, hipStream_t st) {
+                     float* lse, void* queue, hipStream_t st) {
   const xattn::Shape s = shape_of(p);
   hipError_t e;
   if (p->dtype == XATTN_BF16)
     e = xattn::launch_attn_bf16(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                 static_cast<const uint16_t*>(v), kv_idx, kv_cnt, sm_scale,
-                                static_cast<uint16_t*>(out), lse, st);
+                                static_cast<uint16_t*>(out), lse, static_cast<uint32_t*>(queue), st);
   else
     e = xattn::launch_attn_f32(s, static_cast<const float*>(q), static_cast<const float*>(k),
                                static_cast<const float*>(v), kv_idx, kv_cnt, sm_scale,
                                static_cast<float*>(out), lse, st);
   return hip_status(e, "attention launch");
+}
+
+// The attention queue sits after the score partials in xattn_prefill's
+// workspace, 256-byte aligned.
+size_t queue_offset(size_t score_bytes) { return (score_bytes + 255) & ~(size_t)255; }
+
+xattn_status check_workspace(const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws || ws_bytes < need)
+    return fail(XATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  return XATTN_OK;
 }
 
 }  // namespace
@@ -151,15 +161,24 @@ size_t xattn_score_workspace_bytes(const xattn_problem* p) {
   return (size_t)p->B * p->Hq * (size_t)(p->M / p->block) * (size_t)(p->M / p->stride) * sizeof(float);
 }
 
+size_t xattn_attn_workspace_bytes(const xattn_problem* p) {
+  if (check_problem(p, false) != XATTN_OK) return 0;
+  return xattn::kQueueWords * sizeof(uint32_t);
+}
+
+size_t xattn_prefill_workspace_bytes(const xattn_problem* p) {
+  const size_t score = xattn_score_workspace_bytes(p);
+  if (score == 0) return 0;
+  return queue_offset(score) + xattn_attn_workspace_bytes(p);
+}
+
 xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k, float score_scale,
                          float* block_scores, void* ws, size_t ws_bytes, void* stream) {
   xattn_status s = check_problem(p);
   if (s != XATTN_OK) return s;
   if (!q || !k || !block_scores) return fail(XATTN_ERR_NULL, "q, k and block_scores must be non-NULL");
   if ((s = check_scale(score_scale, "score_scale")) != XATTN_OK) return s;
-  const size_t need = xattn_score_workspace_bytes(p);
-  if (!ws || ws_bytes < need)
-    return fail(XATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  if ((s = check_workspace(ws, ws_bytes, xattn_score_workspace_bytes(p))) != XATTN_OK) return s;
   return do_score(p, q, k, score_scale, block_scores, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
@@ -178,13 +197,14 @@ xattn_status xattn_select(const xattn_problem* p, const float* block_scores, con
 
 xattn_status bsa_fwd(const xattn_problem* p, const void* q, const void* k, const void* v,
                      const int32_t* kv_idx, const int32_t* kv_cnt, float sm_scale, void* out,
-                     float* lse, void* stream) {
+                     float* lse, void* ws, size_t ws_bytes, void* stream) {
   xattn_status s = check_problem(p, false);
   if (s != XATTN_OK) return s;
   if (!q || !k || !v || !kv_idx || !kv_cnt || !out)
     return fail(XATTN_ERR_NULL, "q, k, v, kv_idx, kv_cnt and out must be non-NULL");
   if ((s = check_scale(sm_scale, "sm_scale")) != XATTN_OK) return s;
-  return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, static_cast<hipStream_t>(stream));
+  if ((s = check_workspace(ws, ws_bytes, xattn_attn_workspace_bytes(p))) != XATTN_OK) return s;
+  return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, ws, static_cast<hipStream_t>(stream));
 }
 
 xattn_status dense_fwd(const xattn_problem* p, const void* q, const void* k, const void* v,
@@ -193,7 +213,8 @@ xattn_status dense_fwd(const xattn_problem* p, const void* q, const void* k, con
   if (s != XATTN_OK) return s;
   if (!q || !k || !v || !out) return fail(XATTN_ERR_NULL, "q, k, v and out must be non-NULL");
   if ((s = check_scale(sm_scale, "sm_scale")) != XATTN_OK) return s;
-  return do_attn(p, q, k, v, nullptr, nullptr, sm_scale, out, lse, static_cast<hipStream_t>(stream));
+  return do_attn(p, q, k, v, nullptr, nullptr, sm_scale, out, lse, nullptr,
+                 static_cast<hipStream_t>(stream));
 }
 
 xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k, const void* v,
@@ -208,9 +229,7 @@ xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
   if ((s = check_scale(sm_scale, "sm_scale")) != XATTN_OK) return s;
   xattn::TauArray t;
   if ((s = check_tau(p, tau, &t)) != XATTN_OK) return s;
-  const size_t need = xattn_score_workspace_bytes(p);
-  if (!ws || ws_bytes < need)
-    return fail(XATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+  if ((s = check_workspace(ws, ws_bytes, xattn_prefill_workspace_bytes(p))) != XATTN_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   // partials, then normalisation and selection fused in one launch
   if ((s = do_partials(p, q, k, score_scale, ws, st)) != XATTN_OK) return s;
@@ -218,7 +237,8 @@ xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
                                                  t, mask, kv_idx, kv_cnt, st),
                       "score+select launch")) != XATTN_OK)
     return s;
-  return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, st);
+  void* queue = static_cast<char*>(ws) + queue_offset(xattn_score_workspace_bytes(p));
+  return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, queue, st);
 }
 
 }  // extern "C"

@@ -55,9 +55,12 @@ struct AttnArgs {
   const int32_t* kv_cnt;
   uint16_t* out;
   float* lse;
+  uint32_t* queue;   // sparse: kQueueWords zeroed words (per-XCD item counters)
   int B, Hq, Hkv, M, NB;
   float scale_log2;  // sm_scale * log2(e)
 };
+
+constexpr uint32_t kNoItem = 0xffffffffu;
 
 template <int C>
 struct AttnLds {
@@ -95,11 +98,32 @@ struct AttnLds {
 // The 8-wave modes hold two sub-tiles in flight (registers), SINGLE one.
 enum { MODE_SINGLE = 0, MODE_SIBLINGS = 1, MODE_ROWS = 2 };
 
+// Per-mode constants: SLOTS (head, row) pairs per workgroup of NT threads.
+template <int MODE>
+struct AttnMode {
+  static constexpr int SLOTS = MODE == MODE_SINGLE ? 1 : 2;
+};
+
+// Work items of a launch: one per workgroup-sized unit of (b, g, pw, P), where
+// pw numbers the workgroups of one KV group and P the query rows (row pairs).
+struct AttnItems {
+  uint32_t GW, NP, n;
+  __device__ AttnItems(const AttnArgs& a, int MODE) {
+    const uint32_t G = a.Hq / a.Hkv;
+    NP = MODE == MODE_ROWS ? (a.NB + 1) / 2 : a.NB;
+    GW = MODE == MODE_SIBLINGS ? G / 2 : G;
+    n = (uint32_t)a.B * a.Hkv * GW * NP;
+  }
+};
+
+// One work item: all rows of the slots it covers, from the block list to the
+// normalised output. Starts and ends with every wave of the workgroup past a
+// barrier after its last LDS read, so consecutive items may reuse the LDS.
 template <int C, int BLK, bool CAUSAL, bool SPARSE, int MODE>
-__global__ __launch_bounds__(BLK * 2 * (MODE == MODE_SINGLE ? 1 : 2), MODE == MODE_SINGLE ? 2 : 1)
-void attn_fwd_bf16_kernel(AttnArgs a) {
+__device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item,
+                                          unsigned char* smem, int* scan_s) {
   using L = AttnLds<C>;
-  constexpr int SLOTS = MODE == MODE_SINGLE ? 1 : 2;
+  constexpr int SLOTS = AttnMode<MODE>::SLOTS;
   constexpr int WPH = BLK / 32;               // waves per slot (32 query rows each)
   constexpr int NT = 64 * WPH * SLOTS;        // threads
   constexpr int SUB = BLK / L::KT;            // sub-tiles per key block
@@ -110,14 +134,12 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   constexpr int DEPTH = SLOTS == 2 ? 2 : 1;   // sub-tiles in flight in registers
   static_assert(CHUNKS % NT == 0, "tile load must divide evenly");
 
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes(SLOTS)];
   unsigned char* Ks = smem;                      // [2][KT rows][2C bytes], swizzled
   unsigned char* Vs = smem + 2 * L::TILE_B;      // [2][KT rows][2C bytes], swizzled
   // block list (union over the workgroup's slots) and, per entry, a bit per
   // slot that selected it
   uint16_t* idx_s = reinterpret_cast<uint16_t*>(smem + 4 * L::TILE_B);
   uint8_t* memb_s = smem + 4 * L::TILE_B + 2 * L::IDX_MAX;
-  __shared__ int scan_s[SLOTS > 1 ? NT / 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -127,15 +149,11 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   const int hs = wave / WPH;                   // slot of this wave
   const int slice = wave % WPH;                // 32-row slice of the query block
 
-  // ---- work item: heavy query blocks first; the workgroups that share one KV
-  //      head are dispatched to one XCD (one L2), rotating over XCDs per row
+  // ---- decode the item: heavy query rows (large P) come first in item order
   const int G = a.Hq / a.Hkv;
-  const int NP = MODE == MODE_ROWS ? (a.NB + 1) / 2 : a.NB;     // rows (or row pairs)
-  const int GW = MODE == MODE_SIBLINGS ? G / 2 : G;             // workgroups per group
-  const uint32_t n_items = (uint32_t)a.B * a.Hkv * GW * NP;
-  const uint32_t item = SPARSE ? xcd_map(blockIdx.x, n_items, XATTN_SPARSE_GROUP_ON_XCD ? GW : 1,
-                                           XATTN_SPARSE_ROWS_PER_XCD_LOG2)
-                                : xcd_map(blockIdx.x, n_items, GW, 0);
+  const AttnItems its(a, MODE);
+  const int NP = (int)its.NP;
+  const int GW = (int)its.GW;
   const int pw = item % GW;
   uint32_t rest = item / GW;
   const int g = rest % a.Hkv;
@@ -569,6 +587,65 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   if (a.lse && hh == 0) a.lse[bh * a.M + qi] = (m_run + log2f(l_tot)) * kLn2;
 }
 
+// Claims the next item for a persistent workgroup. queue[32 x] counts the
+// items handed out from XCD x's share: the positions w = 8 j + x of xcd_map's
+// order, which the hardware would have dispatched to XCD x. A workgroup serves
+// the share of the XCD it runs on first, then the other shares in turn
+// (stealing once its own runs dry); q, the offset of the share being served,
+// only grows, so a workgroup makes at most (items it runs) + 8 claims. Each
+// position is handed out once; items never wait on one another.
+__device__ __forceinline__ uint32_t claim_item(uint32_t* queue, const uint32_t n,
+                                               const uint32_t K, const uint32_t x0, uint32_t& q) {
+  for (; q < 8; ++q) {
+    const uint32_t x = (x0 + q) & 7u;
+    const uint32_t j = __hip_atomic_fetch_add(queue + 32 * x, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t w = 8ull * j + x;
+    if (w < n) return xcd_map((uint32_t)w, n, K, XATTN_SPARSE_ROWS_PER_XCD_LOG2);
+  }
+  return kNoItem;
+}
+
+// Dense: one workgroup per item, in xcd_map order (rows of equal length
+// within a window, so the hardware's in-order dispatch keeps every engine busy).
+// Sparse: persistent workgroups (as many as fit on the device at once) pull
+// items from per-XCD queues in the same order. Rows of one query block differ
+// by orders of magnitude in length between heads; the hardware dispatches the
+// workgroups of an XCD in order and round-robin over its shader engines, so a
+// one-workgroup-per-item launch parks the long rows of a dense head on one
+// engine and stalls the others behind it. Pulling from a queue keeps every
+// workgroup slot busy until the queues run dry.
+template <int C, int BLK, bool CAUSAL, bool SPARSE, int MODE>
+__global__ __launch_bounds__(BLK * 2 * AttnMode<MODE>::SLOTS, MODE == MODE_SINGLE ? 2 : 1)
+void attn_fwd_bf16_kernel(AttnArgs a) {
+  using L = AttnLds<C>;
+  constexpr int SLOTS = AttnMode<MODE>::SLOTS;
+  constexpr int NT = 64 * (BLK / 32) * SLOTS;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes(SLOTS)];
+  __shared__ int scan_s[SLOTS > 1 ? NT / 64 : 1];
+  const AttnItems its(a, MODE);
+  if constexpr (!SPARSE) {
+    attn_item<C, BLK, CAUSAL, SPARSE, MODE>(a, xcd_map(blockIdx.x, its.n, its.GW, 0), smem, scan_s);
+  } else {
+    __shared__ uint32_t item_s;
+    const uint32_t K = XATTN_SPARSE_GROUP_ON_XCD ? its.GW : 1;
+    const uint32_t x0 = xcc_id();
+    uint32_t q = 0;
+    for (;;) {
+      if (threadIdx.x == 0) item_s = claim_item(a.queue, its.n, K, x0, q);
+      __syncthreads();
+      const uint32_t item = item_s;
+      if (item == kNoItem) break;  // uniform over the workgroup
+      // every thread reads item_s before the barriers inside attn_item, and
+      // thread 0 rewrites it only after them
+      attn_item<C, BLK, CAUSAL, SPARSE, MODE>(a, item, smem, scan_s);
+    }
+  }
+}
+
+// Clears the item queues of a sparse launch (graph-safe: a kernel, not a memset).
+__global__ void clear_queue_kernel(uint32_t* queue) { queue[threadIdx.x] = 0u; }
+
 // ------------------------------------------------------------------ fp32 path
 
 struct AttnArgsF32 {
@@ -636,22 +713,41 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgsF32 a) {
 
 // ------------------------------------------------------------------ launchers
 
+// Workgroups of one kernel instance that fit on the current device at once.
+template <class Kern>
+static int resident_workgroups(Kern kern, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess) return 0;
+  return cus * per_cu;
+}
+
 template <int C, int BLK, int MODE>
 static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t st) {
   const int G = s.Hq / s.Hkv;
   const int NP = MODE == MODE_ROWS ? (s.NB() + 1) / 2 : s.NB();
   const int GW = MODE == MODE_SIBLINGS ? G / 2 : G;
-  const dim3 grid((unsigned)((size_t)s.B * s.Hkv * GW * NP));
-  const dim3 block(BLK * 2 * (MODE == MODE_SINGLE ? 1 : 2));
-  const bool sp = a.kv_idx != nullptr;
-  if (s.causal && sp)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, true, MODE>), grid, block, 0, st, a);
-  else if (s.causal)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, false, MODE>), grid, block, 0, st, a);
-  else if (sp)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, true, MODE>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, false, MODE>), grid, block, 0, st, a);
+  const size_t n_items = (size_t)s.B * s.Hkv * GW * NP;
+  const int threads = BLK * 2 * AttnMode<MODE>::SLOTS;
+  if (a.kv_idx == nullptr) {
+    const dim3 grid((unsigned)n_items);
+    if (s.causal)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, false, MODE>), grid, dim3(threads), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, false, MODE>), grid, dim3(threads), 0, st, a);
+    return hipGetLastError();
+  }
+  if (a.queue == nullptr) return hipErrorInvalidValue;
+  auto kern = s.causal ? attn_fwd_bf16_kernel<C, BLK, true, true, MODE>
+                       : attn_fwd_bf16_kernel<C, BLK, false, true, MODE>;
+  const int slots = resident_workgroups(kern, threads);
+  if (slots <= 0) return hipErrorInvalidDeviceFunction;
+  hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(kQueueWords), 0, st, a.queue);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)(n_items < (size_t)slots ? n_items : (size_t)slots));
+  hipLaunchKernelGGL(kern, grid, dim3(threads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -671,8 +767,9 @@ static hipError_t launch_bf16_cb(const Shape& s, const AttnArgs& a, hipStream_t 
 
 hipError_t launch_attn_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, const int32_t* kv_idx, const int32_t* kv_cnt,
-                            float sm_scale, uint16_t* out, float* lse, hipStream_t st) {
-  AttnArgs a{q, k, v, kv_idx, kv_cnt, out, lse, s.B, s.Hq, s.Hkv, s.M, s.NB(), sm_scale * kLog2e};
+                            float sm_scale, uint16_t* out, float* lse, uint32_t* queue,
+                            hipStream_t st) {
+  AttnArgs a{q, k, v, kv_idx, kv_cnt, out, lse, queue, s.B, s.Hq, s.Hkv, s.M, s.NB(), sm_scale * kLog2e};
   if (s.C == 128 && s.block == 128) return launch_bf16_cb<128, 128>(s, a, st);
   if (s.C == 128 && s.block == 64) return launch_bf16_cb<128, 64>(s, a, st);
   if (s.C == 64 && s.block == 128) return launch_bf16_cb<64, 128>(s, a, st);

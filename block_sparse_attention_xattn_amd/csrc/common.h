@@ -86,6 +86,12 @@ __device__ __forceinline__ uint32_t xcd_map(uint32_t w, uint32_t n, uint32_t K,
   return a * win + ((x + (a >> rot_shift)) & 7u) * K + j % K;
 }
 
+// Index of the XCD (accelerator complex die) the calling wave runs on: the
+// XCC_ID hardware register, bits [3:0].
+__device__ __forceinline__ uint32_t xcc_id() {
+  return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 7u;
+}
+
 __device__ __forceinline__ uint32_t xcd_group4(uint32_t w, uint32_t n) { return xcd_map(w, n, 4); }
 
 }  // namespace xattn

@@ -41,9 +41,14 @@ hipError_t launch_score_select(const Shape& s, const float* ws, float* block_sco
                                uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st);
 
 // Stage 4: attention over listed key blocks (kv_idx == nullptr: every candidate).
+// The sparse bf16 kernel schedules its rows through per-XCD item queues held
+// in `queue` (kQueueWords words of device memory, cleared by the launcher on
+// the stream first); dense launches ignore it.
+constexpr int kQueueWords = 256;
 hipError_t launch_attn_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, const int32_t* kv_idx, const int32_t* kv_cnt,
-                            float sm_scale, uint16_t* out, float* lse, hipStream_t st);
+                            float sm_scale, uint16_t* out, float* lse, uint32_t* queue,
+                            hipStream_t st);
 hipError_t launch_attn_f32(const Shape& s, const float* q, const float* k, const float* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt, float sm_scale,
                            float* out, float* lse, hipStream_t st);

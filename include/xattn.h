@@ -29,7 +29,9 @@
  *    (query block I, key block J).
  *  - The caller owns and allocates every buffer. The library keeps no state,
  *    never allocates, and is re-entrant; scratch memory comes only through
- *    the workspace argument.
+ *    the workspace arguments. A workspace's contents on entry are ignored
+ *    (each call clears what it needs on its stream); calls that may overlap
+ *    in time (other streams) need distinct workspaces.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
  *    call only enqueues work on it and returns without synchronising.
  *  - Arguments are validated on the host before anything is enqueued. On any
@@ -54,7 +56,7 @@
 extern "C" {
 #endif
 
-#define XATTN_ABI_VERSION 1
+#define XATTN_ABI_VERSION 2
 #define XATTN_MAX_HEADS 256
 #define XATTN_MAX_BLOCKS 4096
 
@@ -100,7 +102,7 @@ const char* xattn_status_string(xattn_status s);
 /* Message describing the calling thread's most recent failed call. */
 const char* xattn_last_error(void);
 
-/* Device workspace bytes xattn_score (and xattn_prefill) need for problem p;
+/* Device workspace bytes xattn_score needs for problem p;
  * 0 if p is invalid. The workspace holds per-(strided row, key block) partial
  * log-sum-exp values: B*Hq*NB*R float32. */
 size_t xattn_score_workspace_bytes(const xattn_problem* p);
@@ -147,6 +149,10 @@ xattn_status xattn_select(const xattn_problem* p, const float* block_scores,
                           const float* tau, uint8_t* mask, int32_t* kv_idx,
                           int32_t* kv_cnt, void* stream);
 
+/* Device workspace bytes bsa_fwd needs (a fixed 1 KiB of per-XCD work-queue
+ * counters); 0 if p is invalid. */
+size_t xattn_attn_workspace_bytes(const xattn_problem* p);
+
 /*
  * Stage 4 — block-sparse attention forward ([XA-abs]: block-sparse attention
  * computes only on the important blocks).
@@ -163,10 +169,13 @@ xattn_status xattn_select(const xattn_problem* p, const float* block_scores,
  *  out             device, problem dtype, (B, Hq, M, C).
  *  lse             device float32 (B, Hq, M), natural-log log-sum-exp of the
  *                  scaled logits over A(i); may be NULL.
+ *  ws, ws_bytes    device scratch of at least xattn_attn_workspace_bytes(p):
+ *                  the queues from which the workgroups pull query rows.
  */
 xattn_status bsa_fwd(const xattn_problem* p, const void* q, const void* k,
                      const void* v, const int32_t* kv_idx, const int32_t* kv_cnt,
-                     float sm_scale, void* out, float* lse, void* stream);
+                     float sm_scale, void* out, float* lse, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /*
  * Dense attention forward: bsa_fwd with every candidate block kept (all
@@ -176,10 +185,15 @@ xattn_status dense_fwd(const xattn_problem* p, const void* q, const void* k,
                        const void* v, float sm_scale, void* out, float* lse,
                        void* stream);
 
+/* Device workspace bytes xattn_prefill needs: the score partials, then (at
+ * the next 256-byte boundary) the attention queues; 0 if p is invalid. */
+size_t xattn_prefill_workspace_bytes(const xattn_problem* p);
+
 /*
  * The three stages in one call ([Flex] R Q2: one call in place of standard
  * attention): xattn_score, then xattn_select, then bsa_fwd, all enqueued on
- * `stream`. Arguments as in those calls; mask and lse may be NULL.
+ * `stream`. Arguments as in those calls; mask and lse may be NULL; ws holds at
+ * least xattn_prefill_workspace_bytes(p).
  */
 xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
                            const void* v, const float* tau, float score_scale,

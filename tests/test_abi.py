@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(xa):
 
 
 def test_version_and_strings(xa):
-    assert xa._lib.xattn_abi_version() == 1
+    assert xa._lib.xattn_abi_version() == 2
     for s in range(8):
         assert xa._lib.xattn_status_string(s)
     assert xa._lib.xattn_status_string(99) == b"unknown status"
@@ -66,6 +66,16 @@ def test_workspace_bytes(xa):
     p = _p(xa)
     assert xa.workspace_bytes(p) == 1 * 4 * 8 * 128 * 4
     assert xa.workspace_bytes(_p(xa, Hkv=3)) == 0
+    assert xa.attn_workspace_bytes(p) == 1024
+    assert xa.attn_workspace_bytes(_p(xa, Hkv=3)) == 0
+    # attention ignores the stride
+    assert xa.attn_workspace_bytes(_p(xa, stride=0)) == 1024
+    # score partials, then the queues at the next 256-byte boundary
+    assert xa.prefill_workspace_bytes(p) == 1 * 4 * 8 * 128 * 4 + 1024
+    odd = _p(xa, B=1, Hq=1, Hkv=1, M=192, block=64, stride=32, C=64)   # 3 * 6 * 4 = 72 bytes
+    assert xa.workspace_bytes(odd) == 72
+    assert xa.prefill_workspace_bytes(odd) == 256 + 1024
+    assert xa.prefill_workspace_bytes(_p(xa, stride=0)) == 0
 
 
 def test_null_and_workspace_errors(xa):
@@ -77,8 +87,10 @@ def test_null_and_workspace_errors(xa):
     assert L.xattn_score(ctypes.byref(p), FAKE, FAKE, 0.01, FAKE, None, 1 << 40, None) == 6
     assert L.xattn_score(ctypes.byref(p), FAKE, FAKE, -1.0, FAKE, FAKE, 1 << 40, None) == 4
     assert L.xattn_score(ctypes.byref(p), FAKE, FAKE, math.inf, FAKE, FAKE, 1 << 40, None) == 4
-    assert L.bsa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, 0.1, FAKE, None, None) == 1
-    assert L.bsa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, None, None) == 4
+    assert L.bsa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, None, FAKE, 0.1, FAKE, None, FAKE, 1024, None) == 1
+    assert L.bsa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, FAKE, None, FAKE, 1024, None) == 4
+    assert L.bsa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, None, 1024, None) == 6
+    assert L.bsa_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, None, FAKE, 1023, None) == 6
     assert L.dense_fwd(ctypes.byref(p), FAKE, FAKE, None, 0.1, FAKE, None, None) == 1
     assert L.dense_fwd(ctypes.byref(_p(xa, C=32)), FAKE, FAKE, FAKE, 0.1, FAKE, None, None) == 5
 
@@ -94,6 +106,9 @@ def test_select_rejects_bad_tau(xa):
     assert L.xattn_select(ctypes.byref(p), None, arr, None, FAKE, FAKE, None) == 1
     assert L.xattn_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, arr, 0.01, 0.1, FAKE, None, FAKE, FAKE,
                            FAKE, 16, FAKE, None, None) == 6
+    # the score partials alone are too little: the attention queues follow them
+    assert L.xattn_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, arr, 0.01, 0.1, FAKE, None, FAKE, FAKE,
+                           FAKE, xa.workspace_bytes(p), FAKE, None, None) == 6
 
 
 def test_attention_ignores_stride(xa):

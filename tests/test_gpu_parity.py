@@ -243,7 +243,7 @@ def test_outputs_stay_inside_buffers(xa):
     out_all, out = guarded(B * Hq * M * C, torch.bfloat16, 3.0)
     lse_all, lse = guarded(B * Hq * M, torch.float32, -7.0)
     p = xa.problem(B, Hq, Hkv, M, C, block, 8, 1, torch.bfloat16)
-    ws = torch.empty(xa.workspace_bytes(p), dtype=torch.uint8, device=DEV)
+    ws_all, ws = guarded(xa.prefill_workspace_bytes(p), torch.uint8, 0x5A)
     tau = torch.full((Hq,), 0.9)
     import ctypes
     st = torch.cuda.current_stream().cuda_stream
@@ -254,7 +254,7 @@ def test_outputs_stay_inside_buffers(xa):
     assert rc == 0
     torch.cuda.synchronize()
     for full, fill in ((sc_all, -7.0), (mk_all, 0xAB), (ix_all, -5), (ct_all, -5), (out_all, 3.0),
-                       (lse_all, -7.0)):
+                       (lse_all, -7.0), (ws_all, 0x5A)):
         assert (full[:guard] == fill).all() and (full[-guard:] == fill).all()
 
 
