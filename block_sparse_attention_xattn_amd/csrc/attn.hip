@@ -45,6 +45,11 @@
 #define XATTN_SPARSE_ROWS_PER_XCD_LOG2 0
 #endif
 
+// k-steps of K fragments read from LDS ahead of their MFMAs
+#ifndef XATTN_KBATCH
+#define XATTN_KBATCH 2
+#endif
+
 namespace xattn {
 
 struct AttnArgs {
@@ -252,6 +257,12 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * kk));
+    // Complete the Q loads here. Otherwise the compiler may leave them in flight
+    // into the key loop, and since the load counter is in-order, every first use
+    // of qf per sub-tile would also wait for the next tile's prefetch issued just
+    // before it, serialising the prefetch with the compute.
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qf[kk]));
   }
 
   f32x16 o[DN];
@@ -300,14 +311,24 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
     // S^T tiles n = 0, 1: keys k0 + 32n + [8(r/4) + 4hh + r%4], query q0 + l32
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
     if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);  // MFMA issue first on the SIMD
+    // K fragments are read XATTN_KBATCH k-steps at a time ahead of their MFMAs
+    constexpr int KB = XATTN_KBATCH < KK ? XATTN_KBATCH : KK;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int k0b = 0; k0b < KK; k0b += KB) {
+      bf16x8 ka[KB][2];
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const bf16x8 ka = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(Kb + L::k_off(32 * n + l32, 2 * kk + hh)));
-        sacc[n] = mfma32x32x16(ka, qf[kk], sacc[n]);
-      }
+      for (int u = 0; u < KB; ++u)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          ka[u][n] = __builtin_bit_cast(
+              bf16x8, *reinterpret_cast<const u32x4*>(Kb + L::k_off(32 * n + l32, 2 * (k0b + u) + hh)));
+      // keep the batch's reads ahead of its MFMAs (the scheduler would sink
+      // each read next to its use and expose the LDS latency per pair)
+      if (KB > 1) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < KB; ++u)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) sacc[n] = mfma32x32x16(ka[u][n], qf[k0b + u], sacc[n]);
     }
     if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
     if (CAUSAL && (k0 + L::KT - 1 > q0)) {
