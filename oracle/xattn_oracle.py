@@ -20,7 +20,8 @@ Sources (page title, section):
             section "Response to Q2" (the reshape formulation of XAttention).
   [Flex]    "FlexPrefill: A Context-Aware Sparse Attention Mechanism for
             Efficient Long-Sequence Inference", rebuttal on paperhub.cn,
-            section "R Q3" (minimal |S| under a cumulative-mass constraint).
+            sections "R Q3" (minimal |S| under a cumulative-mass constraint;
+            global, flattened index selection versus query-wise selection).
 
 Notation: Q is (B, Hq, M, C); K, V are (B, Hkv, M, C); query head h reads KV
 head h // (Hq // Hkv). Block size Bk, stride S, r = Bk // S strided rows per
@@ -54,6 +55,8 @@ __all__ = [
     "minimal_set",
     "select_row",
     "select",
+    "select_global_head",
+    "gqa_union",
     "mask_to_index",
     "attend_row",
     "attend",
@@ -211,17 +214,80 @@ def select_row(scores_row: np.ndarray, big_i: int, tau: float, causal: bool) -> 
     return keep
 
 
-def select(scores: np.ndarray, tau, causal: bool, heads=None, qblocks=None) -> np.ndarray:
-    """Mask (B, Hq, NB, NB) uint8 from block scores and per-head ``tau`` (len Hq)."""
+def select_global_head(scores_h: np.ndarray, tau: float, causal: bool) -> np.ndarray:
+    """Global (flattened) selection for one head ([Flex] R Q3): keep-mask (NB, NB).
+
+    Every candidate block (I, J) of the head (J <= I when causal) enters one
+    list in row-major order; the minimal set is taken over that list exactly as
+    for a single row (score descending, ties by list position, i.e. by (I, J)
+    row-major), against tau times the head's total candidate mass. The diagonal
+    blocks are then added.
+    """
+    nb = scores_h.shape[0]
+    rows, cols = [], []
+    for big_i in range(nb):
+        n_cand = big_i + 1 if causal else nb
+        rows.extend([big_i] * n_cand)
+        cols.extend(range(n_cand))
+    rows = np.asarray(rows)
+    cols = np.asarray(cols)
+    flat = _f64(scores_h)[rows, cols]
+    keep = np.zeros((nb, nb), dtype=bool)
+    chosen = minimal_set(flat, tau)
+    keep[rows[chosen], cols[chosen]] = True
+    keep[np.arange(nb), np.arange(nb)] = True
+    return keep
+
+
+def gqa_union(mask: np.ndarray, hkv: int) -> np.ndarray:
+    """GQA union of a mask (B, Hq, NB, NB): every head of a KV group gets the
+    union of the group's kept blocks, row by row.
+
+    Not from the pages: a reuse variant in which the sibling heads that read
+    one KV head share a single block list, so one K/V tile serves all of them.
+    """
+    b_, hq, nb, _ = mask.shape
+    g = hq // hkv
+    out = mask.astype(bool).reshape(b_, hkv, g, nb, nb).any(axis=2, keepdims=True)
+    return np.broadcast_to(out, (b_, hkv, g, nb, nb)).reshape(mask.shape).astype(np.uint8)
+
+
+def select(scores: np.ndarray, tau, causal: bool, heads=None, qblocks=None,
+           mode: str = "row", hkv: int | None = None) -> np.ndarray:
+    """Mask (B, Hq, NB, NB) uint8 from block scores and per-head ``tau`` (len Hq).
+
+    mode "row": the minimal set per query-block row ([XA-sum] Approach);
+    "global": per head over all rows at once ([Flex] R Q3), all rows required;
+    "gqa_union": "row", then the union over each KV group (``hkv`` heads).
+    """
     b_, hq, nb, _ = scores.shape
     tau = np.broadcast_to(np.asarray(tau, dtype=np.float64), (hq,))
+    some_heads = heads is not None
     heads = range(hq) if heads is None else heads
-    qblocks = range(nb) if qblocks is None else qblocks
     mask = np.zeros(scores.shape, dtype=np.uint8)
+    if mode == "global":
+        if qblocks is not None:
+            raise ValueError("global selection needs every query-block row")
+        for b in range(b_):
+            for h in heads:
+                mask[b, h] = select_global_head(scores[b, h], float(tau[h]), causal)
+        return mask
+    if mode not in ("row", "gqa_union"):
+        raise ValueError(f"unknown selection mode {mode!r}")
+    if mode == "gqa_union":
+        if hkv is None:
+            raise ValueError("gqa_union needs hkv")
+        if some_heads:
+            # the union needs every sibling of a selected head
+            g = hq // hkv
+            heads = sorted({hh for h in heads for hh in range((h // g) * g, (h // g + 1) * g)})
+    qblocks = range(nb) if qblocks is None else qblocks
     for b in range(b_):
         for h in heads:
             for big_i in qblocks:
                 mask[b, h, big_i] = select_row(scores[b, h, big_i], big_i, float(tau[h]), causal)
+    if mode == "gqa_union":
+        mask = gqa_union(mask, hkv)
     return mask
 
 
@@ -297,10 +363,13 @@ def dense(q, k, v, block: int, sm_scale: float, causal: bool, heads=None, qblock
 
 
 def prefill(q, k, v, block: int, stride: int, tau, score_scale: float, sm_scale: float,
-            causal: bool, heads=None, qblocks=None, pattern: str = "antidiagonal"):
+            causal: bool, heads=None, qblocks=None, pattern: str = "antidiagonal",
+            mode: str = "row"):
     """All three stages: (block_scores, mask, out, lse)."""
+    if mode == "gqa_union" and heads is not None:
+        raise ValueError("gqa_union prefill runs every head")
     sc = block_scores(q, k, block, stride, score_scale, causal, heads, qblocks, pattern)
-    mk = select(sc, tau, causal, heads, qblocks)
+    mk = select(sc, tau, causal, heads, qblocks, mode=mode, hkv=k.shape[1])
     out, lse = attend(q, k, v, mk, block, sm_scale, causal, heads, qblocks)
     return sc, mk, out, lse
 

@@ -3,7 +3,8 @@
 * brute force over the full attention matrix (antidiagonal tile sums);
 * a hand-worked example stored under tests/golden/;
 * the stride-1 closed form (textbook per-block attention mass via scipy softmax);
-* exhaustive subset enumeration for the minimal set;
+* exhaustive subset enumeration for the minimal set, per row and over a
+  whole head's flattened block matrix (global selection);
 * torch's scaled_dot_product_attention (CPU, float64) with an element mask;
 * invariants: non-negative scores, rows summing to 1, tau=1 keeps every
   candidate and equals dense attention, monotonicity in tau, diagonal kept.
@@ -202,6 +203,105 @@ def test_select_invariants():
     assert prev[..., lower].all()                                     # tau = 1: everything
     only_diag = oracle.select(sc, [0.0, 0.0], True).astype(bool)
     assert only_diag.sum() == 2 * nb
+
+
+def _candidates(nb, causal):
+    return [(i, j) for i in range(nb) for j in range(i + 1 if causal else nb)]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_global_selection_matches_exhaustive_search(causal):
+    # the kept set is the top-m* candidates in (score desc, (I, J) row-major)
+    # order, m* the smallest size any candidate subset needs to reach tau * T,
+    # found by enumerating subsets; then every diagonal block is added
+    rng = _rng(31 if causal else 32)
+    for trial in range(120):
+        nb = int(rng.integers(1, 5 if causal else 4))
+        sc = rng.dirichlet(np.full(nb, 0.6), size=nb)
+        if causal:
+            sc = np.tril(sc)
+            sc /= sc.sum(axis=1, keepdims=True)
+        if trial % 4 == 0:
+            sc = np.round(sc * 4) / 4                      # ties, zeros
+        tau = float(rng.choice([0.0, 0.3, 0.6, 0.8, 0.9, 0.97, 1.0]))
+        got = oracle.select_global_head(sc, tau, causal)
+        cands = _candidates(nb, causal)
+        vals = np.array([sc[i, j] for i, j in cands])
+        total = vals.sum()
+        if tau >= 1.0:
+            m_star = len(cands)
+        else:
+            m_star = None
+            for size in range(len(cands) + 1):
+                if any(vals[list(sub)].sum() >= tau * total
+                       for sub in itertools.combinations(range(len(cands)), size)):
+                    m_star = size
+                    break
+        order = sorted(range(len(cands)), key=lambda t: (-vals[t], t))
+        want = np.zeros((nb, nb), dtype=bool)
+        for t in order[:m_star]:
+            want[cands[t]] = True
+        want[np.arange(nb), np.arange(nb)] = True
+        np.testing.assert_array_equal(got, want, err_msg=f"{sc} tau={tau}")
+
+
+def test_global_selection_invariants():
+    rng = _rng(5)
+    q = rng.standard_normal((1, 1, 512, 16))
+    k = rng.standard_normal((1, 1, 512, 16))
+    sc = oracle.block_scores(q, k, 32, 4, 0.5, True)
+    nb = sc.shape[-1]
+    lower = np.tril(np.ones((nb, nb), dtype=bool))
+    prev = None
+    for tau in [0.0, 0.4, 0.8, 0.95, 1.0]:
+        mk = oracle.select(sc, [tau], True, mode="global").astype(bool)[0, 0]
+        assert mk[np.arange(nb), np.arange(nb)].all()
+        assert not mk[~lower].any()
+        # the kept mass reaches tau * T (T = NB: every row sums to 1)
+        assert sc[0, 0][mk].sum() >= tau * nb - 1e-12
+        if prev is not None:
+            assert (mk >= prev).all()
+        prev = mk
+    assert prev[lower].all()
+    # global differs from per-row selection on the same scores (mass moves
+    # between rows), yet keeps a comparable number of blocks
+    row = oracle.select(sc, [0.8], True).astype(bool)[0, 0]
+    glob = oracle.select(sc, [0.8], True, mode="global").astype(bool)[0, 0]
+    assert (row != glob).any()
+
+
+def test_gqa_union_groups_consecutive_heads():
+    # head h marks only block (h + 1, 0); with Hkv = 2 the groups are heads
+    # {0, 1, 2} and {3, 4, 5} (h // 3), not h % 2
+    b, hq, hkv, nb = 1, 6, 2, 8
+    mk = np.zeros((b, hq, nb, nb), dtype=np.uint8)
+    for h in range(hq):
+        mk[0, h, h + 1, 0] = 1
+    u = oracle.gqa_union(mk, hkv).astype(bool)
+    for h in range(hq):
+        group = range(3 * (h // 3), 3 * (h // 3) + 3)
+        want = np.zeros((nb, nb), dtype=bool)
+        for hh in group:
+            want[hh + 1, 0] = True
+        np.testing.assert_array_equal(u[0, h], want)
+
+
+def test_gqa_union_selection_contains_each_head():
+    rng = _rng(6)
+    q = rng.standard_normal((1, 4, 256, 16))
+    k = rng.standard_normal((1, 2, 256, 16))
+    sc = oracle.block_scores(q, k, 32, 4, 0.5, True)
+    tau = [0.5, 0.9, 0.7, 0.3]
+    row = oracle.select(sc, tau, True).astype(bool)
+    uni = oracle.select(sc, tau, True, mode="gqa_union", hkv=2).astype(bool)
+    assert (uni >= row).all()
+    assert (uni[0, 0] == uni[0, 1]).all() and (uni[0, 2] == uni[0, 3]).all()
+    assert (uni[0, 0] == (row[0, 0] | row[0, 1])).all()
+    # with one head per KV head the union is the per-row selection
+    k4 = rng.standard_normal((1, 4, 256, 16))
+    sc4 = oracle.block_scores(q, k4, 32, 4, 0.5, True)
+    np.testing.assert_array_equal(oracle.select(sc4, tau, True, mode="gqa_union", hkv=4),
+                                  oracle.select(sc4, tau, True))
 
 
 def test_tau_one_keeps_underflowed_blocks():
