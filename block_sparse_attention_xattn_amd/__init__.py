@@ -27,12 +27,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 XATTN_BF16 = 0
 XATTN_F32 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_HEADS = 256
 
 EXPORTS = (
     "xattn_abi_version", "xattn_status_string", "xattn_last_error",
-    "xattn_score_workspace_bytes", "xattn_attn_workspace_bytes",
+    "xattn_score_workspace_bytes", "xattn_select_workspace_bytes", "xattn_attn_workspace_bytes",
     "xattn_prefill_workspace_bytes", "xattn_score", "xattn_select", "bsa_fwd",
     "dense_fwd", "xattn_prefill",
 )
@@ -41,10 +41,16 @@ EXPORTS = (
 ANTIDIAGONAL = 0
 DIAGONAL = 1
 
+SELECT_ROW = 0
+SELECT_GLOBAL = 1
+SELECT_GQA_UNION = 2
+_SELECTIONS = {"row": SELECT_ROW, "global": SELECT_GLOBAL, "gqa_union": SELECT_GQA_UNION}
+
 
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("B", "Hq", "Hkv", "M", "C", "block", "stride", "causal", "dtype", "pattern")]
+                ("B", "Hq", "Hkv", "M", "C", "block", "stride", "causal", "dtype", "pattern", "selection",
+                 "Mk")]
 
 
 _P = ctypes.POINTER(Problem)
@@ -56,6 +62,8 @@ _lib.xattn_status_string.argtypes = [ctypes.c_int]
 _lib.xattn_last_error.restype = ctypes.c_char_p
 _lib.xattn_score_workspace_bytes.restype = ctypes.c_size_t
 _lib.xattn_score_workspace_bytes.argtypes = [_P]
+_lib.xattn_select_workspace_bytes.restype = ctypes.c_size_t
+_lib.xattn_select_workspace_bytes.argtypes = [_P]
 _lib.xattn_attn_workspace_bytes.restype = ctypes.c_size_t
 _lib.xattn_attn_workspace_bytes.argtypes = [_P]
 _lib.xattn_prefill_workspace_bytes.restype = ctypes.c_size_t
@@ -63,7 +71,7 @@ _lib.xattn_prefill_workspace_bytes.argtypes = [_P]
 _lib.xattn_score.restype = ctypes.c_int
 _lib.xattn_score.argtypes = [_P, _vp, _vp, _f, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.xattn_select.restype = ctypes.c_int
-_lib.xattn_select.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp]
+_lib.xattn_select.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.bsa_fwd.restype = ctypes.c_int
 _lib.bsa_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.dense_fwd.restype = ctypes.c_int
@@ -89,18 +97,25 @@ def _check(status: int):
         raise XAttnError(status)
 
 
-def problem(B, Hq, Hkv, M, C, block, stride, causal, dtype, pattern=ANTIDIAGONAL) -> Problem:
-    """C struct for the given sizes; dtype is torch.bfloat16/torch.float32 or 0/1."""
+def _selection(sel) -> int:
+    return _SELECTIONS[sel] if isinstance(sel, str) else int(sel)
+
+
+def problem(B, Hq, Hkv, M, C, block, stride, causal, dtype, pattern=ANTIDIAGONAL,
+            selection=SELECT_ROW) -> Problem:
+    """C struct for the given sizes; dtype is torch.bfloat16/torch.float32 or 0/1;
+    selection is an xattn_selection value or "row" / "global" / "gqa_union"."""
     if isinstance(dtype, torch.dtype):
         dtype = {torch.bfloat16: XATTN_BF16, torch.float32: XATTN_F32}.get(dtype, 99)
-    return Problem(B, Hq, Hkv, M, C, block, stride, int(bool(causal)), dtype, pattern)
+    return Problem(B, Hq, Hkv, M, C, block, stride, int(bool(causal)), dtype, pattern,
+                   _selection(selection), 0)
 
 
-def _problem_of(q, k, block, stride, causal, pattern=ANTIDIAGONAL) -> Problem:
+def _problem_of(q, k, block, stride, causal, pattern=ANTIDIAGONAL, selection=SELECT_ROW) -> Problem:
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be 4-D (B, H, M, C)")
     B, Hq, M, C = q.shape
-    return problem(B, Hq, k.shape[1], M, C, block, stride, causal, q.dtype, pattern)
+    return problem(B, Hq, k.shape[1], M, C, block, stride, causal, q.dtype, pattern, selection)
 
 
 def _ptr(t):
@@ -124,6 +139,11 @@ def _same(q, *ts):
 def workspace_bytes(p: Problem) -> int:
     """Workspace bytes of xattn_score."""
     return int(_lib.xattn_score_workspace_bytes(ctypes.byref(p)))
+
+
+def select_workspace_bytes(p: Problem) -> int:
+    """Workspace bytes of xattn_select."""
+    return int(_lib.xattn_select_workspace_bytes(ctypes.byref(p)))
 
 
 def attn_workspace_bytes(p: Problem) -> int:
@@ -162,10 +182,10 @@ def _tau_host(tau, hq):
 
 
 def xattn_select(block_scores, tau, block, stride, causal=True, Hkv=None, C=128, dtype=torch.bfloat16,
-                 want_mask=True, mask=None, kv_idx=None, kv_cnt=None):
+                 want_mask=True, mask=None, kv_idx=None, kv_cnt=None, selection=SELECT_ROW):
     """(mask u8 or None, kv_idx int32, kv_cnt int32) for block scores (B, Hq, NB, NB)."""
     B, Hq, nb, _ = block_scores.shape
-    p = problem(B, Hq, Hkv or Hq, nb * block, C, block, stride, causal, dtype)
+    p = problem(B, Hq, Hkv or Hq, nb * block, C, block, stride, causal, dtype, selection=selection)
     dev = block_scores.device
     if mask is None and want_mask:
         mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev)
@@ -174,15 +194,19 @@ def xattn_select(block_scores, tau, block, stride, causal=True, Hkv=None, C=128,
     if kv_cnt is None:
         kv_cnt = torch.empty((B, Hq, nb), dtype=torch.int32, device=dev)
     tau_h = _tau_host(tau, Hq)
+    need = select_workspace_bytes(p)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     _check(_lib.xattn_select(ctypes.byref(p), _ptr(block_scores), tau_h.data_ptr(), _ptr(mask),
-                             _ptr(kv_idx), _ptr(kv_cnt), _stream(dev)))
+                             _ptr(kv_idx), _ptr(kv_cnt), _ptr(ws), need, _stream(dev)))
     return mask, kv_idx, kv_cnt
 
 
-def bsa_fwd(q, k, v, kv_idx, kv_cnt, block, sm_scale, causal=True, out=None, want_lse=False, ws=None):
-    """Block-sparse attention: (out, lse or None)."""
+def bsa_fwd(q, k, v, kv_idx, kv_cnt, block, sm_scale, causal=True, out=None, want_lse=False, ws=None,
+            selection=SELECT_ROW):
+    """Block-sparse attention: (out, lse or None). selection=SELECT_GQA_UNION
+    declares lists shared by sibling heads (any lists stay correct)."""
     _same(q, k, v)
-    p = _problem_of(q, k, block, 0, causal)
+    p = _problem_of(q, k, block, 0, causal, selection=selection)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
     if ws is None:
@@ -208,8 +232,8 @@ class PrefillBuffers:
     """Reusable device buffers for xattn_prefill (allocated once per shape)."""
 
     def __init__(self, q, k, block, stride, causal=True, want_mask=True, want_lse=False,
-                 pattern=ANTIDIAGONAL):
-        p = _problem_of(q, k, block, stride, causal, pattern)
+                 pattern=ANTIDIAGONAL, selection=SELECT_ROW):
+        p = _problem_of(q, k, block, stride, causal, pattern, selection)
         B, Hq, M, C = q.shape
         nb = M // block
         dev = q.device
@@ -224,10 +248,10 @@ class PrefillBuffers:
 
 
 def xattn_prefill(q, k, v, tau, block, stride, score_scale, sm_scale, causal=True, buffers=None,
-                  pattern=ANTIDIAGONAL):
+                  pattern=ANTIDIAGONAL, selection=SELECT_ROW):
     """All three stages in one call. Returns the PrefillBuffers holding the results."""
     _same(q, k, v)
-    bufs = buffers or PrefillBuffers(q, k, block, stride, causal, pattern=pattern)
+    bufs = buffers or PrefillBuffers(q, k, block, stride, causal, pattern=pattern, selection=selection)
     tau_h = _tau_host(tau, q.shape[1])
     b = bufs
     _check(_lib.xattn_prefill(ctypes.byref(b.problem), _ptr(q), _ptr(k), _ptr(v), tau_h.data_ptr(),

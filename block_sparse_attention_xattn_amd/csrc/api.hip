@@ -35,6 +35,11 @@ xattn_status check_problem(const xattn_problem* p, bool need_stride = true) {
   if (p->causal != 0 && p->causal != 1) return fail(XATTN_ERR_ARG, "causal must be 0 or 1");
   if (p->pattern != XATTN_ANTIDIAGONAL && p->pattern != XATTN_DIAGONAL)
     return fail(XATTN_ERR_ARG, "pattern %d is neither antidiagonal nor diagonal", p->pattern);
+  if (p->selection != XATTN_SELECT_ROW && p->selection != XATTN_SELECT_GLOBAL &&
+      p->selection != XATTN_SELECT_GQA_UNION)
+    return fail(XATTN_ERR_ARG, "selection %d is not an xattn_selection", p->selection);
+  if (p->Mk != 0 && p->Mk != p->M)
+    return fail(XATTN_ERR_UNSUPPORTED, "Mk=%d differs from M=%d", p->Mk, p->M);
   if (p->Hq % p->Hkv) return fail(XATTN_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
   if (p->Hq > XATTN_MAX_HEADS) return fail(XATTN_ERR_UNSUPPORTED, "Hq=%d exceeds %d", p->Hq, XATTN_MAX_HEADS);
   if (p->M % p->block) return fail(XATTN_ERR_SHAPE, "M=%d is not a multiple of block=%d", p->M, p->block);
@@ -54,7 +59,8 @@ xattn_status check_problem(const xattn_problem* p, bool need_stride = true) {
 }
 
 xattn::Shape shape_of(const xattn_problem* p) {
-  return xattn::Shape{p->B, p->Hq, p->Hkv, p->M, p->C, p->block, p->stride, p->causal, p->pattern};
+  return xattn::Shape{p->B,      p->Hq,     p->Hkv,    p->M,      p->C,
+                      p->block,  p->stride, p->causal, p->pattern, p->selection};
 }
 
 xattn_status check_scale(float x, const char* name) {
@@ -124,14 +130,39 @@ xattn_status do_attn(const xattn_problem* p, const void* q, const void* k, const
   return hip_status(e, "attention launch");
 }
 
-// The attention queue sits after the score partials in xattn_prefill's
-// workspace, 256-byte aligned.
-size_t queue_offset(size_t score_bytes) { return (score_bytes + 255) & ~(size_t)255; }
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 xattn_status check_workspace(const void* ws, size_t ws_bytes, size_t need) {
   if (!ws || ws_bytes < need)
     return fail(XATTN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
   return XATTN_OK;
+}
+
+xattn_status do_select(const xattn_problem* p, const float* block_scores, const xattn::TauArray& t,
+                       uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, void* ws, hipStream_t st) {
+  const xattn::Shape s = shape_of(p);
+  if (p->selection == XATTN_SELECT_GLOBAL)
+    return hip_status(xattn::launch_select_global(s, block_scores, t, mask, kv_idx, kv_cnt, ws, st),
+                      "global select launch");
+  xattn_status r = hip_status(xattn::launch_select(s, block_scores, t, mask, kv_idx, kv_cnt, st), "select launch");
+  if (r == XATTN_OK && p->selection == XATTN_SELECT_GQA_UNION)
+    r = hip_status(xattn::launch_gqa_union(s, mask, kv_idx, kv_cnt, st), "GQA union launch");
+  return r;
+}
+
+// xattn_prefill's workspace: score partials | select scratch | attention queues,
+// each part starting on a 256-byte boundary.
+struct PrefillLayout {
+  size_t select_off, queue_off, total;
+};
+PrefillLayout prefill_layout(const xattn_problem* p) {
+  const size_t score = xattn_score_workspace_bytes(p);
+  const size_t sel = xattn::select_workspace_bytes(shape_of(p), p->selection);
+  PrefillLayout l;
+  l.select_off = align256(score);
+  l.queue_off = align256(l.select_off + sel);
+  l.total = l.queue_off + xattn_attn_workspace_bytes(p);
+  return l;
 }
 
 }  // namespace
@@ -167,9 +198,8 @@ size_t xattn_attn_workspace_bytes(const xattn_problem* p) {
 }
 
 size_t xattn_prefill_workspace_bytes(const xattn_problem* p) {
-  const size_t score = xattn_score_workspace_bytes(p);
-  if (score == 0) return 0;
-  return queue_offset(score) + xattn_attn_workspace_bytes(p);
+  if (check_problem(p) != XATTN_OK) return 0;
+  return prefill_layout(p).total;
 }
 
 xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k, float score_scale,
@@ -182,17 +212,23 @@ xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k, f
   return do_score(p, q, k, score_scale, block_scores, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
+size_t xattn_select_workspace_bytes(const xattn_problem* p) {
+  if (check_problem(p) != XATTN_OK) return 0;
+  return xattn::select_workspace_bytes(shape_of(p), p->selection);
+}
+
 xattn_status xattn_select(const xattn_problem* p, const float* block_scores, const float* tau,
-                          uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, void* stream) {
+                          uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, void* ws, size_t ws_bytes,
+                          void* stream) {
   xattn_status s = check_problem(p);
   if (s != XATTN_OK) return s;
   if (!block_scores || !kv_idx || !kv_cnt)
     return fail(XATTN_ERR_NULL, "block_scores, kv_idx and kv_cnt must be non-NULL");
   xattn::TauArray t;
   if ((s = check_tau(p, tau, &t)) != XATTN_OK) return s;
-  return hip_status(xattn::launch_select(shape_of(p), block_scores, t, mask, kv_idx, kv_cnt,
-                                         static_cast<hipStream_t>(stream)),
-                    "select launch");
+  const size_t need = xattn_select_workspace_bytes(p);
+  if (need && (s = check_workspace(ws, ws_bytes, need)) != XATTN_OK) return s;
+  return do_select(p, block_scores, t, mask, kv_idx, kv_cnt, ws, static_cast<hipStream_t>(stream));
 }
 
 xattn_status bsa_fwd(const xattn_problem* p, const void* q, const void* k, const void* v,
@@ -231,14 +267,30 @@ xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
   if ((s = check_tau(p, tau, &t)) != XATTN_OK) return s;
   if ((s = check_workspace(ws, ws_bytes, xattn_prefill_workspace_bytes(p))) != XATTN_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // partials, then normalisation and selection fused in one launch
+  const PrefillLayout lay = prefill_layout(p);
+  char* wsb = static_cast<char*>(ws);
+  const xattn::Shape sh = shape_of(p);
   if ((s = do_partials(p, q, k, score_scale, ws, st)) != XATTN_OK) return s;
-  if ((s = hip_status(xattn::launch_score_select(shape_of(p), static_cast<const float*>(ws), block_scores,
-                                                 t, mask, kv_idx, kv_cnt, st),
-                      "score+select launch")) != XATTN_OK)
-    return s;
-  void* queue = static_cast<char*>(ws) + queue_offset(xattn_score_workspace_bytes(p));
-  return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, queue, st);
+  if (p->selection == XATTN_SELECT_GLOBAL) {
+    // the head's whole block matrix is needed first
+    if ((s = hip_status(xattn::launch_score_finalize(sh, static_cast<const float*>(ws), block_scores, st),
+                        "score finalize launch")) != XATTN_OK)
+      return s;
+    if ((s = hip_status(xattn::launch_select_global(sh, block_scores, t, mask, kv_idx, kv_cnt,
+                                                    wsb + lay.select_off, st),
+                        "global select launch")) != XATTN_OK)
+      return s;
+  } else {
+    // normalisation and per-row selection fused in one launch
+    if ((s = hip_status(xattn::launch_score_select(sh, static_cast<const float*>(ws), block_scores, t, mask,
+                                                   kv_idx, kv_cnt, st),
+                        "score+select launch")) != XATTN_OK)
+      return s;
+    if (p->selection == XATTN_SELECT_GQA_UNION &&
+        (s = hip_status(xattn::launch_gqa_union(sh, mask, kv_idx, kv_cnt, st), "GQA union launch")) != XATTN_OK)
+      return s;
+  }
+  return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, wsb + lay.queue_off, st);
 }
 
 }  // extern "C"

@@ -772,15 +772,20 @@ static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t
   return hipGetLastError();
 }
 
-// 128-row blocks use the 8-wave modes: dense pairs GQA siblings (identical
-// block lists) when the group size is even, sparse pairs neighbouring rows of
-// one head (sibling heads keep very different numbers of blocks, so a sibling
-// pair would leave one half idle). 64-row blocks use one (head, row) per
-// workgroup.
+// 128-row blocks: dense attention pairs GQA siblings (identical block lists)
+// when the group size is even, and so does sparse attention over GQA-union
+// lists. Other sparse lists run one (head, row) per workgroup: sibling heads
+// keep very different numbers of blocks, so a sibling pair would leave one
+// half idle (pairing neighbouring rows of a head is available behind
+// XATTN_SPARSE_PAIR_ROWS). 64-row blocks use one (head, row) per workgroup.
 template <int C, int BLK>
 static hipError_t launch_bf16_cb(const Shape& s, const AttnArgs& a, hipStream_t st) {
   if (BLK == 128) {
-    if (a.kv_idx == nullptr && (s.Hq / s.Hkv) % 2 == 0) return launch_bf16_cbm<C, BLK, MODE_SIBLINGS>(s, a, st);
+    const bool pairs = (s.Hq / s.Hkv) % 2 == 0;
+    if (a.kv_idx == nullptr && pairs) return launch_bf16_cbm<C, BLK, MODE_SIBLINGS>(s, a, st);
+    // GQA-union lists are shared by the siblings: one tile load serves both
+    if (a.kv_idx != nullptr && pairs && s.selection == SEL_GQA_UNION)
+      return launch_bf16_cbm<C, BLK, MODE_SIBLINGS>(s, a, st);
     if (a.kv_idx != nullptr && XATTN_SPARSE_PAIR_ROWS) return launch_bf16_cbm<C, BLK, MODE_ROWS>(s, a, st);
   }
   return launch_bf16_cbm<C, BLK, MODE_SINGLE>(s, a, st);

@@ -12,6 +12,7 @@ namespace xattn {
 struct Shape {
   int B, Hq, Hkv, M, C, block, stride, causal;
   int diagonal;  // 1: scoring pairs q[iS+s] with k[jS+s] instead of k[jS+S-1-s]
+  int selection; // SEL_ROW, SEL_GLOBAL or SEL_GQA_UNION
   int NB() const { return M / block; }
   int R() const { return M / stride; }
   int r() const { return block / stride; }
@@ -34,6 +35,19 @@ struct TauArray {
 };
 hipError_t launch_select(const Shape& s, const float* block_scores, const TauArray& tau,
                          uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st);
+
+// Selection variants (xattn_selection): per-row minimal sets, one minimal set
+// per head over the flattened block matrix, or per-row sets united over each
+// KV group.
+enum { SEL_ROW = 0, SEL_GLOBAL = 1, SEL_GQA_UNION = 2 };
+// Device scratch of a selection in `mode` (0 unless global).
+size_t select_workspace_bytes(const Shape& s, int mode);
+hipError_t launch_select_global(const Shape& s, const float* block_scores, const TauArray& tau,
+                                uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, void* ws,
+                                hipStream_t st);
+// Rewrites the per-row lists of every KV group's heads with their union.
+hipError_t launch_gqa_union(const Shape& s, uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt,
+                            hipStream_t st);
 
 // Stages 2+3 fused (one launch per layer in xattn_prefill): block scores from
 // the partials, written out, then selected without re-reading them.

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define XATTN_ABI_VERSION 2
+#define XATTN_ABI_VERSION 3
 #define XATTN_MAX_HEADS 256
 #define XATTN_MAX_BLOCKS 4096
 
@@ -85,6 +85,8 @@ typedef struct {
   int32_t causal; /* 1: key j visible to query i iff j <= i; 0: all keys */
   int32_t dtype;  /* xattn_dtype of Q, K, V and O */
   int32_t pattern; /* xattn_pattern of the strided scoring (0 = antidiagonal) */
+  int32_t selection; /* xattn_selection of the block selection (0 = per row) */
+  int32_t Mk;     /* key length; 0 or M (the only value supported) */
 } xattn_problem;
 
 /* Which line of each stride x stride tile the scoring sums:
@@ -92,6 +94,21 @@ typedef struct {
  *  DIAGONAL (the older variant compared in [DuSA] Response to Q2 and in the
  *  [XA-sum] ablation table): query row i*S+s with key row j*S+s. */
 typedef enum { XATTN_ANTIDIAGONAL = 0, XATTN_DIAGONAL = 1 } xattn_pattern;
+
+/* How xattn_select (and xattn_prefill) choose blocks:
+ *  ROW (the method, [XA-sum] Approach): a minimal set per query-block row;
+ *  GLOBAL ([Flex] R Q3, global index selection over the flattened block
+ *  matrix): one minimal set per head over every candidate (I, J) at once,
+ *  ordered by score descending, ties by (I, J) row-major, against tau_h times
+ *  the head's candidate mass; then every diagonal block is added;
+ *  GQA_UNION (a reuse variant, not from the pages): ROW, then every head of a
+ *  KV group keeps the union of the group's rows. bsa_fwd then serves two
+ *  sibling heads per workgroup from one K/V tile. */
+typedef enum {
+  XATTN_SELECT_ROW = 0,
+  XATTN_SELECT_GLOBAL = 1,
+  XATTN_SELECT_GQA_UNION = 2
+} xattn_selection;
 
 /* ABI version of the loaded library (XATTN_ABI_VERSION). */
 int32_t xattn_abi_version(void);
@@ -128,6 +145,10 @@ xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k,
                          float score_scale, float* block_scores, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* Device workspace bytes xattn_select needs: 0 for ROW and GQA_UNION; for
+ * GLOBAL, per head a 64-byte state, a 48 KiB mass histogram and NB words. */
+size_t xattn_select_workspace_bytes(const xattn_problem* p);
+
 /*
  * Stage 3 — minimal-set threshold selection ([XA-sum] Approach: the minimal
  * set of blocks whose normalised mass exceeds the per-head threshold;
@@ -137,6 +158,9 @@ xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k,
  * by score descending, ties by J ascending; with prefix masses c_k (float64)
  * and total T = c_n, the kept set is the first k* = min{k >= 0 : c_k >= tau_h*T}
  * candidates (tau_h >= 1 keeps all). The diagonal block J = I is then added.
+ * p->selection picks the GLOBAL or GQA_UNION variant instead (see
+ * xattn_selection); GLOBAL sums fixed-point masses (score * 2^50, exact and
+ * order-independent) instead of float64 prefixes.
  *
  *  block_scores  device float32 (B, Hq, NB, NB), as written by xattn_score.
  *  tau           HOST array of Hq floats, each in [0, 1] (copied at the call).
@@ -144,10 +168,12 @@ xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k,
  *  kv_idx        device int32 (B, Hq, NB, NB): per row the kept J in ascending
  *                order; only the first kv_cnt entries of a row are written.
  *  kv_cnt        device int32 (B, Hq, NB): kept blocks per row (>= 1).
+ *  ws, ws_bytes  device scratch of xattn_select_workspace_bytes(p) (may be
+ *                NULL when that is 0).
  */
 xattn_status xattn_select(const xattn_problem* p, const float* block_scores,
                           const float* tau, uint8_t* mask, int32_t* kv_idx,
-                          int32_t* kv_cnt, void* stream);
+                          int32_t* kv_cnt, void* ws, size_t ws_bytes, void* stream);
 
 /* Device workspace bytes bsa_fwd needs (a fixed 1 KiB of per-XCD work-queue
  * counters); 0 if p is invalid. */
@@ -185,8 +211,9 @@ xattn_status dense_fwd(const xattn_problem* p, const void* q, const void* k,
                        const void* v, float sm_scale, void* out, float* lse,
                        void* stream);
 
-/* Device workspace bytes xattn_prefill needs: the score partials, then (at
- * the next 256-byte boundary) the attention queues; 0 if p is invalid. */
+/* Device workspace bytes xattn_prefill needs: the score partials, the
+ * selection scratch and the attention queues, each part starting on a
+ * 256-byte boundary; 0 if p is invalid. */
 size_t xattn_prefill_workspace_bytes(const xattn_problem* p);
 
 /*

@@ -249,7 +249,7 @@ def gqa_union(mask: np.ndarray, hkv: int) -> np.ndarray:
     b_, hq, nb, _ = mask.shape
     g = hq // hkv
     out = mask.astype(bool).reshape(b_, hkv, g, nb, nb).any(axis=2, keepdims=True)
-    return np.broadcast_to(out, (b_, hkv, g, nb, nb)).reshape(mask.shape).astype(np.uint8)
+    return np.ascontiguousarray(np.broadcast_to(out, (b_, hkv, g, nb, nb)).reshape(mask.shape), dtype=np.uint8)
 
 
 def select(scores: np.ndarray, tau, causal: bool, heads=None, qblocks=None,
@@ -294,7 +294,7 @@ def select(scores: np.ndarray, tau, causal: bool, heads=None, qblocks=None,
 def mask_to_index(mask: np.ndarray):
     """Ascending per-row block lists: kv_idx (.., NB) int32 padded with -1, kv_cnt int32."""
     nb = mask.shape[-1]
-    cnt = mask.astype(bool).sum(axis=-1).astype(np.int32)
+    cnt = np.ascontiguousarray(mask.astype(bool).sum(axis=-1), dtype=np.int32)
     idx = np.full(mask.shape, -1, dtype=np.int32)
     flat_m = mask.reshape(-1, nb).astype(bool)
     flat_i = idx.reshape(-1, nb)

@@ -33,17 +33,18 @@ def test_every_declared_symbol_is_exported(xa):
 
 
 def test_version_and_strings(xa):
-    assert xa._lib.xattn_abi_version() == 2
+    assert xa._lib.xattn_abi_version() == 3
     for s in range(8):
         assert xa._lib.xattn_status_string(s)
     assert xa._lib.xattn_status_string(99) == b"unknown status"
 
 
 def _p(xa, **kw):
-    base = dict(B=1, Hq=4, Hkv=2, M=1024, C=128, block=128, stride=8, causal=1, dtype=0, pattern=0)
+    base = dict(B=1, Hq=4, Hkv=2, M=1024, C=128, block=128, stride=8, causal=1, dtype=0, pattern=0,
+                selection=0, Mk=0)
     base.update(kw)
     return xa.Problem(*[base[k] for k in ("B", "Hq", "Hkv", "M", "C", "block", "stride", "causal", "dtype",
-                                          "pattern")])
+                                          "pattern", "selection", "Mk")])
 
 
 FAKE = 0x1000  # never dereferenced: validation fails first
@@ -54,6 +55,7 @@ FAKE = 0x1000  # never dereferenced: validation fails first
     (dict(block=32, stride=4), 5), (dict(stride=128), 5), (dict(stride=1), 5),
     (dict(dtype=7), 3), (dict(causal=2), 4), (dict(Hq=512, Hkv=1), 5), (dict(B=0), 2),
     (dict(M=4096 * 128 * 2), 5), (dict(pattern=2), 4), (dict(pattern=-1), 4),
+    (dict(selection=3), 4), (dict(selection=-1), 4), (dict(Mk=2048), 5),
 ])
 def test_score_rejects_bad_problems(xa, kw, status):
     p = _p(xa, **kw)
@@ -76,6 +78,14 @@ def test_workspace_bytes(xa):
     assert xa.workspace_bytes(odd) == 72
     assert xa.prefill_workspace_bytes(odd) == 256 + 1024
     assert xa.prefill_workspace_bytes(_p(xa, stride=0)) == 0
+    # selection scratch: none per row or for the GQA union; per head a 64-byte
+    # state, a 4096-bucket histogram (8 + 4 bytes each) and NB words for global
+    assert xa.select_workspace_bytes(p) == 0
+    assert xa.select_workspace_bytes(_p(xa, selection=2)) == 0
+    g = _p(xa, selection=1)
+    assert xa.select_workspace_bytes(g) == 4 * (64 + 4096 * 12 + 4 * 8)
+    sel_end = 16384 + 4 * (64 + 4096 * 12 + 4 * 8)
+    assert xa.prefill_workspace_bytes(g) == (sel_end + 255) // 256 * 256 + 1024
 
 
 def test_null_and_workspace_errors(xa):
@@ -100,10 +110,15 @@ def test_select_rejects_bad_tau(xa):
     L = xa._lib
     for bad in ([0.9, 0.9, 1.5, 0.9], [0.9, -0.1, 0.9, 0.9], [0.9, 0.9, 0.9, float("nan")]):
         arr = (ctypes.c_float * 4)(*bad)
-        assert L.xattn_select(ctypes.byref(p), FAKE, arr, None, FAKE, FAKE, None) == 4
+        assert L.xattn_select(ctypes.byref(p), FAKE, arr, None, FAKE, FAKE, None, 0, None) == 4
     arr = (ctypes.c_float * 4)(0.9, 0.9, 0.9, 0.9)
-    assert L.xattn_select(ctypes.byref(p), FAKE, None, None, FAKE, FAKE, None) == 1
-    assert L.xattn_select(ctypes.byref(p), None, arr, None, FAKE, FAKE, None) == 1
+    assert L.xattn_select(ctypes.byref(p), FAKE, None, None, FAKE, FAKE, None, 0, None) == 1
+    assert L.xattn_select(ctypes.byref(p), None, arr, None, FAKE, FAKE, None, 0, None) == 1
+    # global selection needs its scratch
+    g = _p(xa, selection=1)
+    need = xa.select_workspace_bytes(g)
+    assert L.xattn_select(ctypes.byref(g), FAKE, arr, None, FAKE, FAKE, None, 0, None) == 6
+    assert L.xattn_select(ctypes.byref(g), FAKE, arr, None, FAKE, FAKE, FAKE, need - 1, None) == 6
     assert L.xattn_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, arr, 0.01, 0.1, FAKE, None, FAKE, FAKE,
                            FAKE, 16, FAKE, None, None) == 6
     # the score partials alone are too little: the attention queues follow them
