@@ -232,6 +232,41 @@ def cpu_baseline(wl, torch, res, budget_s):
     }
 
 
+def run_variants(xa, torch, head, steps):
+    """The headline layer through xattn_prefill with each method variant:
+    global and GQA-union selection, and the diagonal scoring pattern."""
+    w = head["workload"]
+    q, k, v, tau = head["_tensors"][:4]
+    sscale, smscale = 1.0 / (w.stride * math.sqrt(w.C)), 1.0 / math.sqrt(w.C)
+    cand = w.B * w.Hq * (w.nb * (w.nb + 1) // 2 if w.causal else w.nb * w.nb)
+    res = {}
+    for label, kw in (("select_global", dict(selection="global")),
+                      ("select_gqa_union", dict(selection="gqa_union")),
+                      ("pattern_diagonal", dict(pattern=xa.DIAGONAL))):
+        bufs = xa.PrefillBuffers(q, k, w.block, w.stride, w.causal, want_mask=False, **kw)
+
+        def step():
+            xa.xattn_prefill(q, k, v, tau, w.block, w.stride, sscale, smscale, w.causal, buffers=bufs)
+
+        step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        dens = float(bufs.kv_cnt.sum().item()) / cand
+        res[label] = {"ms": round(ms, 4), "density": round(dens, 5),
+                      "dense_equiv_tflops": round(w.dense_flops / ms / 1e9, 2)}
+        log(f"[{w.name}] variant {label}: {ms:.3f} ms, density {dens * 100:.2f}%")
+        del bufs
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -243,6 +278,8 @@ def main():
     ap.add_argument("--dense-steps", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip timing the selection and scoring variants on the headline layer")
     a = ap.parse_args()
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -284,6 +321,8 @@ def main():
                 "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS}
     roof["traffic"] = traffic_from_profile("bsa_fwd" if dom == "bsa_fwd" else "xattn_score", w.name)
 
+    variants = None if a.no_variants else run_variants(xa, torch, head, max(2, a.steps // 3))
+
     cpu = None
     if not a.no_cpu_baseline:
         log("[cpu] timing the oracle on a bounded sample ...")
@@ -322,6 +361,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "by_length": {n: summary(r) for n, r in results.items()},
+        "variants": variants,
         "kernel_source_sha": kernel_source_sha(),
     }
     print(json.dumps(line))
