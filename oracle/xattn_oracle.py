@@ -23,9 +23,13 @@ Sources (page title, section):
             sections "R Q3" (minimal |S| under a cumulative-mass constraint;
             global, flattened index selection versus query-wise selection).
 
-Notation: Q is (B, Hq, M, C); K, V are (B, Hkv, M, C); query head h reads KV
-head h // (Hq // Hkv). Block size Bk, stride S, r = Bk // S strided rows per
-block, NB = M // Bk blocks, R = M // S strided rows.
+Notation: Q is (B, Hq, Mq, C); K, V are (B, Hkv, Mk, C) with Mk >= Mq; query
+head h reads KV head h // (Hq // Hkv). Query i sits at absolute position
+off + i, off = Mk - Mq (chunked prefill: the queries are the last Mq tokens;
+off = 0 is the plain prefill), and off must be a multiple of the block size.
+Block size Bk, stride S, r = Bk // S strided rows per block,
+NBq = ceil(Mq / Bk) query blocks, NBk = ceil(Mk / Bk) key blocks; query block I
+is key block I + off // Bk. Lengths need not be multiples of S or Bk.
 
 Readings taken where the pages are silent (each one is listed in the design doc):
   * score temperature: the caller passes ``score_scale`` explicitly;
@@ -37,7 +41,12 @@ Readings taken where the pages are silent (each one is listed in the design doc):
   * tau >= 1 keeps every candidate; the diagonal block is always added after
     the threshold cut;
   * sparse attention is exact softmax attention renormalised over the
-    selected keys only.
+    selected keys only;
+  * ragged lengths ([DuSA] rebuttal, "Response to Q1": padding makes the
+    sequence length divisible by the block size): the missing tokens of a
+    partial stride group are zero vectors; strided key rows and keys past the
+    end take no part in any softmax; a partial last query block's scores are
+    divided by its count of real strided rows, so its row still sums to 1.
 
 Pins: every function here is checked in tests/test_oracle_pins.py against
 something other than itself (brute force, closed forms, library routines).
@@ -87,32 +96,48 @@ def _kv_head(h: int, hq: int, hkv: int) -> int:
 # the reshape turns the reshape-matmul into exactly that antidiagonal sum.
 # ---------------------------------------------------------------------------
 
+def _pad_rows(x: np.ndarray, mult: int) -> np.ndarray:
+    """x (m, c) in float64 with zero rows appended up to a multiple of ``mult``."""
+    x = _f64(x)
+    m, c = x.shape
+    extra = (-m) % mult
+    if extra:
+        x = np.concatenate([x, np.zeros((extra, c))], axis=0)
+    return x
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
 def strided_query_rows(qh: np.ndarray, stride: int) -> np.ndarray:
-    """Q' (R, S*C): row i concatenates q[i*S], ..., q[i*S+S-1]."""
-    m, c = qh.shape
-    if m % stride:
-        raise ValueError("M must be a multiple of the stride")
-    return _f64(qh).reshape(m // stride, stride * c)
+    """Q' (R, S*C): row i concatenates q[i*S], ..., q[i*S+S-1] (zero past the end)."""
+    x = _pad_rows(qh, stride)
+    return x.reshape(x.shape[0] // stride, stride * x.shape[1])
 
 
 def reversed_key_rows(kh: np.ndarray, stride: int) -> np.ndarray:
-    """K~' (R, S*C): row j concatenates k[j*S+S-1], ..., k[j*S]."""
-    m, c = kh.shape
-    if m % stride:
-        raise ValueError("M must be a multiple of the stride")
-    return _f64(kh).reshape(m // stride, stride, c)[:, ::-1, :].reshape(m // stride, stride * c)
+    """K~' (R, S*C): row j concatenates k[j*S+S-1], ..., k[j*S] (zero past the end)."""
+    x = _pad_rows(kh, stride)
+    r = x.shape[0] // stride
+    return x.reshape(r, stride, x.shape[1])[:, ::-1, :].reshape(r, stride * x.shape[1])
 
 
 def strided_logits(qh, kh, stride: int, score_scale: float, causal: bool,
                    rows: slice | None = None, pattern: str = "antidiagonal") -> np.ndarray:
-    """Scaled strided logits for strided query ``rows`` vs all keys.
+    """Scaled strided logits for strided query ``rows`` vs all strided keys.
 
     ``pattern="antidiagonal"`` (the method) reverses K inside each stride group;
     ``pattern="diagonal"`` (the older variant the DuSA rebuttal, Response to Q2,
     describes: plain (M/stride, stride*C) reshapes of Q and K) does not, which
     sums the main diagonal of each stride x stride tile instead.
-    Entries with key j > query i are -inf when ``causal`` (strided level).
+    With queries the last Mq of Mk tokens, strided query row i is absolute
+    strided row i + (Mk - Mq) / S. Entries with key j > that row are -inf when
+    ``causal`` (strided level).
     """
+    off = kh.shape[0] - qh.shape[0]
+    if off < 0 or off % stride:
+        raise ValueError("Mk - Mq must be a non-negative multiple of the stride")
     qs = strided_query_rows(qh, stride)
     if pattern == "antidiagonal":
         ks = reversed_key_rows(kh, stride)
@@ -126,7 +151,7 @@ def strided_logits(qh, kh, stride: int, score_scale: float, causal: bool,
     a = qs[rows] @ ks.T
     a *= score_scale
     if causal:
-        i = np.arange(lo, lo + a.shape[0])[:, None]
+        i = np.arange(lo, lo + a.shape[0])[:, None] + off // stride
         j = np.arange(ks.shape[0])[None, :]
         a[j > i] = -np.inf
     return a
@@ -142,32 +167,37 @@ def strided_logits(qh, kh, stride: int, score_scale: float, causal: bool,
 
 def block_score_row(qh, kh, big_i: int, block: int, stride: int,
                     score_scale: float, causal: bool, pattern: str = "antidiagonal") -> np.ndarray:
-    """Block scores S^[I, :] (length NB) for query block ``big_i`` of one head."""
+    """Block scores S^[I, :] (length NBk) for query block ``big_i`` of one head."""
     if block % stride:
         raise ValueError("block must be a multiple of the stride")
-    m = qh.shape[0]
+    mq, mk = qh.shape[0], kh.shape[0]
+    if (mk - mq) % block:
+        raise ValueError("Mk - Mq must be a multiple of the block size")
     r = block // stride
-    nb = m // block
-    logits = strided_logits(qh, kh, stride, score_scale, causal,
-                            rows=slice(big_i * r, (big_i + 1) * r), pattern=pattern)
+    nbk = _cdiv(mk, block)
+    rq = _cdiv(mq, stride)
+    rows = slice(big_i * r, min((big_i + 1) * r, rq))   # the block's real strided rows
+    logits = strided_logits(qh, kh, stride, score_scale, causal, rows=rows, pattern=pattern)
+    n_rows = logits.shape[0]
     # row softmax over keys
     mx = logits.max(axis=1, keepdims=True)
     p = np.exp(logits - mx)
     p /= p.sum(axis=1, keepdims=True)
-    # sum each (r x r) tile: columns grouped into NB blocks of r strided keys
-    per_block = p.reshape(r, nb, r).sum(axis=2).sum(axis=0)
-    return per_block / r
+    # sum each tile: strided key j belongs to key block j // r
+    p = np.concatenate([p, np.zeros((n_rows, nbk * r - p.shape[1]))], axis=1)
+    per_block = p.reshape(n_rows, nbk, r).sum(axis=2).sum(axis=0)
+    return per_block / n_rows
 
 
 def block_scores(q, k, block: int, stride: int, score_scale: float, causal: bool,
                  heads=None, qblocks=None, pattern: str = "antidiagonal") -> np.ndarray:
-    """Block scores (B, Hq, NB, NB), float64. Rows not in ``qblocks`` stay 0."""
-    b_, hq, m, _ = q.shape
-    hkv = k.shape[1]
-    nb = m // block
+    """Block scores (B, Hq, NBq, NBk), float64. Rows not in ``qblocks`` stay 0."""
+    b_, hq, mq, _ = q.shape
+    hkv, mk = k.shape[1], k.shape[2]
+    nbq, nbk = _cdiv(mq, block), _cdiv(mk, block)
     heads = range(hq) if heads is None else heads
-    qblocks = range(nb) if qblocks is None else qblocks
-    out = np.zeros((b_, hq, nb, nb))
+    qblocks = range(nbq) if qblocks is None else qblocks
+    out = np.zeros((b_, hq, nbq, nbk))
     for b in range(b_):
         for h in heads:
             g = _kv_head(h, hq, hkv)
@@ -205,7 +235,8 @@ def minimal_set(cand: np.ndarray, tau: float) -> np.ndarray:
 
 
 def select_row(scores_row: np.ndarray, big_i: int, tau: float, causal: bool) -> np.ndarray:
-    """Boolean keep-mask (length NB) for one query-block row."""
+    """Boolean keep-mask (length NBk) for one query-block row; ``big_i`` is the
+    row's key-block index (its position in the whole sequence)."""
     nb = scores_row.shape[0]
     n_cand = big_i + 1 if causal else nb
     keep = np.zeros(nb, dtype=bool)
@@ -215,27 +246,28 @@ def select_row(scores_row: np.ndarray, big_i: int, tau: float, causal: bool) -> 
 
 
 def select_global_head(scores_h: np.ndarray, tau: float, causal: bool) -> np.ndarray:
-    """Global (flattened) selection for one head ([Flex] R Q3): keep-mask (NB, NB).
+    """Global (flattened) selection for one head ([Flex] R Q3): keep-mask (NBq, NBk).
 
-    Every candidate block (I, J) of the head (J <= I when causal) enters one
-    list in row-major order; the minimal set is taken over that list exactly as
-    for a single row (score descending, ties by list position, i.e. by (I, J)
-    row-major), against tau times the head's total candidate mass. The diagonal
-    blocks are then added.
+    Every candidate block (I, J) of the head (J <= I + NBk - NBq when causal)
+    enters one list in row-major order; the minimal set is taken over that list
+    exactly as for a single row (score descending, ties by list position, i.e.
+    by (I, J) row-major), against tau times the head's total candidate mass. The
+    diagonal blocks (I, I + NBk - NBq) are then added.
     """
-    nb = scores_h.shape[0]
+    nbq, nbk = scores_h.shape
+    qoff = nbk - nbq
     rows, cols = [], []
-    for big_i in range(nb):
-        n_cand = big_i + 1 if causal else nb
+    for big_i in range(nbq):
+        n_cand = big_i + qoff + 1 if causal else nbk
         rows.extend([big_i] * n_cand)
         cols.extend(range(n_cand))
     rows = np.asarray(rows)
     cols = np.asarray(cols)
     flat = _f64(scores_h)[rows, cols]
-    keep = np.zeros((nb, nb), dtype=bool)
+    keep = np.zeros((nbq, nbk), dtype=bool)
     chosen = minimal_set(flat, tau)
     keep[rows[chosen], cols[chosen]] = True
-    keep[np.arange(nb), np.arange(nb)] = True
+    keep[np.arange(nbq), np.arange(nbq) + qoff] = True
     return keep
 
 
@@ -246,10 +278,11 @@ def gqa_union(mask: np.ndarray, hkv: int) -> np.ndarray:
     Not from the pages: a reuse variant in which the sibling heads that read
     one KV head share a single block list, so one K/V tile serves all of them.
     """
-    b_, hq, nb, _ = mask.shape
+    b_, hq, nbq, nbk = mask.shape
     g = hq // hkv
-    out = mask.astype(bool).reshape(b_, hkv, g, nb, nb).any(axis=2, keepdims=True)
-    return np.ascontiguousarray(np.broadcast_to(out, (b_, hkv, g, nb, nb)).reshape(mask.shape), dtype=np.uint8)
+    out = mask.astype(bool).reshape(b_, hkv, g, nbq, nbk).any(axis=2, keepdims=True)
+    return np.ascontiguousarray(np.broadcast_to(out, (b_, hkv, g, nbq, nbk)).reshape(mask.shape),
+                                dtype=np.uint8)
 
 
 def select(scores: np.ndarray, tau, causal: bool, heads=None, qblocks=None,
@@ -260,7 +293,8 @@ def select(scores: np.ndarray, tau, causal: bool, heads=None, qblocks=None,
     "global": per head over all rows at once ([Flex] R Q3), all rows required;
     "gqa_union": "row", then the union over each KV group (``hkv`` heads).
     """
-    b_, hq, nb, _ = scores.shape
+    b_, hq, nbq, nbk = scores.shape
+    qoff = nbk - nbq          # key block of query block 0
     tau = np.broadcast_to(np.asarray(tau, dtype=np.float64), (hq,))
     some_heads = heads is not None
     heads = range(hq) if heads is None else heads
@@ -281,11 +315,11 @@ def select(scores: np.ndarray, tau, causal: bool, heads=None, qblocks=None,
             # the union needs every sibling of a selected head
             g = hq // hkv
             heads = sorted({hh for h in heads for hh in range((h // g) * g, (h // g + 1) * g)})
-    qblocks = range(nb) if qblocks is None else qblocks
+    qblocks = range(nbq) if qblocks is None else qblocks
     for b in range(b_):
         for h in heads:
             for big_i in qblocks:
-                mask[b, h, big_i] = select_row(scores[b, h, big_i], big_i, float(tau[h]), causal)
+                mask[b, h, big_i] = select_row(scores[b, h, big_i], big_i + qoff, float(tau[h]), causal)
     if mode == "gqa_union":
         mask = gqa_union(mask, hkv)
     return mask
@@ -313,15 +347,19 @@ def mask_to_index(mask: np.ndarray):
 
 def attend_row(qh, kh, vh, keep_row: np.ndarray, big_i: int, block: int,
                sm_scale: float, causal: bool):
-    """Output (Bk, C) and natural-log LSE (Bk,) for query block ``big_i``."""
+    """Output (rows, C) and natural-log LSE (rows,) for query block ``big_i``
+    (rows = the block's queries, fewer in a partial last block)."""
+    mq, mk = qh.shape[0], kh.shape[0]
+    off = mk - mq
     qb = _f64(qh[big_i * block:(big_i + 1) * block])
     blocks = np.nonzero(keep_row)[0]
     keys = (blocks[:, None] * block + np.arange(block)[None, :]).reshape(-1)
+    keys = keys[keys < mk]
     kk = _f64(kh[keys])
     vv = _f64(vh[keys])
     s = (qb @ kk.T) * sm_scale
     if causal:
-        qi = big_i * block + np.arange(block)[:, None]
+        qi = off + big_i * block + np.arange(qb.shape[0])[:, None]
         s[keys[None, :] > qi] = -np.inf
     mx = s.max(axis=1, keepdims=True)
     p = np.exp(s - mx)
@@ -333,32 +371,33 @@ def attend_row(qh, kh, vh, keep_row: np.ndarray, big_i: int, block: int,
 
 def attend(q, k, v, mask, block: int, sm_scale: float, causal: bool,
            heads=None, qblocks=None):
-    """Block-sparse attention with a block mask (B, Hq, NB, NB): (out, lse) float64."""
-    b_, hq, m, c = q.shape
+    """Block-sparse attention with a block mask (B, Hq, NBq, NBk): (out, lse) float64."""
+    b_, hq, mq, c = q.shape
     hkv = k.shape[1]
-    nb = m // block
+    nbq = _cdiv(mq, block)
     heads = range(hq) if heads is None else heads
-    qblocks = range(nb) if qblocks is None else qblocks
-    out = np.zeros((b_, hq, m, c))
-    lse = np.zeros((b_, hq, m))
+    qblocks = range(nbq) if qblocks is None else qblocks
+    out = np.zeros((b_, hq, mq, c))
+    lse = np.zeros((b_, hq, mq))
     for b in range(b_):
         for h in heads:
             g = _kv_head(h, hq, hkv)
             for big_i in qblocks:
                 o, l = attend_row(q[b, h], k[b, g], v[b, g], mask[b, h, big_i], big_i,
                                   block, sm_scale, causal)
-                out[b, h, big_i * block:(big_i + 1) * block] = o
-                lse[b, h, big_i * block:(big_i + 1) * block] = l
+                out[b, h, big_i * block:big_i * block + o.shape[0]] = o
+                lse[b, h, big_i * block:big_i * block + o.shape[0]] = l
     return out, lse
 
 
 def dense(q, k, v, block: int, sm_scale: float, causal: bool, heads=None, qblocks=None):
     """Dense attention: every candidate block kept."""
-    b_, hq, m, _ = q.shape
-    nb = m // block
-    full = np.ones((b_, hq, nb, nb), dtype=np.uint8)
+    b_, hq, mq, _ = q.shape
+    nbq, nbk = _cdiv(mq, block), _cdiv(k.shape[2], block)
+    full = np.ones((b_, hq, nbq, nbk), dtype=np.uint8)
     if causal:
-        full = np.broadcast_to(np.tril(np.ones((nb, nb), dtype=np.uint8)), full.shape).copy()
+        tri = np.tril(np.ones((nbq, nbk), dtype=np.uint8), k=nbk - nbq)
+        full = np.broadcast_to(tri, full.shape).copy()
     return attend(q, k, v, full, block, sm_scale, causal, heads, qblocks)
 
 
@@ -376,11 +415,11 @@ def prefill(q, k, v, block: int, stride: int, tau, score_scale: float, sm_scale:
 
 def density(mask: np.ndarray, causal: bool, qblocks=None) -> float:
     """Selected blocks / candidate blocks (diagonal counted as 1)."""
-    nb = mask.shape[-1]
-    rows = range(nb) if qblocks is None else list(qblocks)
+    nbq, nbk = mask.shape[-2:]
+    rows = range(nbq) if qblocks is None else list(qblocks)
     sel = 0
     cand = 0
     for big_i in rows:
         sel += int(mask[..., big_i, :].astype(bool).sum())
-        cand += (big_i + 1 if causal else nb) * int(np.prod(mask.shape[:-2]))
+        cand += (big_i + nbk - nbq + 1 if causal else nbk) * int(np.prod(mask.shape[:-2]))
     return sel / cand

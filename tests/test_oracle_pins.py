@@ -322,14 +322,15 @@ def test_mask_to_index():
 # --------------------------------------------------------------- attention
 
 def _sdpa_masked(q, k, v, mask, block, scale, causal):
-    """torch SDPA on the CPU in float64 with the block mask expanded to elements."""
+    """torch SDPA on the CPU in float64 with the block mask expanded to elements
+    (cropped to Mq x Mk; causal with the queries the last Mq of Mk tokens)."""
     hq, hkv = q.shape[1], k.shape[1]
+    mq, mk = q.shape[2], k.shape[2]
     kr = torch.from_numpy(np.repeat(k, hq // hkv, axis=1))
     vr = torch.from_numpy(np.repeat(v, hq // hkv, axis=1))
-    elem = np.repeat(np.repeat(mask.astype(bool), block, axis=-2), block, axis=-1)
+    elem = np.repeat(np.repeat(mask.astype(bool), block, axis=-2), block, axis=-1)[..., :mq, :mk]
     if causal:
-        m = q.shape[2]
-        elem = elem & np.tril(np.ones((m, m), dtype=bool))
+        elem = elem & np.tril(np.ones((mq, mk), dtype=bool), k=mk - mq)
     out = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(q), kr, vr, attn_mask=torch.from_numpy(elem), scale=scale)
     logits = scale * torch.from_numpy(q) @ kr.transpose(-1, -2)
@@ -400,3 +401,134 @@ def test_diagonal_pattern_block_scores_are_normalised():
     sc = oracle.block_scores(q, k, 32, 4, 0.3, True, pattern="diagonal")
     np.testing.assert_allclose(sc.sum(-1), 1.0, rtol=1e-12)
     assert (sc >= 0).all()
+
+
+# ------------------------------------------------ ragged and chunked lengths
+
+@pytest.mark.parametrize("stride,mq,mk,c", [(4, 30, 30, 3), (8, 61, 61, 2), (2, 7, 15, 4), (4, 13, 29, 3)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_ragged_strided_logits_equal_bruteforce(stride, mq, mk, c, causal):
+    # tokens past the end of a partial stride group count as zero vectors; the
+    # queries are the last mq of mk tokens (strided offset (mk - mq) / stride)
+    rng = _rng(stride + mq)
+    q = rng.standard_normal((mq, c))
+    k = rng.standard_normal((mk, c))
+    rq, rk = -(-mq // stride), -(-mk // stride)
+    off_s = (mk - mq) // stride
+    brute = np.zeros((rq, rk))
+    for i in range(rq):
+        for j in range(rk):
+            for a in range(stride):
+                qi, kj = i * stride + stride - 1 - a, j * stride + a
+                if qi < mq and kj < mk:
+                    brute[i, j] += q[qi] @ k[kj]
+            if causal and j > i + off_s:
+                brute[i, j] = -np.inf
+    got = oracle.strided_logits(q, k, stride, 1.0, causal)
+    np.testing.assert_allclose(got, brute, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_stride_one_ragged_equals_textbook_block_attention_mass(causal):
+    # S = 1, M = 61 with 16-row blocks: the last block holds 13 queries and 13
+    # keys; its score row averages over its 13 real rows
+    rng = _rng(12)
+    m, c, block = 61, 8, 16
+    q = rng.standard_normal((m, c))
+    k = rng.standard_normal((m, c))
+    scale = 0.6
+    logits = scale * (q @ k.T)
+    if causal:
+        logits = np.where(np.tril(np.ones((m, m), dtype=bool)), logits, -np.inf)
+    p = scipy.special.softmax(logits, axis=1)
+    nb = -(-m // block)
+    expect = np.zeros((nb, nb))
+    for big_i in range(nb):
+        rows = p[big_i * block:(big_i + 1) * block]
+        for big_j in range(nb):
+            expect[big_i, big_j] = rows[:, big_j * block:(big_j + 1) * block].sum() / rows.shape[0]
+    got = oracle.block_scores(q[None, None], k[None, None], block, 1, scale, causal)[0, 0]
+    np.testing.assert_allclose(got, expect, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(got.sum(axis=1), 1.0, rtol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_chunk_equals_last_rows_of_full_sequence(causal):
+    # queries = the last mq tokens of the sequence: the chunk's block scores,
+    # per-row selection and attention equal the last rows of the full run
+    rng = _rng(14)
+    mk, off, block, stride, c = 200, 64, 32, 4, 8      # NBk = 7 (last block 8 keys)
+    q = rng.standard_normal((1, 2, mk, c))
+    k = rng.standard_normal((1, 1, mk, c))
+    v = rng.standard_normal((1, 1, mk, c))
+    qc = q[:, :, off:]
+    full = oracle.block_scores(q, k, block, stride, 0.4, causal)
+    chunk = oracle.block_scores(qc, k, block, stride, 0.4, causal)
+    assert chunk.shape == (1, 2, 5, 7)
+    np.testing.assert_allclose(chunk, full[:, :, off // block:], rtol=1e-12, atol=1e-15)
+    tau = [0.8, 0.95]
+    mf = oracle.select(full, tau, causal)
+    mc = oracle.select(chunk, tau, causal)
+    np.testing.assert_array_equal(mc, mf[:, :, off // block:])
+    of, lf = oracle.attend(q, k, v, mf, block, 0.3, causal)
+    oc, lc = oracle.attend(qc, k, v, mc, block, 0.3, causal)
+    np.testing.assert_allclose(oc, of[:, :, off:], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lc, lf[:, :, off:], rtol=1e-12, atol=1e-13)
+    assert oracle.density(mc, causal) > 0
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attend_ragged_chunk_matches_sdpa(causal):
+    rng = _rng(15)
+    mq, mk, block = 100, 164, 32                         # NBq = 4, NBk = 6, offset 2 blocks
+    q = rng.standard_normal((1, 2, mq, 16))
+    k = rng.standard_normal((1, 1, mk, 16))
+    v = rng.standard_normal((1, 1, mk, 16))
+    nbq, nbk = 4, 6
+    mask = (rng.random((1, 2, nbq, nbk)) < 0.4).astype(np.uint8)
+    mask[..., np.arange(nbq), np.arange(nbq) + 2] = 1
+    if causal:
+        mask = mask * np.tril(np.ones((nbq, nbk), dtype=np.uint8), k=2)
+    out, lse = oracle.attend(q, k, v, mask, block, 0.25, causal)
+    ref, ref_lse = _sdpa_masked(q, k, v, mask, block, 0.25, causal)
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-12, atol=1e-12)
+    # tau = 1 keeps every candidate: dense attention over the chunk
+    sc = oracle.block_scores(q, k, block, 4, 0.3, causal)
+    np.testing.assert_allclose(sc.sum(axis=-1), 1.0, rtol=1e-12)
+    mk1 = oracle.select(sc, [1.0, 1.0], causal)
+    full = np.ones((1, 2, nbq, nbk), dtype=np.uint8)
+    if causal:
+        full = full * np.tril(np.ones((nbq, nbk), dtype=np.uint8), k=2)
+    np.testing.assert_array_equal(mk1, full)
+    o1, _ = oracle.attend(q, k, v, mk1, block, 0.25, causal)
+    d1, _ = _sdpa_masked(q, k, v, full, block, 0.25, causal)
+    np.testing.assert_allclose(o1, d1, rtol=1e-10, atol=1e-12)
+
+
+def test_global_selection_chunk_exhaustive():
+    # rectangular (chunked) block matrices: candidates J <= I + NBk - NBq
+    rng = _rng(33)
+    for trial in range(80):
+        nbq = int(rng.integers(1, 3))
+        qoff = int(rng.integers(1, 3))
+        nbk = nbq + qoff
+        sc = np.tril(rng.dirichlet(np.full(nbk, 0.6), size=nbq), k=qoff)
+        if trial % 4 == 0:
+            sc = np.round(sc * 4) / 4
+        tau = float(rng.choice([0.0, 0.5, 0.8, 0.95, 1.0]))
+        got = oracle.select_global_head(sc, tau, True)
+        cands = [(i, j) for i in range(nbq) for j in range(i + qoff + 1)]
+        vals = np.array([sc[i, j] for i, j in cands])
+        if tau >= 1.0:
+            m_star = len(cands)
+        else:
+            m_star = next(size for size in range(len(cands) + 1)
+                          if any(vals[list(sub)].sum() >= tau * vals.sum()
+                                 for sub in itertools.combinations(range(len(cands)), size)))
+        order = sorted(range(len(cands)), key=lambda t: (-vals[t], t))
+        want = np.zeros((nbq, nbk), dtype=bool)
+        for t in order[:m_star]:
+            want[cands[t]] = True
+        want[np.arange(nbq), np.arange(nbq) + qoff] = True
+        np.testing.assert_array_equal(got, want)
