@@ -7,7 +7,9 @@ stream. If the library is missing the import fails loudly; there is no
 fallback.
 
 Functions take contiguous CUDA (HIP) tensors: q (B, Hq, M, C), k and v
-(B, Hkv, M, C), all bfloat16 or all float32.
+(B, Hkv, Mk, C), all bfloat16 or all float32. Mk > M is a chunked prefill (the
+queries are the last M of the Mk tokens; Mk - M a multiple of the block), and
+neither length needs to be a multiple of the block or the stride.
 """
 from __future__ import annotations
 
@@ -102,20 +104,27 @@ def _selection(sel) -> int:
 
 
 def problem(B, Hq, Hkv, M, C, block, stride, causal, dtype, pattern=ANTIDIAGONAL,
-            selection=SELECT_ROW) -> Problem:
+            selection=SELECT_ROW, Mk=0) -> Problem:
     """C struct for the given sizes; dtype is torch.bfloat16/torch.float32 or 0/1;
-    selection is an xattn_selection value or "row" / "global" / "gqa_union"."""
+    selection is an xattn_selection value or "row" / "global" / "gqa_union";
+    Mk is the key length (0: M; the queries are the last M of Mk tokens)."""
     if isinstance(dtype, torch.dtype):
         dtype = {torch.bfloat16: XATTN_BF16, torch.float32: XATTN_F32}.get(dtype, 99)
     return Problem(B, Hq, Hkv, M, C, block, stride, int(bool(causal)), dtype, pattern,
-                   _selection(selection), 0)
+                   _selection(selection), Mk)
 
 
 def _problem_of(q, k, block, stride, causal, pattern=ANTIDIAGONAL, selection=SELECT_ROW) -> Problem:
+    """Sizes from q (B, Hq, M, C) and k (B, Hkv, Mk, C)."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be 4-D (B, H, M, C)")
     B, Hq, M, C = q.shape
-    return problem(B, Hq, k.shape[1], M, C, block, stride, causal, q.dtype, pattern, selection)
+    return problem(B, Hq, k.shape[1], M, C, block, stride, causal, q.dtype, pattern, selection,
+                   Mk=k.shape[2])
+
+
+def _cdiv(a, b):
+    return -(-a // b)
 
 
 def _ptr(t):
@@ -158,12 +167,12 @@ def prefill_workspace_bytes(p: Problem) -> int:
 
 def xattn_score(q, k, block, stride, score_scale, causal=True, block_scores=None, ws=None,
                 pattern=ANTIDIAGONAL):
-    """Block scores (B, Hq, NB, NB) float32."""
+    """Block scores (B, Hq, NBq, NBk) float32."""
     _same(q, k)
     p = _problem_of(q, k, block, stride, causal, pattern)
-    nb = q.shape[2] // block
+    nbq, nbk = _cdiv(q.shape[2], block), _cdiv(k.shape[2], block)
     if block_scores is None:
-        block_scores = torch.empty((q.shape[0], q.shape[1], nb, nb), dtype=torch.float32, device=q.device)
+        block_scores = torch.empty((q.shape[0], q.shape[1], nbq, nbk), dtype=torch.float32, device=q.device)
     need = workspace_bytes(p)
     if ws is None:
         ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
@@ -183,16 +192,18 @@ def _tau_host(tau, hq):
 
 def xattn_select(block_scores, tau, block, stride, causal=True, Hkv=None, C=128, dtype=torch.bfloat16,
                  want_mask=True, mask=None, kv_idx=None, kv_cnt=None, selection=SELECT_ROW):
-    """(mask u8 or None, kv_idx int32, kv_cnt int32) for block scores (B, Hq, NB, NB)."""
-    B, Hq, nb, _ = block_scores.shape
-    p = problem(B, Hq, Hkv or Hq, nb * block, C, block, stride, causal, dtype, selection=selection)
+    """(mask u8 or None, kv_idx int32, kv_cnt int32) for block scores (B, Hq, NBq, NBk);
+    NBk > NBq means the queries are the last NBq blocks of the NBk-block sequence."""
+    B, Hq, nbq, nbk = block_scores.shape
+    p = problem(B, Hq, Hkv or Hq, nbq * block, C, block, stride, causal, dtype, selection=selection,
+                Mk=nbk * block)
     dev = block_scores.device
     if mask is None and want_mask:
-        mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev)
+        mask = torch.empty((B, Hq, nbq, nbk), dtype=torch.uint8, device=dev)
     if kv_idx is None:
-        kv_idx = torch.empty((B, Hq, nb, nb), dtype=torch.int32, device=dev)
+        kv_idx = torch.empty((B, Hq, nbq, nbk), dtype=torch.int32, device=dev)
     if kv_cnt is None:
-        kv_cnt = torch.empty((B, Hq, nb), dtype=torch.int32, device=dev)
+        kv_cnt = torch.empty((B, Hq, nbq), dtype=torch.int32, device=dev)
     tau_h = _tau_host(tau, Hq)
     need = select_workspace_bytes(p)
     ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
@@ -235,13 +246,13 @@ class PrefillBuffers:
                  pattern=ANTIDIAGONAL, selection=SELECT_ROW):
         p = _problem_of(q, k, block, stride, causal, pattern, selection)
         B, Hq, M, C = q.shape
-        nb = M // block
+        nbq, nbk = _cdiv(M, block), _cdiv(k.shape[2], block)
         dev = q.device
         self.problem = p
-        self.block_scores = torch.empty((B, Hq, nb, nb), dtype=torch.float32, device=dev)
-        self.mask = torch.empty((B, Hq, nb, nb), dtype=torch.uint8, device=dev) if want_mask else None
-        self.kv_idx = torch.empty((B, Hq, nb, nb), dtype=torch.int32, device=dev)
-        self.kv_cnt = torch.empty((B, Hq, nb), dtype=torch.int32, device=dev)
+        self.block_scores = torch.empty((B, Hq, nbq, nbk), dtype=torch.float32, device=dev)
+        self.mask = torch.empty((B, Hq, nbq, nbk), dtype=torch.uint8, device=dev) if want_mask else None
+        self.kv_idx = torch.empty((B, Hq, nbq, nbk), dtype=torch.int32, device=dev)
+        self.kv_cnt = torch.empty((B, Hq, nbq), dtype=torch.int32, device=dev)
         self.ws = torch.empty(max(prefill_workspace_bytes(p), 4), dtype=torch.uint8, device=dev)
         self.out = torch.empty_like(q)
         self.lse = torch.empty((B, Hq, M), dtype=torch.float32, device=dev) if want_lse else None

@@ -38,11 +38,12 @@ xattn_status check_problem(const xattn_problem* p, bool need_stride = true) {
   if (p->selection != XATTN_SELECT_ROW && p->selection != XATTN_SELECT_GLOBAL &&
       p->selection != XATTN_SELECT_GQA_UNION)
     return fail(XATTN_ERR_ARG, "selection %d is not an xattn_selection", p->selection);
-  if (p->Mk != 0 && p->Mk != p->M)
-    return fail(XATTN_ERR_UNSUPPORTED, "Mk=%d differs from M=%d", p->Mk, p->M);
+  const int mk = p->Mk ? p->Mk : p->M;
+  if (mk < p->M) return fail(XATTN_ERR_SHAPE, "Mk=%d is shorter than M=%d", p->Mk, p->M);
   if (p->Hq % p->Hkv) return fail(XATTN_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
   if (p->Hq > XATTN_MAX_HEADS) return fail(XATTN_ERR_UNSUPPORTED, "Hq=%d exceeds %d", p->Hq, XATTN_MAX_HEADS);
-  if (p->M % p->block) return fail(XATTN_ERR_SHAPE, "M=%d is not a multiple of block=%d", p->M, p->block);
+  if ((mk - p->M) % p->block)
+    return fail(XATTN_ERR_SHAPE, "Mk - M = %d is not a multiple of block=%d", mk - p->M, p->block);
   if (need_stride && p->block % p->stride)
     return fail(XATTN_ERR_SHAPE, "block=%d is not a multiple of stride=%d", p->block, p->stride);
   if (p->C != 64 && p->C != 128) return fail(XATTN_ERR_UNSUPPORTED, "head dim C=%d (supported: 64, 128)", p->C);
@@ -50,17 +51,19 @@ xattn_status check_problem(const xattn_problem* p, bool need_stride = true) {
   const int r = need_stride ? p->block / p->stride : 2;
   if (!pow2(r) || r < 2 || r > 32)
     return fail(XATTN_ERR_UNSUPPORTED, "block/stride=%d (supported: 2, 4, 8, 16, 32)", r);
-  if (p->M / p->block > XATTN_MAX_BLOCKS)
-    return fail(XATTN_ERR_UNSUPPORTED, "NB=%d exceeds %d blocks", p->M / p->block, XATTN_MAX_BLOCKS);
-  const size_t per_head = (size_t)p->M * p->C;
+  const int nbk = (mk + p->block - 1) / p->block;
+  if (nbk > XATTN_MAX_BLOCKS)
+    return fail(XATTN_ERR_UNSUPPORTED, "%d key blocks exceed %d", nbk, XATTN_MAX_BLOCKS);
+  const size_t per_head = (size_t)mk * p->C;
   if ((size_t)p->B * p->Hq * per_head > ((size_t)1 << 40))
     return fail(XATTN_ERR_UNSUPPORTED, "problem too large");
   return XATTN_OK;
 }
 
 xattn::Shape shape_of(const xattn_problem* p) {
-  return xattn::Shape{p->B,      p->Hq,     p->Hkv,    p->M,      p->C,
-                      p->block,  p->stride, p->causal, p->pattern, p->selection};
+  return xattn::Shape{p->B,      p->Hq,     p->Hkv,    p->M,       p->C,
+                      p->block,  p->stride, p->causal, p->pattern, p->selection,
+                      p->Mk ? p->Mk : p->M};
 }
 
 xattn_status check_scale(float x, const char* name) {
@@ -189,7 +192,8 @@ const char* xattn_last_error(void) { return g_err; }
 
 size_t xattn_score_workspace_bytes(const xattn_problem* p) {
   if (check_problem(p) != XATTN_OK) return 0;
-  return (size_t)p->B * p->Hq * (size_t)(p->M / p->block) * (size_t)(p->M / p->stride) * sizeof(float);
+  const xattn::Shape s = shape_of(p);
+  return (size_t)p->B * p->Hq * (size_t)s.NBq() * s.NBk() * s.r() * sizeof(float);
 }
 
 size_t xattn_attn_workspace_bytes(const xattn_problem* p) {

@@ -3,11 +3,16 @@
 // Semantics ("XAttention: Block Sparse Attention with Antidiagonal Scoring",
 // arXiv abstract: block-sparse attention computes only on the important
 // blocks): for query i of block I, exact softmax attention over the keys of
-// the listed key blocks, restricted to keys <= i when causal.
+// the listed key blocks, restricted to keys <= i when causal. The queries may
+// be the last Mq of Mk tokens (query i is then at position Mk - Mq + i), and
+// either length may end in a partial block: keys past the end are masked,
+// query rows past the end are not written.
 //
 // bf16 path (gfx950 MFMA):
-//  * one workgroup per (b, h, I) query block; BLK/32 waves, each wave owns 32
-//    query rows whose Q fragments stay in VGPRs for the whole row;
+//  * a work item is one (b, h, I) query block (or a pair, see the modes);
+//    BLK/32 waves, each wave owns 32 query rows whose Q fragments stay in VGPRs
+//    for the whole row. Dense launches one workgroup per item; sparse runs
+//    persistent workgroups that pull items from per-XCD queues;
 //  * key blocks are consumed in 64-key sub-tiles: K and V rows are fetched from
 //    HBM into registers one sub-tile ahead and written to a double-buffered LDS
 //    tile, so one barrier per sub-tile orders reuse;
@@ -21,17 +26,10 @@
 #include "common.h"
 #include "kernels.h"
 
-// log2 of the neighbouring query-block rows a KV group keeps on one XCD in the
-// sparse kernel (see xcd_map)
 // 1: raise wave priority around the MFMA blocks (s_setprio), so a wave issuing
 // matrix work is preferred over one in its softmax phase on the same SIMD
 #ifndef XATTN_ATTN_SETPRIO
 #define XATTN_ATTN_SETPRIO 0
-#endif
-// 1: software-pipelined attention loop (S(t+1) MFMAs overlap the softmax of
-// tile t); 0: the plain loop
-#ifndef XATTN_ATTN_PIPELINE
-#define XATTN_ATTN_PIPELINE 0
 #endif
 // 1: sparse workgroups pair neighbouring rows of a head; 0: one row each
 #ifndef XATTN_SPARSE_PAIR_ROWS
@@ -41,6 +39,8 @@
 #ifndef XATTN_SPARSE_GROUP_ON_XCD
 #define XATTN_SPARSE_GROUP_ON_XCD 1
 #endif
+// log2 of the neighbouring query-block rows a KV group keeps on one XCD in the
+// sparse kernel (see xcd_map)
 #ifndef XATTN_SPARSE_ROWS_PER_XCD_LOG2
 #define XATTN_SPARSE_ROWS_PER_XCD_LOG2 0
 #endif
@@ -52,6 +52,7 @@
 
 namespace xattn {
 
+// Queries are the last Mq of Mk tokens: query block I is key block I + qoff.
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -61,7 +62,7 @@ struct AttnArgs {
   uint16_t* out;
   float* lse;
   uint32_t* queue;   // sparse: kQueueWords zeroed words (per-XCD item counters)
-  int B, Hq, Hkv, M, NB;
+  int B, Hq, Hkv, Mq, Mk, NBq, NBk, qoff;
   float scale_log2;  // sm_scale * log2(e)
 };
 
@@ -115,7 +116,7 @@ struct AttnItems {
   uint32_t GW, NP, n;
   __device__ AttnItems(const AttnArgs& a, int MODE) {
     const uint32_t G = a.Hq / a.Hkv;
-    NP = MODE == MODE_ROWS ? (a.NB + 1) / 2 : a.NB;
+    NP = MODE == MODE_ROWS ? (a.NBq + 1) / 2 : a.NBq;
     GW = MODE == MODE_SIBLINGS ? G / 2 : G;
     n = (uint32_t)a.B * a.Hkv * GW * NP;
   }
@@ -170,42 +171,43 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   auto slot_I = [&](int s2) { return MODE == MODE_ROWS ? 2 * P + s2 : P; };
   const int h = slot_h(hs);                    // this wave's head
   const int I = slot_I(hs);                    // this wave's query block
-  const bool live = I < a.NB;                  // the odd row count leaves a half-empty pair
+  const bool live = I < a.NBq;                 // the odd row count leaves a half-empty pair
 
   const size_t bh = (size_t)b * a.Hq + h;
   const size_t bg = (size_t)b * a.Hkv + g;
-  const uint16_t* qh = a.q + bh * a.M * C;
-  const uint16_t* kh = a.k + bg * a.M * C;
-  const uint16_t* vh = a.v + bg * a.M * C;
+  const uint16_t* qh = a.q + bh * a.Mq * C;
+  const uint16_t* kh = a.k + bg * a.Mk * C;
+  const uint16_t* vh = a.v + bg * a.Mk * C;
+  const int NBk = a.NBk;
 
   int cnt;  // entries in the (union) block list
   if constexpr (SPARSE) {
     // cache the row's block list in LDS once, so no dependent global load sits
     // in front of each tile fetch; out-of-range entries are clamped
     if constexpr (SLOTS == 1) {
-      cnt = a.kv_cnt[bh * a.NB + I];
-      cnt = cnt < 0 ? 0 : (cnt > a.NB ? a.NB : cnt);
-      const int32_t* idx = a.kv_idx + (bh * a.NB + I) * a.NB;
+      cnt = a.kv_cnt[bh * a.NBq + I];
+      cnt = cnt < 0 ? 0 : (cnt > NBk ? NBk : cnt);
+      const int32_t* idx = a.kv_idx + (bh * a.NBq + I) * NBk;
       for (int t = tid; t < cnt; t += NT) {
         int jb = idx[t];
-        jb = jb < 0 ? 0 : (jb >= a.NB ? a.NB - 1 : jb);
+        jb = jb < 0 ? 0 : (jb >= NBk ? NBk - 1 : jb);
         idx_s[t] = (uint16_t)jb;
       }
     } else {
       // union of the slots' ascending lists: per-block slot bits, then an
       // ascending compaction
       uint8_t* flag = memb_s + L::IDX_MAX;     // [NB] scratch bits
-      for (int j = tid; j < a.NB; j += NT) flag[j] = 0;
+      for (int j = tid; j < NBk; j += NT) flag[j] = 0;
       __syncthreads();
       for (int s2 = 0; s2 < SLOTS; ++s2) {
-        if (slot_I(s2) >= a.NB) continue;
-        const size_t row = ((size_t)b * a.Hq + slot_h(s2)) * a.NB + slot_I(s2);
+        if (slot_I(s2) >= a.NBq) continue;
+        const size_t row = ((size_t)b * a.Hq + slot_h(s2)) * a.NBq + slot_I(s2);
         int c2 = a.kv_cnt[row];
-        c2 = c2 < 0 ? 0 : (c2 > a.NB ? a.NB : c2);
-        const int32_t* idx = a.kv_idx + row * a.NB;
+        c2 = c2 < 0 ? 0 : (c2 > NBk ? NBk : c2);
+        const int32_t* idx = a.kv_idx + row * NBk;
         for (int t = tid; t < c2; t += NT) {
           int jb = idx[t];
-          jb = jb < 0 ? 0 : (jb >= a.NB ? a.NB - 1 : jb);
+          jb = jb < 0 ? 0 : (jb >= NBk ? NBk - 1 : jb);
           // slots write distinct bits; byte-wide OR through a word atomic
           __hip_atomic_fetch_or(reinterpret_cast<unsigned*>(flag + (jb & ~3)),
                                 (unsigned)(1u << s2) << (8 * (jb & 3)), __ATOMIC_RELAXED,
@@ -213,8 +215,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
         }
       }
       __syncthreads();
-      const int per = (a.NB + NT - 1) / NT;
-      const int j0 = tid * per, j1 = min(j0 + per, a.NB);
+      const int per = (NBk + NT - 1) / NT;
+      const int j0 = tid * per, j1 = min(j0 + per, NBk);
       int mine = 0;
       for (int j = j0; j < j1; ++j) mine += flag[j] != 0;
       int incl = mine;
@@ -243,17 +245,19 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
     }
   } else {
     // dense: every candidate of the workgroup's (latest) row
-    const int Imax = slot_I(SLOTS - 1) < a.NB ? slot_I(SLOTS - 1) : slot_I(0);
-    cnt = CAUSAL ? Imax + 1 : a.NB;
+    const int Imax = slot_I(SLOTS - 1) < a.NBq ? slot_I(SLOTS - 1) : slot_I(0);
+    cnt = CAUSAL ? Imax + a.qoff + 1 : NBk;
   }
   const int n_sub = cnt * SUB;
 
   // ---- Q fragments (B operand of S^T = K Q^T): Q[q0 + l32][16kk + 8hh .. +7]
-  const int q0 = I * BLK + slice * 32;
+  const int q0 = I * BLK + slice * 32;           // first query row of this wave
+  const int qa0 = q0 + a.qoff * BLK;             // its position in the key sequence
   bf16x8 qf[KK];
   {
-    // a dead slot reads row 0 of its head (never used) instead of past the end
-    const uint16_t* qrow = qh + (size_t)(live ? q0 + l32 : l32) * C + 8 * hh;
+    // rows past the end (a partial last block, or a dead slot) read the last
+    // query row instead; their outputs are never stored
+    const uint16_t* qrow = qh + (size_t)min(live ? q0 + l32 : l32, a.Mq - 1) * C + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
       qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * kk));
@@ -287,8 +291,11 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
     for (int p = 0; p < PER_T; ++p) {
       const int c = tid + p * NT;
       const int row = c / (C / 8), col = (c % (C / 8)) * 8;
-      r[p] = *reinterpret_cast<const u32x4*>(kh + (size_t)(k0 + row) * C + col);
-      r[PER_T + p] = *reinterpret_cast<const u32x4*>(vh + (size_t)(k0 + row) * C + col);
+      // keys past the end (a partial last block) load the last key; they are
+      // masked out of the softmax
+      const size_t kr = (size_t)min(k0 + row, a.Mk - 1);
+      r[p] = *reinterpret_cast<const u32x4*>(kh + kr * C + col);
+      r[PER_T + p] = *reinterpret_cast<const u32x4*>(vh + kr * C + col);
     }
   };
   auto store_tile = [&](int buf, const Stage& r) {
@@ -304,7 +311,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   // one sub-tile of online-softmax attention for this wave
   auto compute = [&](int t, int buf) {
     const int k0 = key_start(t);
-    if (CAUSAL && (k0 > q0 + 31)) return;       // whole sub-tile above this wave's rows
+    if (CAUSAL && (k0 > qa0 + 31)) return;      // whole sub-tile above this wave's rows
+    if (k0 >= a.Mk) return;                     // whole sub-tile past the last key
     if (!mine_tile(t)) return;                  // selected only by the other head
     const unsigned char* Kb = Ks + buf * L::TILE_B;
     const unsigned char* Vb = Vs + buf * L::TILE_B;
@@ -331,14 +339,15 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
         for (int n = 0; n < 2; ++n) sacc[n] = mfma32x32x16(ka[u][n], qf[k0b + u], sacc[n]);
     }
     if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-    if (CAUSAL && (k0 + L::KT - 1 > q0)) {
-      const int qi = q0 + l32;
+    if ((CAUSAL && (k0 + L::KT - 1 > qa0)) || k0 + L::KT > a.Mk) {
+      const int qi = qa0 + l32;
+      const int kmax = CAUSAL ? min(qi, a.Mk - 1) : a.Mk - 1;  // last visible key
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * n + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > qi) sacc[n][r] = -INFINITY;
+          if (key > kmax) sacc[n][r] = -INFINITY;
         }
     }
     float mx = -INFINITY;
@@ -397,163 +406,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   };
 
   __syncthreads();  // block list visible
-  if constexpr (XATTN_ATTN_PIPELINE != 0) {
-    // Software-pipelined loop. K runs one LDS stage ahead of V: while a wave
-    // turns S(t) into P(t) (max, exp2, sum, bf16 pack — VALU work), it already
-    // issues the MFMAs of S(t+1) = K(t+1) Q^T, so the matrix pipe and the VALU
-    // overlap inside the wave; PV(t) follows. The exp2 runs against the current
-    // reference m_run; in the rare case the tile max exceeds it by more than 8
-    // (log2 units) the reference is raised, O and l rescaled and P recomputed.
-    // Iteration t reads K(t+1) from Kbuf[(t+1)&1] and V(t) from Vbuf[t&1] and,
-    // after the barrier-protected compute, stores K(t+2) -> Kbuf[t&1] and
-    // V(t+1) -> Vbuf[(t+1)&1]; each buffer was last read one iteration earlier.
-    typedef u32x4 Half[PER_T];
-    auto load_k = [&](int t, Half& r) {
-      const int k0 = key_start(t);
-#pragma unroll
-      for (int p = 0; p < PER_T; ++p) {
-        const int c = tid + p * NT;
-        r[p] = *reinterpret_cast<const u32x4*>(kh + (size_t)(k0 + c / (C / 8)) * C + (c % (C / 8)) * 8);
-      }
-    };
-    auto load_v = [&](int t, Half& r) {
-      const int k0 = key_start(t);
-#pragma unroll
-      for (int p = 0; p < PER_T; ++p) {
-        const int c = tid + p * NT;
-        r[p] = *reinterpret_cast<const u32x4*>(vh + (size_t)(k0 + c / (C / 8)) * C + (c % (C / 8)) * 8);
-      }
-    };
-    auto store_k = [&](int buf, const Half& r) {
-#pragma unroll
-      for (int p = 0; p < PER_T; ++p) {
-        const int c = tid + p * NT;
-        *reinterpret_cast<u32x4*>(Ks + buf * L::TILE_B + L::k_off(c / (C / 8), c % (C / 8))) = r[p];
-      }
-    };
-    auto store_v = [&](int buf, const Half& r) {
-#pragma unroll
-      for (int p = 0; p < PER_T; ++p) {
-        const int c = tid + p * NT;
-        *reinterpret_cast<u32x4*>(Vs + buf * L::TILE_B + L::v_off(c / (C / 8), 16 * (c % (C / 8)))) = r[p];
-      }
-    };
-    auto qk = [&](int kbuf, f32x16 (&sacc)[2]) {
-      const unsigned char* Kb = Ks + kbuf * L::TILE_B;
-      sacc[0] = f32x16{};
-      sacc[1] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-          const bf16x8 ka = __builtin_bit_cast(
-              bf16x8, *reinterpret_cast<const u32x4*>(Kb + L::k_off(32 * n + l32, 2 * kk + hh)));
-          sacc[n] = mfma32x32x16(ka, qf[kk], sacc[n]);
-        }
-    };
-    // P(t) from S(t), O += V(t)^T P(t); S(t+1) is issued in between
-    auto step = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-      const int k0 = key_start(t);
-      const bool mine = mine_tile(t);
-      if ((CAUSAL && (k0 + L::KT - 1 > q0)) || !mine) {
-        const int qi = q0 + l32;
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * n + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (!mine || (CAUSAL && key > qi)) sc[n][r] = -INFINITY;
-          }
-      }
-      // S(t+1): issued now, consumed next iteration (a stale buffer after the
-      // last tile; the result is then unused)
-      qk((t + 1) & 1, sn);
-      float mx = -INFINITY;
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[n][r]);
-      mx = halves_max(mx);
-      const float m_tile = mx * a.scale_log2;
-      float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      bf16x8 pb[4];
-      float lsum = 0.f;
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(fmaf(sc[n][r], a.scale_log2, -m_use));
-          lsum += pr;
-          pb[2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
-        }
-      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + 8.f) != 0) {
-        const float m_new = fmaxf(m_run, m_tile);
-        // 0 on a lane's first visible tile; 1 while a lane has seen no key
-        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int d = 0; d < DN; ++d)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-        m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        lsum = 0.f;
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float pr = fast_exp2(fmaf(sc[n][r], a.scale_log2, -m_use));
-            lsum += pr;
-            pb[2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
-          }
-      }
-      l_run += lsum;
-      const unsigned char* Vb = Vs + (t & 1) * L::TILE_B;
-      const int G16 = lane >> 4, s16 = lane & 15;
-#pragma unroll
-      for (int tc = 0; tc < 4; ++tc) {
-        const int vrow = 16 * tc + 4 * (G16 >> 1) + (s16 >> 2);
-#pragma unroll
-        for (int d = 0; d < DN; ++d) {
-          const int vbyte = 2 * (32 * d + 16 * (G16 & 1) + 4 * (s16 & 3));
-          const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow, vbyte)));
-          const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow + 8, vbyte)));
-          typedef short i16x8 __attribute__((ext_vector_type(8)));
-          const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[d] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pb[tc], o[d]);
-        }
-      }
-    };
-
-    Half rk, rv;
-    f32x16 sa[2], sb[2];
-    if (n_sub > 0) {
-      load_k(0, rk);
-      load_v(0, rv);
-      store_k(0, rk);
-      store_v(0, rv);
-      if (n_sub > 1) {
-        load_k(1, rk);
-        store_k(1, rk);
-      }
-    }
-    __syncthreads();
-    if (n_sub > 0) qk(0, sa);
-    __syncthreads();  // Kbuf[0] is refilled in iteration 0
-    auto iter = [&](int t, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
-      const bool k2 = t + 2 < n_sub, v1 = t + 1 < n_sub;
-      if (k2) load_k(t + 2, rk);
-      if (v1) load_v(t + 1, rv);
-      step(t, sc, sn);
-      if (k2) store_k(t & 1, rk);
-      if (v1) store_v((t + 1) & 1, rv);
-      __syncthreads();
-    };
-    for (int t = 0; t < n_sub; t += 2) {
-      iter(t, sa, sb);
-      if (t + 1 < n_sub) iter(t + 1, sb, sa);
-    }
-  } else if constexpr (DEPTH == 1) {
+  if constexpr (DEPTH == 1) {
     Stage r0;
     if (n_sub > 0) {
       load_tile(0, r0);
@@ -592,7 +445,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   const float l_tot = halves_sum(l_run);
   const float inv = 1.f / l_tot;
   const int qi = q0 + l32;
-  uint16_t* orow = a.out + (bh * a.M + qi) * C;
+  if (qi >= a.Mq) return;  // padding rows of a partial last block
+  uint16_t* orow = a.out + (bh * a.Mq + qi) * C;
 #pragma unroll
   for (int d = 0; d < DN; ++d)
 #pragma unroll
@@ -605,7 +459,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
              ((uint32_t)f32_to_bf16(o[d][4 * g4 + 3] * inv) << 16);
       *reinterpret_cast<u32x2*>(orow + dc) = w;
     }
-  if (a.lse && hh == 0) a.lse[bh * a.M + qi] = (m_run + log2f(l_tot)) * kLn2;
+  if (a.lse && hh == 0) a.lse[bh * a.Mq + qi] = (m_run + log2f(l_tot)) * kLn2;
 }
 
 // Claims the next item for a persistent workgroup. queue[32 x] counts the
@@ -677,21 +531,24 @@ struct AttnArgsF32 {
   const int32_t* kv_cnt;
   float* out;
   float* lse;
-  int B, Hq, Hkv, M, NB, block, causal;
+  int B, Hq, Hkv, Mq, Mk, NBq, NBk, qoff, block, causal;
   float scale_log2;
 };
 
 template <int C>
 __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgsF32 a) {
-  const int qi = blockIdx.x * 64 + threadIdx.x;   // M is a multiple of 64
+  const int qi = blockIdx.x * 64 + threadIdx.x;
+  if (qi >= a.Mq) return;  // no barriers below
   const int h = blockIdx.y % a.Hq;
   const int b = blockIdx.y / a.Hq;
   const int g = h / (a.Hq / a.Hkv);
   const size_t bh = (size_t)b * a.Hq + h, bg = (size_t)b * a.Hkv + g;
-  const float* qrow = a.q + (bh * a.M + qi) * C;
-  const float* kh = a.k + bg * a.M * C;
-  const float* vh = a.v + bg * a.M * C;
+  const float* qrow = a.q + (bh * a.Mq + qi) * C;
+  const float* kh = a.k + bg * a.Mk * C;
+  const float* vh = a.v + bg * a.Mk * C;
   const int I = qi / a.block;
+  const int qa = qi + a.qoff * a.block;           // position in the key sequence
+  const int kmax = a.causal ? min(qa, a.Mk - 1) : a.Mk - 1;
   float qv[C], acc[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) { qv[c] = qrow[c]; acc[c] = 0.f; }
@@ -699,17 +556,17 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgsF32 a) {
   int cnt;
   const int32_t* idx = nullptr;
   if (a.kv_idx) {
-    cnt = a.kv_cnt[bh * a.NB + I];
-    cnt = cnt < 0 ? 0 : (cnt > a.NB ? a.NB : cnt);
-    idx = a.kv_idx + (bh * a.NB + I) * a.NB;
+    cnt = a.kv_cnt[bh * a.NBq + I];
+    cnt = cnt < 0 ? 0 : (cnt > a.NBk ? a.NBk : cnt);
+    idx = a.kv_idx + (bh * a.NBq + I) * a.NBk;
   } else {
-    cnt = a.causal ? I + 1 : a.NB;
+    cnt = a.causal ? I + a.qoff + 1 : a.NBk;
   }
   for (int t = 0; t < cnt; ++t) {
     int jb = idx ? idx[t] : t;
-    jb = jb < 0 ? 0 : (jb >= a.NB ? a.NB - 1 : jb);
+    jb = jb < 0 ? 0 : (jb >= a.NBk ? a.NBk - 1 : jb);
     for (int kj = jb * a.block; kj < (jb + 1) * a.block; ++kj) {
-      if (a.causal && kj > qi) break;
+      if (kj > kmax) break;
       const float* kr = kh + (size_t)kj * C;
       float s = 0.f;
 #pragma unroll
@@ -726,10 +583,10 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgsF32 a) {
     }
   }
   const float inv = 1.f / l;
-  float* orow = a.out + (bh * a.M + qi) * C;
+  float* orow = a.out + (bh * a.Mq + qi) * C;
 #pragma unroll
   for (int c = 0; c < C; ++c) orow[c] = acc[c] * inv;
-  if (a.lse) a.lse[bh * a.M + qi] = (m + log2f(l)) * kLn2;
+  if (a.lse) a.lse[bh * a.Mq + qi] = (m + log2f(l)) * kLn2;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -747,7 +604,7 @@ static int resident_workgroups(Kern kern, int threads) {
 template <int C, int BLK, int MODE>
 static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t st) {
   const int G = s.Hq / s.Hkv;
-  const int NP = MODE == MODE_ROWS ? (s.NB() + 1) / 2 : s.NB();
+  const int NP = MODE == MODE_ROWS ? (s.NBq() + 1) / 2 : s.NBq();
   const int GW = MODE == MODE_SIBLINGS ? G / 2 : G;
   const size_t n_items = (size_t)s.B * s.Hkv * GW * NP;
   const int threads = BLK * 2 * AttnMode<MODE>::SLOTS;
@@ -795,7 +652,9 @@ hipError_t launch_attn_bf16(const Shape& s, const uint16_t* q, const uint16_t* k
                             const uint16_t* v, const int32_t* kv_idx, const int32_t* kv_cnt,
                             float sm_scale, uint16_t* out, float* lse, uint32_t* queue,
                             hipStream_t st) {
-  AttnArgs a{q, k, v, kv_idx, kv_cnt, out, lse, queue, s.B, s.Hq, s.Hkv, s.M, s.NB(), sm_scale * kLog2e};
+  AttnArgs a{q,   k,    v,        kv_idx,  kv_cnt,  out,    lse,    queue,
+             s.B, s.Hq, s.Hkv,    s.M,     s.Mk,    s.NBq(), s.NBk(), s.qoff(),
+             sm_scale * kLog2e};
   if (s.C == 128 && s.block == 128) return launch_bf16_cb<128, 128>(s, a, st);
   if (s.C == 128 && s.block == 64) return launch_bf16_cb<128, 64>(s, a, st);
   if (s.C == 64 && s.block == 128) return launch_bf16_cb<64, 128>(s, a, st);
@@ -806,9 +665,10 @@ hipError_t launch_attn_bf16(const Shape& s, const uint16_t* q, const uint16_t* k
 hipError_t launch_attn_f32(const Shape& s, const float* q, const float* k, const float* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt, float sm_scale,
                            float* out, float* lse, hipStream_t st) {
-  AttnArgsF32 a{q, k, v, kv_idx, kv_cnt, out, lse, s.B, s.Hq, s.Hkv, s.M, s.NB(), s.block,
-                s.causal, sm_scale * kLog2e};
-  dim3 grid(s.M / 64, s.B * s.Hq);
+  AttnArgsF32 a{q,    k,       v,       kv_idx,   kv_cnt,  out,      lse,
+                s.B,  s.Hq,    s.Hkv,   s.M,      s.Mk,    s.NBq(),  s.NBk(),
+                s.qoff(), s.block, s.causal, sm_scale * kLog2e};
+  dim3 grid((s.M + 63) / 64, s.B * s.Hq);
   if (s.C == 64)
     hipLaunchKernelGGL((attn_fwd_f32_kernel<64>), grid, dim3(64), 0, st, a);
   else if (s.C == 128)

@@ -9,18 +9,26 @@
 
 namespace xattn {
 
+// Queries are the last M of Mk tokens (Mk = M: plain prefill); Mk - M is a
+// multiple of the block. Lengths need not be multiples of the stride or block:
+// the last stride group and the last block may be partial.
 struct Shape {
   int B, Hq, Hkv, M, C, block, stride, causal;
   int diagonal;  // 1: scoring pairs q[iS+s] with k[jS+s] instead of k[jS+S-1-s]
   int selection; // SEL_ROW, SEL_GLOBAL or SEL_GQA_UNION
-  int NB() const { return M / block; }
-  int R() const { return M / stride; }
+  int Mk;        // key length
+  int NBq() const { return (M + block - 1) / block; }
+  int NBk() const { return (Mk + block - 1) / block; }
+  int qoff() const { return (Mk - M) / block; }  // key block of query block 0
+  int Rq() const { return (M + stride - 1) / stride; }
+  int Rk() const { return (Mk + stride - 1) / stride; }
   int r() const { return block / stride; }
 };
 
 // Stage 1: per (strided row i, key block J) partial log2-sum-exp of the scaled
 // strided antidiagonal logits, written to ws as [b][h][I][J][t] float32 with
-// I = i / r, t = i % r.
+// I = i / r < NBq, J < NBk, t = i % r (rows past the last strided query row of
+// a partial block are not written).
 hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
                                       float score_scale, float* ws, hipStream_t st);
 hipError_t launch_score_partials_f32(const Shape& s, const float* q, const float* k,

@@ -8,6 +8,10 @@
 //   A'[i][j] = sum_{s<S} q[i*S+s] . k[j*S+S-1-s],  logit = score_scale * A',
 //   causal: j <= i at the strided level; softmax over j per strided row i;
 //   block score [I][J] = (1/r) sum_{i in I, j in J} p[i][j].
+// Ragged and chunked lengths: tokens past the end of a partial stride group are
+// zero vectors; strided keys past the last one are masked; a partial last
+// query block divides by its count of real strided rows; with the queries the
+// last M of Mk tokens, strided query row i is absolute row i + (Mk - M) / S.
 //
 // Design: the strided logits are an R x R x (S*C) GEMM per head. The
 // (M/S)^2 logit matrix never reaches HBM. Each 128 x 128 output tile
@@ -24,6 +28,8 @@
 // 128 x 128 one (128 vs 64 FLOP per byte). K~' row j, chunk c is the contiguous run
 // k[j*S + S-1 - (64c)/C][(64c)%C ...] — the stride group read in reverse, so
 // the reversal costs only address arithmetic.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 #include "score_row.h"
@@ -34,10 +40,13 @@ struct ScoreArgs {
   const uint16_t* q;
   const uint16_t* k;
   float* ws;
-  int B, Hq, Hkv, M, S, R, NB;
+  int B, Hq, Hkv, Mq, Mk, S, Rq, Rk, NBq, NBk;
+  int qoff_s;     // absolute strided row of strided query row 0: (Mk - Mq) / S
   int diagonal;   // 1: key row j*S + s instead of j*S + S-1-s
-  int T;          // strided tiles per head: ceil(R / SC_TILE)
+  int Tq, Tk;     // strided tiles per head: ceil(Rq / SC_TILE), ceil(Rk / SC_TILE)
+  int c0;         // causal: key tiles of query tile tq are tk <= tq + c0
   int pairs;      // tile pairs per head
+  int tail;       // 1: Mq or Mk is not a multiple of S (partial stride groups)
   float scale2;   // score_scale * log2(e)
 };
 
@@ -63,17 +72,22 @@ __device__ __forceinline__ int sc_off(int row, int chunk) {
   return row * SC_KC + 8 * (chunk ^ ((row >> 2) & 3));
 }
 
-__device__ __forceinline__ void tile_pair(int p, bool causal, int T, int& tq, int& tk) {
+// Tile pair p of a head -> (query tile, key tile). Causal: query tile tq meets
+// key tiles 0 .. min(Tk - 1, tq + c0), a trapezoid (a triangle when the
+// queries start at the first token); the row walk is at most Tq steps.
+__device__ __forceinline__ void tile_pair(int p, bool causal, int Tq, int Tk, int c0, int& tq, int& tk) {
   if (!causal) {
-    tq = p / T;
-    tk = p % T;
+    tq = p / Tk;
+    tk = p % Tk;
     return;
   }
-  int x = (int)((sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
-  while ((x + 1) * (x + 2) / 2 <= p) ++x;
-  while (x * (x + 1) / 2 > p) --x;
-  tq = x;
-  tk = p - x * (x + 1) / 2;
+  int base = 0;
+  for (tq = 0; tq < Tq - 1; ++tq) {
+    const int n = min(Tk, tq + c0 + 1);
+    if (p < base + n) break;
+    base += n;
+  }
+  tk = p - base;
 }
 
 template <int C, int RB, bool CAUSAL>
@@ -98,41 +112,58 @@ __global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a)
   const int b = rest / a.Hkv;
   const int h = g * G + hq_in;
   int tq, tk;
-  tile_pair(pair, CAUSAL, a.T, tq, tk);
+  tile_pair(pair, CAUSAL, a.Tq, a.Tk, a.c0, tq, tk);
 
   const size_t bh = (size_t)b * a.Hq + h, bg = (size_t)b * a.Hkv + g;
-  const uint16_t* qh = a.q + bh * a.M * C;
-  const uint16_t* kh = a.k + bg * a.M * C;
+  const uint16_t* qh = a.q + bh * a.Mq * C;
+  const uint16_t* kh = a.k + bg * a.Mk * C;
   const int i0 = tq * SC_TILE, j0 = tk * SC_TILE;  // strided row / key origin
   const int S = a.S;
   const int n_chunks = S * C / SC_KC;
 
   // global -> register staging: SC_TILE rows x SC_KC elements per operand.
   // Row pointers are formed once; per chunk only a uniform offset changes.
-  // Rows past R (a ragged last tile) are clamped to row R-1: they load valid
-  // memory and their outputs are never stored.
+  // Rows past the last strided row (a ragged last tile) are clamped to it: they
+  // load valid memory and their outputs are never stored.
   constexpr int LPT = SC_TILE * SC_CPR / SC_NT;  // 16-byte loads per thread per operand
   static_assert(LPT * SC_NT == SC_TILE * SC_CPR, "tile load must divide evenly");
   const uint16_t* kp[LPT];
   const uint16_t* qp[LPT];
+  int ktok[LPT], qtok[LPT];  // token of the row's first (Q) / base (K) element
 #pragma unroll
   for (int p = 0; p < LPT; ++p) {
     const int id = tid + SC_NT * p;
     const int row = id / SC_CPR, col = (id % SC_CPR) * 8;
-    const int j = min(j0 + row, a.R - 1), i = min(i0 + row, a.R - 1);
+    const int j = min(j0 + row, a.Rk - 1), i = min(i0 + row, a.Rq - 1);
     // antidiagonal: the stride group is read in reverse (row j*S + S-1-s)
-    kp[p] = kh + (size_t)(j * S + (a.diagonal ? 0 : S - 1)) * C + col;
-    qp[p] = qh + (size_t)(i * S) * C + col;
+    ktok[p] = j * S + (a.diagonal ? 0 : S - 1);
+    qtok[p] = i * S;
+    kp[p] = kh + (size_t)ktok[p] * C + col;
+    qp[p] = qh + (size_t)qtok[p] * C + col;
   }
   const int kdir = a.diagonal ? 1 : -1;
   typedef u32x4 Stage[2 * LPT];  // K chunks then Q chunks
   auto load_chunk = [&](int c, Stage& r) {
     const int srow = (SC_KC * c) / C, col0 = (SC_KC * c) % C;
     const int koff = kdir * srow * C + col0, qoff = srow * C + col0;
+    if (!a.tail) {
 #pragma unroll
-    for (int p = 0; p < LPT; ++p) {
-      r[p] = *reinterpret_cast<const u32x4*>(kp[p] + koff);
-      r[LPT + p] = *reinterpret_cast<const u32x4*>(qp[p] + qoff);
+      for (int p = 0; p < LPT; ++p) {
+        r[p] = *reinterpret_cast<const u32x4*>(kp[p] + koff);
+        r[LPT + p] = *reinterpret_cast<const u32x4*>(qp[p] + qoff);
+      }
+    } else {
+      // tokens past the end of a partial stride group read as zeros; the load
+      // address is pulled back to the last token, so it stays in bounds
+#pragma unroll
+      for (int p = 0; p < LPT; ++p) {
+        const int kover = max(0, ktok[p] + kdir * srow - (a.Mk - 1));
+        const int qover = max(0, qtok[p] + srow - (a.Mq - 1));
+        const u32x4 kv = *reinterpret_cast<const u32x4*>(kp[p] + koff - (ptrdiff_t)kover * C);
+        const u32x4 qv = *reinterpret_cast<const u32x4*>(qp[p] + qoff - (ptrdiff_t)qover * C);
+        r[p] = kover ? u32x4{0u, 0u, 0u, 0u} : kv;
+        r[LPT + p] = qover ? u32x4{0u, 0u, 0u, 0u} : qv;
+      }
     }
   };
   auto store_chunk = [&](int buf, const Stage& r) {
@@ -186,10 +217,11 @@ __global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a)
 
   // ---- epilogue: acc[x][y][r] is strided key j = j0 + 64wk + 32x + 8(r/4) + 4hh + r%4,
   //      strided query i = i0 + 64wq + 32y + l32. Reduce each run of RB keys.
-  float* wsh = a.ws + bh * (size_t)a.NB * a.R;
+  float* wsh = a.ws + bh * (size_t)a.NBq * a.NBk * RB;
 #pragma unroll
   for (int y = 0; y < 2; ++y) {
     const int i = i0 + 64 * wq + 32 * y + l32;
+    const int ia = i + a.qoff_s;  // absolute strided row
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
       const int jb = j0 + 64 * wk + 32 * x;  // first strided key of this 32-key sub-tile
@@ -198,7 +230,7 @@ __global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a)
       for (int r = 0; r < 16; ++r) {
         const int j = jb + 8 * (r >> 2) + 4 * hh + (r & 3);
         float xv = acc[x][y][r] * a.scale2;
-        if ((CAUSAL && j > i) || j >= a.R) xv = -INFINITY;
+        if ((CAUSAL && j > ia) || j >= a.Rk) xv = -INFINITY;
         v[r] = xv;
       }
       if constexpr (RB <= 4) {
@@ -216,7 +248,7 @@ __global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a)
           const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
           const int j = jb + 8 * (r0 >> 2) + 4 * hh + (r0 & 3);
           const int J = j / RB;
-          if (i < a.R && j < a.R) wsh[((size_t)(i / RB) * a.NB + J) * RB + i % RB] = Lv;
+          if (i < a.Rq && j < a.Rk) wsh[((size_t)(i / RB) * a.NBk + J) * RB + i % RB] = Lv;
         }
       } else {
         // a run of RB >= 8 keys = registers [4q .. 4q + RB/2) in both wave halves
@@ -236,7 +268,7 @@ __global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a)
           const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
           const int j = jb + 8 * (r0 >> 2);
           const int J = j / RB;
-          if (hh == 0 && i < a.R && j < a.R) wsh[((size_t)(i / RB) * a.NB + J) * RB + i % RB] = Lv;
+          if (hh == 0 && i < a.Rq && j < a.Rk) wsh[((size_t)(i / RB) * a.NBk + J) * RB + i % RB] = Lv;
         }
       }
     }
@@ -248,31 +280,34 @@ struct ScoreArgsF32 {
   const float* q;
   const float* k;
   float* ws;
-  int B, Hq, Hkv, M, C, S, R, NB, r, causal, diagonal;
+  int B, Hq, Hkv, Mq, Mk, C, S, Rq, Rk, NBq, NBk, r, qoff_s, causal, diagonal;
   float scale2;
 };
 
 __global__ __launch_bounds__(256) void score_partials_f32_kernel(ScoreArgsF32 a) {
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t per_head = (size_t)a.R * a.NB;
+  const size_t per_head = (size_t)a.Rq * a.NBk;
   const size_t total = per_head * a.B * a.Hq;
   if (gid >= total) return;
   const size_t bh = gid / per_head;
   const int rem = (int)(gid % per_head);
-  const int J = rem / a.R, i = rem % a.R;
+  const int J = rem / a.Rq, i = rem % a.Rq;
+  const int ia = i + a.qoff_s;  // absolute strided row
   const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
   const int g = h / (a.Hq / a.Hkv);
-  if (a.causal && J > i / a.r) return;   // never read by the finalize pass
-  const float* qh = a.q + bh * (size_t)a.M * a.C;
-  const float* kh = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.M * a.C;
+  if (a.causal && J > ia / a.r) return;   // never read by the finalize pass
+  const float* qh = a.q + bh * (size_t)a.Mq * a.C;
+  const float* kh = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.Mk * a.C;
   float m = -INFINITY, s = 0.f;
   for (int u = 0; u < a.r; ++u) {
     const int j = J * a.r + u;
-    if (a.causal && j > i) break;
+    if ((a.causal && j > ia) || j >= a.Rk) break;
     float dot = 0.f;
     for (int st = 0; st < a.S; ++st) {
-      const float* qr = qh + (size_t)(i * a.S + st) * a.C;
-      const float* kr = kh + (size_t)(j * a.S + (a.diagonal ? st : a.S - 1 - st)) * a.C;
+      const int qt = i * a.S + st, kt = j * a.S + (a.diagonal ? st : a.S - 1 - st);
+      if (qt >= a.Mq || kt >= a.Mk) continue;  // zero past the end of a stride group
+      const float* qr = qh + (size_t)qt * a.C;
+      const float* kr = kh + (size_t)kt * a.C;
       for (int c = 0; c < a.C; ++c) dot = fmaf(qr[c], kr[c], dot);
     }
     const float x = dot * a.scale2;
@@ -280,7 +315,7 @@ __global__ __launch_bounds__(256) void score_partials_f32_kernel(ScoreArgsF32 a)
     s = s * fast_exp2(m - mn) + fast_exp2(x - mn);
     m = mn;
   }
-  a.ws[bh * per_head + ((size_t)(i / a.r) * a.NB + J) * a.r + i % a.r] =
+  a.ws[bh * (size_t)a.NBq * a.NBk * a.r + ((size_t)(i / a.r) * a.NBk + J) * a.r + i % a.r] =
       (m == -INFINITY) ? -INFINITY : m + log2f(s);
 }
 
@@ -288,19 +323,20 @@ __global__ __launch_bounds__(256) void score_partials_f32_kernel(ScoreArgsF32 a)
 struct FinalizeArgs {
   const float* ws;
   float* out;
-  int B, Hq, R, NB, r, causal;
+  int B, Hq, Rq, NBq, NBk, qoff, r, causal;
 };
 
 template <int RB>
 __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
   __shared__ ScoreRowLds sh;
-  const size_t row = blockIdx.x;  // bh * NB + I
-  const int I = (int)(row % a.NB);
-  const size_t bh = row / a.NB;
-  const int n_cand = a.causal ? I + 1 : a.NB;
-  const float* L = a.ws + (bh * (size_t)a.NB + I) * (size_t)a.NB * RB;  // [J][t] of row I
-  float* orow = a.out + row * a.NB;
-  block_score_row<RB>(L, n_cand, a.NB, sh, [&](int J, float sc) { orow[J] = sc; });
+  const size_t row = blockIdx.x;  // bh * NBq + I
+  const int I = (int)(row % a.NBq);
+  const size_t bh = row / a.NBq;
+  const int n_cand = a.causal ? I + a.qoff + 1 : a.NBk;
+  const int rows = min(RB, a.Rq - I * RB);
+  const float* L = a.ws + (bh * (size_t)a.NBq + I) * (size_t)a.NBk * RB;  // [J][t] of row I
+  float* orow = a.out + row * a.NBk;
+  block_score_row<RB>(L, n_cand, a.NBk, rows, sh, [&](int J, float sc) { orow[J] = sc; });
 }
 
 // ------------------------------------------------------------------ launchers
@@ -329,11 +365,18 @@ static hipError_t launch_partials_c(const Shape& s, const ScoreArgs& a, hipStrea
 
 hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
                                       float score_scale, float* ws, hipStream_t st) {
-  const int R = s.R();
-  const int T = (R + SC_TILE - 1) / SC_TILE;
-  const int pairs = s.causal ? T * (T + 1) / 2 : T * T;
-  ScoreArgs a{q, k, ws, s.B, s.Hq, s.Hkv, s.M, s.stride, R, s.NB(), s.diagonal, T, pairs,
-              score_scale * kLog2e};
+  const int Rq = s.Rq(), Rk = s.Rk();
+  const int Tq = (Rq + SC_TILE - 1) / SC_TILE, Tk = (Rk + SC_TILE - 1) / SC_TILE;
+  const int qoff_s = (s.Mk - s.M) / s.stride;
+  const int c0 = (qoff_s + SC_TILE - 1) / SC_TILE;
+  int pairs = 0;
+  if (s.causal)
+    for (int tq = 0; tq < Tq; ++tq) pairs += std::min(Tk, tq + c0 + 1);
+  else
+    pairs = Tq * Tk;
+  const int tail = (s.M % s.stride) != 0 || (s.Mk % s.stride) != 0;
+  ScoreArgs a{q, k, ws, s.B, s.Hq, s.Hkv, s.M, s.Mk, s.stride, Rq, Rk, s.NBq(), s.NBk(), qoff_s,
+              s.diagonal, Tq, Tk, c0, pairs, tail, score_scale * kLog2e};
   if (s.C == 128) return launch_partials_c<128>(s, a, st);
   if (s.C == 64) return launch_partials_c<64>(s, a, st);
   return hipErrorInvalidValue;
@@ -341,9 +384,9 @@ hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const u
 
 hipError_t launch_score_partials_f32(const Shape& s, const float* q, const float* k,
                                      float score_scale, float* ws, hipStream_t st) {
-  ScoreArgsF32 a{q, k, ws, s.B, s.Hq, s.Hkv, s.M, s.C, s.stride, s.R(), s.NB(), s.r(),
-                 s.causal, s.diagonal, score_scale * kLog2e};
-  const size_t total = (size_t)s.R() * s.NB() * s.B * s.Hq;
+  ScoreArgsF32 a{q, k, ws, s.B, s.Hq, s.Hkv, s.M, s.Mk, s.C, s.stride, s.Rq(), s.Rk(), s.NBq(), s.NBk(),
+                 s.r(), (s.Mk - s.M) / s.stride, s.causal, s.diagonal, score_scale * kLog2e};
+  const size_t total = (size_t)s.Rq() * s.NBk() * s.B * s.Hq;
   hipLaunchKernelGGL(score_partials_f32_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
                      0, st, a);
   return hipGetLastError();
@@ -351,8 +394,8 @@ hipError_t launch_score_partials_f32(const Shape& s, const float* q, const float
 
 hipError_t launch_score_finalize(const Shape& s, const float* ws, float* block_scores,
                                  hipStream_t st) {
-  FinalizeArgs a{ws, block_scores, s.B, s.Hq, s.R(), s.NB(), s.r(), s.causal};
-  const dim3 grid((unsigned)((size_t)s.B * s.Hq * s.NB()));
+  FinalizeArgs a{ws, block_scores, s.B, s.Hq, s.Rq(), s.NBq(), s.NBk(), s.qoff(), s.r(), s.causal};
+  const dim3 grid((unsigned)((size_t)s.B * s.Hq * s.NBq()));
   switch (s.r()) {
     case 2: hipLaunchKernelGGL(score_finalize_kernel<2>, grid, dim3(256), 0, st, a); break;
     case 4: hipLaunchKernelGGL(score_finalize_kernel<4>, grid, dim3(256), 0, st, a); break;

@@ -2,8 +2,10 @@
 // key block) partial log2-sum-exps, shared by the score finalize pass and the
 // fused score+select kernel so both produce bit-identical scores.
 //
-// Row I's partials are L[J][t] (J < NB, t < RB); candidates are J < n_cand.
-// lse_t = log2 sum_J 2^L[J][t]; score[J] = (1/RB) sum_t 2^(L[J][t] - lse_t).
+// Row I's partials are L[J][t] (J < NB key blocks, t < RB); the first `rows`
+// strided rows are real (fewer than RB only in a partial last query block) and
+// candidates are J < n_cand.
+// lse_t = log2 sum_J 2^L[J][t]; score[J] = (1/rows) sum_{t<rows} 2^(L[J][t] - lse_t).
 // emit(J, score) is called once for every J in [0, NB) (0 for non-candidates).
 // Needs 256 threads and the given LDS scratch.
 #pragma once
@@ -19,8 +21,8 @@ struct ScoreRowLds {
 };
 
 template <int RB, class Emit>
-__device__ __forceinline__ void block_score_row(const float* L, int n_cand, int NB, ScoreRowLds& sh,
-                                                Emit&& emit) {
+__device__ __forceinline__ void block_score_row(const float* L, int n_cand, int NB, int rows,
+                                                ScoreRowLds& sh, Emit&& emit) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // pass 1: per strided row t, log2-sum-exp over candidate blocks
   float m[RB], s[RB];
@@ -30,7 +32,7 @@ __device__ __forceinline__ void block_score_row(const float* L, int n_cand, int 
     const float* p = L + (size_t)J * RB;
 #pragma unroll
     for (int t = 0; t < RB; ++t) {
-      const float x = p[t];
+      const float x = t < rows ? p[t] : -INFINITY;  // rows past the end were never written
       const float mn = fmaxf(m[t], x);
       if (mn != -INFINITY) {
         s[t] = s[t] * fast_exp2(m[t] - mn) + fast_exp2(x - mn);
@@ -65,14 +67,15 @@ __device__ __forceinline__ void block_score_row(const float* L, int n_cand, int 
     sh.lse[tid] = mt + log2f(stv);
   }
   __syncthreads();
-  // pass 2: block score = (1/r) sum_t 2^(L[J][t] - lse_t)
-  const float inv_r = 1.f / (float)RB;
+  // pass 2: block score = (1/rows) sum_t 2^(L[J][t] - lse_t)
+  const float inv_r = 1.f / (float)rows;
   for (int J = tid; J < NB; J += 256) {
     float sc = 0.f;
     if (J < n_cand) {
       const float* p = L + (size_t)J * RB;
 #pragma unroll
-      for (int t = 0; t < RB; ++t) sc += fast_exp2(p[t] - sh.lse[t]);
+      for (int t = 0; t < RB; ++t)
+        if (t < rows) sc += fast_exp2(p[t] - sh.lse[t]);
       sc *= inv_r;
     }
     emit(J, sc);

@@ -20,12 +20,14 @@
 
 namespace xattn {
 
+// Rows are (b, h, I) with I < NBq; row I's candidates are key blocks
+// J <= I + qoff (causal) or all J < NBk, and its diagonal block is I + qoff.
 struct SelectArgs {
   const float* scores;
   uint8_t* mask;
   int32_t* kv_idx;
   int32_t* kv_cnt;
-  int Hq, NB, causal;
+  int Hq, NBq, NBk, qoff, causal;
   TauArray tau;
 };
 
@@ -151,18 +153,19 @@ __device__ void select_from_keys(SelectLds& sh, int n, int npad, int NB, int I, 
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   __shared__ SelectLds sh;
   const int tid = threadIdx.x;
-  const size_t row = blockIdx.x;  // (b*Hq + h)*NB + I
-  const int I = (int)(row % a.NB);
-  const int h = (int)((row / a.NB) % a.Hq);
-  const int NB = a.NB;
-  const int n = a.causal ? I + 1 : NB;
+  const size_t row = blockIdx.x;  // (b*Hq + h)*NBq + I
+  const int I = (int)(row % a.NBq);
+  const int h = (int)((row / a.NBq) % a.Hq);
+  const int NB = a.NBk;
+  const int Ia = I + a.qoff;
+  const int n = a.causal ? Ia + 1 : NB;
   int npad = 1;
   while (npad < n) npad <<= 1;
   const float* srow = a.scores + row * NB;
   for (int p = tid; p < npad; p += 256) sh.keys[p] = p < n ? sel_key(srow[p], p) : 0;
   for (int p = tid; p < NB; p += 256) sh.flags[p] = 0;
   __syncthreads();
-  select_from_keys(sh, n, npad, NB, I, a.tau.v[h], row, a.mask, a.kv_idx, a.kv_cnt);
+  select_from_keys(sh, n, npad, NB, Ia, a.tau.v[h], row, a.mask, a.kv_idx, a.kv_cnt);
 }
 
 // Fused stage 2 + 3: the row's block scores are computed from the partials
@@ -174,7 +177,7 @@ struct FusedArgs {
   uint8_t* mask;
   int32_t* kv_idx;
   int32_t* kv_cnt;
-  int Hq, NB, causal;
+  int Hq, NBq, NBk, qoff, Rq, causal;
   TauArray tau;
 };
 
@@ -183,30 +186,32 @@ __global__ __launch_bounds__(256) void score_select_kernel(FusedArgs a) {
   __shared__ SelectLds sh;
   __shared__ ScoreRowLds shs;
   const int tid = threadIdx.x;
-  const size_t row = blockIdx.x;  // (b*Hq + h)*NB + I
-  const int I = (int)(row % a.NB);
-  const size_t bh = row / a.NB;
+  const size_t row = blockIdx.x;  // (b*Hq + h)*NBq + I
+  const int I = (int)(row % a.NBq);
+  const size_t bh = row / a.NBq;
   const int h = (int)(bh % a.Hq);
-  const int NB = a.NB;
-  const int n = a.causal ? I + 1 : NB;
+  const int NB = a.NBk;
+  const int Ia = I + a.qoff;
+  const int n = a.causal ? Ia + 1 : NB;
+  const int rows = min(RB, a.Rq - I * RB);
   int npad = 1;
   while (npad < n) npad <<= 1;
-  const float* L = a.ws + (bh * (size_t)NB + I) * (size_t)NB * RB;
+  const float* L = a.ws + (bh * (size_t)a.NBq + I) * (size_t)NB * RB;
   float* orow = a.scores + row * NB;
   for (int p = tid; p < NB; p += 256) sh.flags[p] = 0;
   for (int p = n + tid; p < npad; p += 256) sh.keys[p] = 0;
-  block_score_row<RB>(L, n, NB, shs, [&](int J, float sc) {
+  block_score_row<RB>(L, n, NB, rows, shs, [&](int J, float sc) {
     orow[J] = sc;
     if (J < n) sh.keys[J] = sel_key(sc, J);
   });
   __syncthreads();
-  select_from_keys(sh, n, npad, NB, I, a.tau.v[h], row, a.mask, a.kv_idx, a.kv_cnt);
+  select_from_keys(sh, n, npad, NB, Ia, a.tau.v[h], row, a.mask, a.kv_idx, a.kv_cnt);
 }
 
 hipError_t launch_score_select(const Shape& s, const float* ws, float* block_scores, const TauArray& tau,
                                uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st) {
-  FusedArgs a{ws, block_scores, mask, kv_idx, kv_cnt, s.Hq, s.NB(), s.causal, tau};
-  const dim3 grid((unsigned)((size_t)s.B * s.Hq * s.NB()));
+  FusedArgs a{ws, block_scores, mask, kv_idx, kv_cnt, s.Hq, s.NBq(), s.NBk(), s.qoff(), s.Rq(), s.causal, tau};
+  const dim3 grid((unsigned)((size_t)s.B * s.Hq * s.NBq()));
   switch (s.r()) {
     case 2: hipLaunchKernelGGL(score_select_kernel<2>, grid, dim3(256), 0, st, a); break;
     case 4: hipLaunchKernelGGL(score_select_kernel<4>, grid, dim3(256), 0, st, a); break;
@@ -220,8 +225,8 @@ hipError_t launch_score_select(const Shape& s, const float* ws, float* block_sco
 
 hipError_t launch_select(const Shape& s, const float* block_scores, const TauArray& tau,
                          uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st) {
-  SelectArgs a{block_scores, mask, kv_idx, kv_cnt, s.Hq, s.NB(), s.causal, tau};
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)((size_t)s.B * s.Hq * s.NB())), dim3(256), 0,
+  SelectArgs a{block_scores, mask, kv_idx, kv_cnt, s.Hq, s.NBq(), s.NBk(), s.qoff(), s.causal, tau};
+  hipLaunchKernelGGL(select_kernel, dim3((unsigned)((size_t)s.B * s.Hq * s.NBq())), dim3(256), 0,
                      st, a);
   return hipGetLastError();
 }
@@ -237,24 +242,24 @@ struct UnionArgs {
   uint8_t* mask;
   int32_t* kv_idx;
   int32_t* kv_cnt;
-  int Hq, Hkv, NB;
+  int Hq, Hkv, NBq, NBk;
 };
 
 __global__ __launch_bounds__(256) void gqa_union_kernel(UnionArgs a) {
   __shared__ uint8_t flags[SEL_MAX];
   __shared__ int wcnt[4];
   const int tid = threadIdx.x;
-  const int NB = a.NB;
-  const size_t gi = blockIdx.x;  // (b*Hkv + g)*NB + I
-  const int I = (int)(gi % NB);
-  const size_t bg = gi / NB;
+  const int NB = a.NBk;
+  const size_t gi = blockIdx.x;  // (b*Hkv + g)*NBq + I
+  const int I = (int)(gi % a.NBq);
+  const size_t bg = gi / a.NBq;
   const int g = (int)(bg % a.Hkv);
   const size_t b = bg / a.Hkv;
   const int G = a.Hq / a.Hkv;
   for (int p = tid; p < NB; p += 256) flags[p] = 0;
   __syncthreads();
   for (int s2 = 0; s2 < G; ++s2) {
-    const size_t row = (b * a.Hq + (size_t)(g * G + s2)) * NB + I;
+    const size_t row = (b * a.Hq + (size_t)(g * G + s2)) * a.NBq + I;
     int c = a.kv_cnt[row];
     c = c < 0 ? 0 : (c > NB ? NB : c);
     const int32_t* idx = a.kv_idx + row * NB;
@@ -265,15 +270,15 @@ __global__ __launch_bounds__(256) void gqa_union_kernel(UnionArgs a) {
   }
   __syncthreads();  // every sibling list is read before any is rewritten
   for (int s2 = 0; s2 < G; ++s2) {
-    const size_t row = (b * a.Hq + (size_t)(g * G + s2)) * NB + I;
+    const size_t row = (b * a.Hq + (size_t)(g * G + s2)) * a.NBq + I;
     compact_row(flags, NB, row, a.mask, a.kv_idx, a.kv_cnt, wcnt);
   }
 }
 
 hipError_t launch_gqa_union(const Shape& s, uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt,
                             hipStream_t st) {
-  UnionArgs a{mask, kv_idx, kv_cnt, s.Hq, s.Hkv, s.NB()};
-  hipLaunchKernelGGL(gqa_union_kernel, dim3((unsigned)((size_t)s.B * s.Hkv * s.NB())), dim3(256), 0,
+  UnionArgs a{mask, kv_idx, kv_cnt, s.Hq, s.Hkv, s.NBq(), s.NBk()};
+  hipLaunchKernelGGL(gqa_union_kernel, dim3((unsigned)((size_t)s.B * s.Hkv * s.NBq())), dim3(256), 0,
                      st, a);
   return hipGetLastError();
 }
@@ -282,10 +287,10 @@ hipError_t launch_gqa_union(const Shape& s, uint8_t* mask, int32_t* kv_idx, int3
 //
 // FlexPrefill rebuttal, "R Q3": the blocks of a head may be chosen globally,
 // over the flattened block-score matrix, rather than row by row. Per head, the
-// candidates (I, J) (J <= I when causal) are ordered by score descending, ties
-// by (I, J) row-major; the kept set is the shortest prefix whose mass reaches
-// tau * T (T = the head's candidate mass; tau >= 1 keeps all), plus the
-// diagonal blocks.
+// candidates (I, J) (J <= I + qoff when causal) are ordered by score
+// descending, ties by (I, J) row-major; the kept set is the shortest prefix
+// whose mass reaches tau * T (T = the head's candidate mass; tau >= 1 keeps
+// all), plus the diagonal blocks (I, I + qoff).
 //
 // Implementation: a radix select on the score bits (non-negative floats order
 // like their bit patterns). Three histogram passes over bits [31:20], [19:8]
@@ -326,8 +331,8 @@ struct GselArgs {
   int32_t* kv_cnt;
   GselHead* head;   // [B*Hq]
   GselHist* hist;   // [B*Hq]
-  uint32_t* tieoff; // [B*Hq][NB]: ties at v* in the rows before I
-  int Hq, NB, causal;
+  uint32_t* tieoff; // [B*Hq][NBq]: ties at v* in the rows before I
+  int Hq, NBq, NBk, qoff, causal;
   TauArray tau;
 };
 
@@ -346,7 +351,7 @@ struct GselLevel {
 size_t select_workspace_bytes(const Shape& s, int mode) {
   if (mode != SEL_GLOBAL) return 0;
   const size_t heads = (size_t)s.B * s.Hq;
-  return heads * (sizeof(GselHead) + sizeof(GselHist) + sizeof(uint32_t) * (size_t)s.NB());
+  return heads * (sizeof(GselHead) + sizeof(GselHist) + sizeof(uint32_t) * (size_t)s.NBq());
 }
 
 // Clears the head records and histograms of a global selection.
@@ -369,12 +374,12 @@ __global__ __launch_bounds__(256) void gsel_hist_kernel(GselArgs a) {
     cnt[b] = 0u;
   }
   __syncthreads();
-  const int NB = a.NB;
+  const int NB = a.NBk;
   const int I0 = blockIdx.x * GSEL_ROWS_PER_WG;
-  const int I1 = min(I0 + GSEL_ROWS_PER_WG, NB);
+  const int I1 = min(I0 + GSEL_ROWS_PER_WG, a.NBq);
   for (int I = I0; I < I1; ++I) {
-    const int n = a.causal ? I + 1 : NB;
-    const float* srow = a.scores + (bh * NB + I) * (size_t)NB;
+    const int n = a.causal ? I + a.qoff + 1 : NB;
+    const float* srow = a.scores + (bh * a.NBq + I) * (size_t)NB;
     for (int J = tid; J < n; J += 256) {
       const float sc = srow[J];
       const uint32_t key = __float_as_uint(sc);
@@ -476,17 +481,17 @@ __global__ __launch_bounds__(256) void gsel_ties_kernel(GselArgs a) {
   const GselHead* st = a.head + bh;
   if (st->mode != 0 || st->count_v <= st->need_ties) return;  // uniform
   const uint32_t vstar = st->vstar;
-  const int NB = a.NB;
+  const int NB = a.NBk;
   uint32_t run = 0u;
-  for (int I = 0; I < NB; ++I) {
-    const int n = a.causal ? I + 1 : NB;
-    const float* srow = a.scores + (bh * NB + I) * (size_t)NB;
+  for (int I = 0; I < a.NBq; ++I) {
+    const int n = a.causal ? I + a.qoff + 1 : NB;
+    const float* srow = a.scores + (bh * a.NBq + I) * (size_t)NB;
     int c = 0;
     for (int J = tid; J < n; J += 256) c += __float_as_uint(srow[J]) == vstar;
     c = wave_incl_scan_i(c, lane);
     if (lane == 63) wsum[wave] = (uint32_t)c;
     __syncthreads();
-    if (tid == 0) a.tieoff[bh * NB + I] = run;
+    if (tid == 0) a.tieoff[bh * a.NBq + I] = run;
     run += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
@@ -496,15 +501,16 @@ __global__ __launch_bounds__(256) void gsel_compact_kernel(GselArgs a) {
   __shared__ uint8_t flags[SEL_MAX];
   __shared__ int wcnt[4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int NB = a.NB;
-  const size_t row = blockIdx.x;  // (b*Hq + h)*NB + I
-  const int I = (int)(row % NB);
-  const size_t bh = row / NB;
+  const int NB = a.NBk;
+  const size_t row = blockIdx.x;  // (b*Hq + h)*NBq + I
+  const int I = (int)(row % a.NBq);
+  const size_t bh = row / a.NBq;
   const GselHead* st = a.head + bh;
   const int mode = st->mode;
   const uint32_t vstar = st->vstar, need = st->need_ties;
   const bool all_ties = st->count_v <= need;
-  const int n = a.causal ? I + 1 : NB;
+  const int Ia = I + a.qoff;
+  const int n = a.causal ? Ia + 1 : NB;
   const float* srow = a.scores + row * NB;
   // per-thread contiguous runs of J, so tie ranks follow ascending J
   const int per = (NB + 255) / 256;
@@ -533,7 +539,7 @@ __global__ __launch_bounds__(256) void gsel_compact_kernel(GselArgs a) {
       if (flags[p] == 2) flags[p] = rank++ < need ? 1 : 0;
   }
   __syncthreads();
-  if (tid == 0) flags[I] = 1;  // diagonal block
+  if (tid == 0) flags[Ia] = 1;  // diagonal block
   __syncthreads();
   compact_row(flags, NB, row, a.mask, a.kv_idx, a.kv_cnt, wcnt);
 }
@@ -542,17 +548,17 @@ hipError_t launch_select_global(const Shape& s, const float* block_scores, const
                                 uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, void* ws,
                                 hipStream_t st) {
   const size_t heads = (size_t)s.B * s.Hq;
-  const int NB = s.NB();
+  const int NBq = s.NBq();
   char* base = static_cast<char*>(ws);
   GselArgs a{block_scores, mask, kv_idx, kv_cnt,
              reinterpret_cast<GselHead*>(base),
              reinterpret_cast<GselHist*>(base + heads * sizeof(GselHead)),
              reinterpret_cast<uint32_t*>(base + heads * (sizeof(GselHead) + sizeof(GselHist))),
-             s.Hq, NB, s.causal, tau};
+             s.Hq, NBq, s.NBk(), s.qoff(), s.causal, tau};
   const size_t clear_words = heads * (sizeof(GselHead) + sizeof(GselHist)) / 4;
   hipLaunchKernelGGL(gsel_clear_kernel, dim3(256), dim3(256), 0, st,
                      reinterpret_cast<uint32_t*>(base), clear_words);
-  const dim3 hgrid((unsigned)((NB + GSEL_ROWS_PER_WG - 1) / GSEL_ROWS_PER_WG), (unsigned)heads);
+  const dim3 hgrid((unsigned)((NBq + GSEL_ROWS_PER_WG - 1) / GSEL_ROWS_PER_WG), (unsigned)heads);
   hipLaunchKernelGGL(gsel_hist_kernel<0>, hgrid, dim3(256), 0, st, a);
   hipLaunchKernelGGL(gsel_find_kernel<0>, dim3((unsigned)heads), dim3(256), 0, st, a);
   hipLaunchKernelGGL(gsel_hist_kernel<1>, hgrid, dim3(256), 0, st, a);
@@ -560,7 +566,7 @@ hipError_t launch_select_global(const Shape& s, const float* block_scores, const
   hipLaunchKernelGGL(gsel_hist_kernel<2>, hgrid, dim3(256), 0, st, a);
   hipLaunchKernelGGL(gsel_find_kernel<2>, dim3((unsigned)heads), dim3(256), 0, st, a);
   hipLaunchKernelGGL(gsel_ties_kernel, dim3((unsigned)heads), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(gsel_compact_kernel, dim3((unsigned)(heads * NB)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(gsel_compact_kernel, dim3((unsigned)(heads * NBq)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -20,12 +20,22 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - Q is (B, Hq, M, C); K and V are (B, Hkv, M, C); O has Q's shape. All are
- *    contiguous row-major DEVICE buffers of the problem dtype. Query head h
- *    reads KV head h / (Hq / Hkv) (grouped-query attention).
- *  - Block size Bk = p->block, stride S = p->stride, NB = M / Bk blocks,
- *    R = M / S strided rows, r = Bk / S strided rows per block.
- *  - Block tensors are (B, Hq, NB, NB) row-major, indexed [b][h][I][J]
+ *  - Q is (B, Hq, M, C); K and V are (B, Hkv, Mk, C) with Mk = p->Mk (0 means
+ *    M); O has Q's shape. All are contiguous row-major DEVICE buffers of the
+ *    problem dtype. Query head h reads KV head h / (Hq / Hkv) (grouped-query
+ *    attention).
+ *  - Chunked prefill: the queries are the last M of the Mk tokens, so query i
+ *    sits at position off + i, off = Mk - M (0 for a plain prefill); off must
+ *    be a multiple of the block size.
+ *  - Block size Bk = p->block, stride S = p->stride, r = Bk / S strided rows
+ *    per block; NBq = ceil(M / Bk) query blocks and NBk = ceil(Mk / Bk) key
+ *    blocks; query block I is key block I + off / Bk ("its diagonal").
+ *  - Lengths need not be multiples of S or Bk ([DuSA] rebuttal, Response to
+ *    Q1: padding makes the length divisible by the block size): the missing
+ *    tokens of a partial stride group count as zero vectors in the scoring,
+ *    keys past the end take no part in any softmax, and query rows past the end
+ *    of a partial last block are not written.
+ *  - Block tensors are (B, Hq, NBq, NBk) row-major, indexed [b][h][I][J]
  *    (query block I, key block J).
  *  - The caller owns and allocates every buffer. The library keeps no state,
  *    never allocates, and is re-entrant; scratch memory comes only through
@@ -43,8 +53,8 @@
  *
  * Supported shapes: dtype XATTN_BF16 or XATTN_F32; C in {64, 128};
  * block in {64, 128}; r = block/stride in {2, 4, 8, 16, 32};
- * M a positive multiple of block with NB <= 4096; 1 <= Hq <= 256;
- * Hq a multiple of Hkv; causal in {0, 1}.
+ * 1 <= M <= Mk with Mk - M a multiple of block and NBk <= 4096;
+ * 1 <= Hq <= 256; Hq a multiple of Hkv; causal in {0, 1}.
  */
 #ifndef XATTN_H
 #define XATTN_H
@@ -78,7 +88,7 @@ typedef struct {
   int32_t B;      /* batch */
   int32_t Hq;     /* query heads */
   int32_t Hkv;    /* key/value heads, divides Hq */
-  int32_t M;      /* sequence length (queries = keys) */
+  int32_t M;      /* query length (= key length unless Mk says otherwise) */
   int32_t C;      /* head dimension */
   int32_t block;  /* block size Bk (queries and keys) */
   int32_t stride; /* antidiagonal stride S, divides block */
@@ -86,7 +96,7 @@ typedef struct {
   int32_t dtype;  /* xattn_dtype of Q, K, V and O */
   int32_t pattern; /* xattn_pattern of the strided scoring (0 = antidiagonal) */
   int32_t selection; /* xattn_selection of the block selection (0 = per row) */
-  int32_t Mk;     /* key length; 0 or M (the only value supported) */
+  int32_t Mk;     /* key length; 0 means M. Mk - M is a multiple of block */
 } xattn_problem;
 
 /* Which line of each stride x stride tile the scoring sums:
@@ -121,24 +131,26 @@ const char* xattn_last_error(void);
 
 /* Device workspace bytes xattn_score needs for problem p;
  * 0 if p is invalid. The workspace holds per-(strided row, key block) partial
- * log-sum-exp values: B*Hq*NB*R float32. */
+ * log-sum-exp values: B*Hq*NBq*NBk*r float32. */
 size_t xattn_score_workspace_bytes(const xattn_problem* p);
 
 /*
  * Stage 1+2 — strided antidiagonal block scores ([XA-abs]; [XA-sum] Approach;
  * [DuSA] Response to Q2).
  *
- * For strided query row i and strided key row j (i, j < R):
+ * For strided query row i < ceil(M/S) and strided key row j < ceil(Mk/S):
  *   A'[i][j] = sum_{s<S} dot(q[i*S+s], k[j*S+S-1-s]),  logit = score_scale*A'
- * (k[j*S+s] instead for p->pattern = XATTN_DIAGONAL).
- * Causal problems keep j <= i. Each strided row is softmax-normalised over its
- * keys, and the probabilities are summed over each r x r tile:
- *   block_scores[b][h][I][J] = (1/r) * sum_{i in I, j in J} softmax_j(logit[i][j]).
- * Every row of block_scores sums to 1; causal entries with J > I are 0.
+ * (k[j*S+s] instead for p->pattern = XATTN_DIAGONAL; tokens past the end are
+ * zero). Causal problems keep j <= i + off/S. Each strided row is
+ * softmax-normalised over its keys, and the probabilities are summed over each
+ * r x r tile:
+ *   block_scores[b][h][I][J] = (1/r_I) * sum_{i in I, j in J} softmax_j(logit[i][j]),
+ * r_I = the strided rows of query block I (r unless I is a partial last block).
+ * Every row of block_scores sums to 1; causal entries with J > I + off/Bk are 0.
  *
  *  q, k          device, problem dtype, layouts above.
  *  score_scale   > 0 and finite (e.g. 1/(S*sqrt(C)): the mean antidiagonal logit).
- *  block_scores  device float32 (B, Hq, NB, NB), fully written.
+ *  block_scores  device float32 (B, Hq, NBq, NBk), fully written.
  *  ws, ws_bytes  device scratch of at least xattn_score_workspace_bytes(p).
  */
 xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k,
@@ -146,7 +158,7 @@ xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k,
                          size_t ws_bytes, void* stream);
 
 /* Device workspace bytes xattn_select needs: 0 for ROW and GQA_UNION; for
- * GLOBAL, per head a 64-byte state, a 48 KiB mass histogram and NB words. */
+ * GLOBAL, per head a 64-byte state, a 48 KiB mass histogram and NBq words. */
 size_t xattn_select_workspace_bytes(const xattn_problem* p);
 
 /*
@@ -154,20 +166,21 @@ size_t xattn_select_workspace_bytes(const xattn_problem* p);
  * set of blocks whose normalised mass exceeds the per-head threshold;
  * [Flex] R Q3: minimal |S| under the cumulative-mass constraint).
  *
- * Per row (b, h, I): candidates are J <= I (causal) or all J. They are ordered
- * by score descending, ties by J ascending; with prefix masses c_k (float64)
- * and total T = c_n, the kept set is the first k* = min{k >= 0 : c_k >= tau_h*T}
- * candidates (tau_h >= 1 keeps all). The diagonal block J = I is then added.
+ * Per row (b, h, I): candidates are J <= I + off/Bk (causal) or all J < NBk.
+ * They are ordered by score descending, ties by J ascending; with prefix
+ * masses c_k (float64) and total T = c_n, the kept set is the first
+ * k* = min{k >= 0 : c_k >= tau_h*T} candidates (tau_h >= 1 keeps all). The
+ * diagonal block J = I + off/Bk is then added.
  * p->selection picks the GLOBAL or GQA_UNION variant instead (see
  * xattn_selection); GLOBAL sums fixed-point masses (score * 2^50, exact and
  * order-independent) instead of float64 prefixes.
  *
- *  block_scores  device float32 (B, Hq, NB, NB), as written by xattn_score.
+ *  block_scores  device float32 (B, Hq, NBq, NBk), as written by xattn_score.
  *  tau           HOST array of Hq floats, each in [0, 1] (copied at the call).
- *  mask          device uint8 (B, Hq, NB, NB) or NULL; 1 = kept.
- *  kv_idx        device int32 (B, Hq, NB, NB): per row the kept J in ascending
- *                order; only the first kv_cnt entries of a row are written.
- *  kv_cnt        device int32 (B, Hq, NB): kept blocks per row (>= 1).
+ *  mask          device uint8 (B, Hq, NBq, NBk) or NULL; 1 = kept.
+ *  kv_idx        device int32 (B, Hq, NBq, NBk): per row the kept J in
+ *                ascending order; only the first kv_cnt entries are written.
+ *  kv_cnt        device int32 (B, Hq, NBq): kept blocks per row (>= 1).
  *  ws, ws_bytes  device scratch of xattn_select_workspace_bytes(p) (may be
  *                NULL when that is 0).
  */
@@ -185,12 +198,13 @@ size_t xattn_attn_workspace_bytes(const xattn_problem* p);
  *
  * For query i in block I of head h:
  *   O[i] = sum_{j in A(i)} softmax_j(sm_scale * q_i . k_j) v_j,
- *   A(i) = union of key blocks kv_idx[b][h][I][0 .. kv_cnt-1], intersected
- *          with j <= i when causal.
+ *   A(i) = union of key blocks kv_idx[b][h][I][0 .. kv_cnt-1], restricted to
+ *          keys j < Mk, and to j <= off + i when causal.
  *
  *  kv_idx, kv_cnt  device int32 as produced by xattn_select; each listed J
- *                  must be in [0, NB) (and <= I when causal), kv_cnt in
- *                  [1, NB], and for causal problems the list must hold J = I.
+ *                  must be in [0, NBk) (and <= I + off/Bk when causal), kv_cnt
+ *                  in [1, NBk], and for causal problems the list must hold the
+ *                  diagonal J = I + off/Bk.
  *  sm_scale        > 0 and finite (usually 1/sqrt(C)).
  *  out             device, problem dtype, (B, Hq, M, C).
  *  lse             device float32 (B, Hq, M), natural-log log-sum-exp of the
@@ -205,7 +219,8 @@ xattn_status bsa_fwd(const xattn_problem* p, const void* q, const void* k,
 
 /*
  * Dense attention forward: bsa_fwd with every candidate block kept (all
- * J <= I when causal, all J otherwise). The reference point for speedups.
+ * J <= I + off/Bk when causal, all J otherwise). The reference point for
+ * speedups.
  */
 xattn_status dense_fwd(const xattn_problem* p, const void* q, const void* k,
                        const void* v, float sm_scale, void* out, float* lse,

@@ -51,17 +51,27 @@ FAKE = 0x1000  # never dereferenced: validation fails first
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(Hkv=3), 2), (dict(M=1000), 2), (dict(stride=3), 2), (dict(C=96), 5),
+    (dict(Hkv=3), 2), (dict(Mk=1000), 2), (dict(Mk=1100), 2), (dict(stride=3), 2), (dict(C=96), 5),
     (dict(block=32, stride=4), 5), (dict(stride=128), 5), (dict(stride=1), 5),
     (dict(dtype=7), 3), (dict(causal=2), 4), (dict(Hq=512, Hkv=1), 5), (dict(B=0), 2),
     (dict(M=4096 * 128 * 2), 5), (dict(pattern=2), 4), (dict(pattern=-1), 4),
-    (dict(selection=3), 4), (dict(selection=-1), 4), (dict(Mk=2048), 5),
+    (dict(selection=3), 4), (dict(selection=-1), 4), (dict(Mk=4096 * 128 + 128), 5),
 ])
 def test_score_rejects_bad_problems(xa, kw, status):
     p = _p(xa, **kw)
     rc = xa._lib.xattn_score(ctypes.byref(p), FAKE, FAKE, 0.01, FAKE, FAKE, 1 << 40, None)
     assert rc == status, xa._lib.xattn_last_error()
     assert xa._lib.xattn_last_error()
+
+
+def test_ragged_and_chunked_problems_validate(xa):
+    # lengths off the block and stride grid, and queries that are the last M of
+    # Mk tokens, are valid; the workspace follows NBq x NBk
+    for kw, nbq, nbk in ((dict(M=1000), 8, 8), (dict(M=1000, Mk=1256), 8, 10),
+                         (dict(M=1, Mk=129), 1, 2), (dict(M=128, Mk=4096 * 128), 1, 4096)):
+        p = _p(xa, **kw)
+        assert xa.workspace_bytes(p) == 4 * nbq * nbk * 16 * 4, kw
+        assert xa.attn_workspace_bytes(p) == 1024
 
 
 def test_workspace_bytes(xa):
