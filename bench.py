@@ -234,7 +234,8 @@ def cpu_baseline(wl, torch, res, budget_s):
 
 def run_variants(xa, torch, head, steps):
     """The headline layer through xattn_prefill with each method variant:
-    global and GQA-union selection, and the diagonal scoring pattern."""
+    global and GQA-union selection, the diagonal scoring pattern, a chunked
+    prefill step and a ragged length."""
     w = head["workload"]
     q, k, v, tau = head["_tensors"][:4]
     sscale, smscale = 1.0 / (w.stride * math.sqrt(w.C)), 1.0 / math.sqrt(w.C)
@@ -263,6 +264,41 @@ def run_variants(xa, torch, head, steps):
                       "dense_equiv_tflops": round(w.dense_flops / ms / 1e9, 2)}
         log(f"[{w.name}] variant {label}: {ms:.3f} ms, density {dens * 100:.2f}%")
         del bufs
+        torch.cuda.empty_cache()
+    # chunked prefill (the last 32K queries against the whole context) and a
+    # ragged length (not a multiple of the block or the stride)
+    chunk = min(32768, w.M // 2)
+    for label, mq, mk in ((f"chunk_last{chunk // 1024}k", chunk, w.M), ("ragged_" + str(w.M - 12101), w.M - 12101,
+                                                                        w.M - 12101)):
+        qv = q[:, :, mk - mq:mk].contiguous()
+        kv = k[:, :, :mk].contiguous()
+        vv = v[:, :, :mk].contiguous()
+        bufs = xa.PrefillBuffers(qv, kv, w.block, w.stride, w.causal, want_mask=False)
+
+        def step():
+            xa.xattn_prefill(qv, kv, vv, tau, w.block, w.stride, sscale, smscale, w.causal, buffers=bufs)
+
+        step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        nbq, nbk = -(-mq // w.block), -(-mk // w.block)
+        qoff = nbk - nbq
+        cand_v = w.B * w.Hq * (sum(i + qoff + 1 for i in range(nbq)) if w.causal else nbq * nbk)
+        dens = float(bufs.kv_cnt.sum().item()) / cand_v
+        off = mk - mq
+        pairs = mq * off + mq * (mq + 1) / 2 if w.causal else mq * mk
+        flops = 4.0 * w.B * w.Hq * w.C * pairs
+        res[label] = {"ms": round(ms, 4), "density": round(dens, 5), "Mq": mq, "Mk": mk,
+                      "dense_equiv_tflops": round(flops / ms / 1e9, 2)}
+        log(f"[{w.name}] variant {label} (Mq={mq}, Mk={mk}): {ms:.3f} ms, density {dens * 100:.2f}%")
+        del bufs, qv, kv, vv
         torch.cuda.empty_cache()
     return res
 

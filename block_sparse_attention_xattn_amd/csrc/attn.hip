@@ -125,7 +125,9 @@ struct AttnItems {
 // One work item: all rows of the slots it covers, from the block list to the
 // normalised output. Starts and ends with every wave of the workgroup past a
 // barrier after its last LDS read, so consecutive items may reuse the LDS.
-template <int C, int BLK, bool CAUSAL, bool SPARSE, int MODE>
+// KTAIL: the last key block is partial (Mk % BLK != 0): key rows past the end
+// are clamped on load and masked out of the softmax.
+template <int C, int BLK, bool CAUSAL, bool SPARSE, int MODE, bool KTAIL>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item,
                                           unsigned char* smem, int* scan_s) {
   using L = AttnLds<C>;
@@ -293,7 +295,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
       const int row = c / (C / 8), col = (c % (C / 8)) * 8;
       // keys past the end (a partial last block) load the last key; they are
       // masked out of the softmax
-      const size_t kr = (size_t)min(k0 + row, a.Mk - 1);
+      const size_t kr = KTAIL ? (size_t)min(k0 + row, a.Mk - 1) : (size_t)(k0 + row);
       r[p] = *reinterpret_cast<const u32x4*>(kh + kr * C + col);
       r[PER_T + p] = *reinterpret_cast<const u32x4*>(vh + kr * C + col);
     }
@@ -312,7 +314,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   auto compute = [&](int t, int buf) {
     const int k0 = key_start(t);
     if (CAUSAL && (k0 > qa0 + 31)) return;      // whole sub-tile above this wave's rows
-    if (k0 >= a.Mk) return;                     // whole sub-tile past the last key
+    if (KTAIL && k0 >= a.Mk) return;            // whole sub-tile past the last key
     if (!mine_tile(t)) return;                  // selected only by the other head
     const unsigned char* Kb = Ks + buf * L::TILE_B;
     const unsigned char* Vb = Vs + buf * L::TILE_B;
@@ -339,9 +341,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
         for (int n = 0; n < 2; ++n) sacc[n] = mfma32x32x16(ka[u][n], qf[k0b + u], sacc[n]);
     }
     if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-    if ((CAUSAL && (k0 + L::KT - 1 > qa0)) || k0 + L::KT > a.Mk) {
+    if ((CAUSAL && (k0 + L::KT - 1 > qa0)) || (KTAIL && k0 + L::KT > a.Mk)) {
       const int qi = qa0 + l32;
-      const int kmax = CAUSAL ? min(qi, a.Mk - 1) : a.Mk - 1;  // last visible key
+      const int kmax = !KTAIL ? qi : (CAUSAL ? min(qi, a.Mk - 1) : a.Mk - 1);  // last visible key
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
@@ -490,7 +492,7 @@ __device__ __forceinline__ uint32_t claim_item(uint32_t* queue, const uint32_t n
 // one-workgroup-per-item launch parks the long rows of a dense head on one
 // engine and stalls the others behind it. Pulling from a queue keeps every
 // workgroup slot busy until the queues run dry.
-template <int C, int BLK, bool CAUSAL, bool SPARSE, int MODE>
+template <int C, int BLK, bool CAUSAL, bool SPARSE, int MODE, bool KTAIL>
 __global__ __launch_bounds__(BLK * 2 * AttnMode<MODE>::SLOTS, MODE == MODE_SINGLE ? 2 : 1)
 void attn_fwd_bf16_kernel(AttnArgs a) {
   using L = AttnLds<C>;
@@ -500,7 +502,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   __shared__ int scan_s[SLOTS > 1 ? NT / 64 : 1];
   const AttnItems its(a, MODE);
   if constexpr (!SPARSE) {
-    attn_item<C, BLK, CAUSAL, SPARSE, MODE>(a, xcd_map(blockIdx.x, its.n, its.GW, 0), smem, scan_s);
+    attn_item<C, BLK, CAUSAL, SPARSE, MODE, KTAIL>(a, xcd_map(blockIdx.x, its.n, its.GW, 0), smem, scan_s);
   } else {
     __shared__ uint32_t item_s;
     const uint32_t K = XATTN_SPARSE_GROUP_ON_XCD ? its.GW : 1;
@@ -513,7 +515,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
       if (item == kNoItem) break;  // uniform over the workgroup
       // every thread reads item_s before the barriers inside attn_item, and
       // thread 0 rewrites it only after them
-      attn_item<C, BLK, CAUSAL, SPARSE, MODE>(a, item, smem, scan_s);
+      attn_item<C, BLK, CAUSAL, SPARSE, MODE, KTAIL>(a, item, smem, scan_s);
     }
   }
 }
@@ -601,8 +603,8 @@ static int resident_workgroups(Kern kern, int threads) {
   return cus * per_cu;
 }
 
-template <int C, int BLK, int MODE>
-static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t st) {
+template <int C, int BLK, int MODE, bool KTAIL>
+static hipError_t launch_bf16_cbmt(const Shape& s, const AttnArgs& a, hipStream_t st) {
   const int G = s.Hq / s.Hkv;
   const int NP = MODE == MODE_ROWS ? (s.NBq() + 1) / 2 : s.NBq();
   const int GW = MODE == MODE_SIBLINGS ? G / 2 : G;
@@ -611,14 +613,14 @@ static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t
   if (a.kv_idx == nullptr) {
     const dim3 grid((unsigned)n_items);
     if (s.causal)
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, false, MODE>), grid, dim3(threads), 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, false, MODE, KTAIL>), grid, dim3(threads), 0, st, a);
     else
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, false, MODE>), grid, dim3(threads), 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, false, MODE, KTAIL>), grid, dim3(threads), 0, st, a);
     return hipGetLastError();
   }
   if (a.queue == nullptr) return hipErrorInvalidValue;
-  auto kern = s.causal ? attn_fwd_bf16_kernel<C, BLK, true, true, MODE>
-                       : attn_fwd_bf16_kernel<C, BLK, false, true, MODE>;
+  auto kern = s.causal ? attn_fwd_bf16_kernel<C, BLK, true, true, MODE, KTAIL>
+                       : attn_fwd_bf16_kernel<C, BLK, false, true, MODE, KTAIL>;
   const int slots = resident_workgroups(kern, threads);
   if (slots <= 0) return hipErrorInvalidDeviceFunction;
   hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(kQueueWords), 0, st, a.queue);
@@ -627,6 +629,12 @@ static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t
   const dim3 grid((unsigned)(n_items < (size_t)slots ? n_items : (size_t)slots));
   hipLaunchKernelGGL(kern, grid, dim3(threads), 0, st, a);
   return hipGetLastError();
+}
+
+template <int C, int BLK, int MODE>
+static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t st) {
+  return s.Mk % BLK ? launch_bf16_cbmt<C, BLK, MODE, true>(s, a, st)
+                    : launch_bf16_cbmt<C, BLK, MODE, false>(s, a, st);
 }
 
 // 128-row blocks: dense attention pairs GQA siblings (identical block lists)

@@ -74,23 +74,33 @@ __device__ __forceinline__ int sc_off(int row, int chunk) {
 
 // Tile pair p of a head -> (query tile, key tile). Causal: query tile tq meets
 // key tiles 0 .. min(Tk - 1, tq + c0), a trapezoid (a triangle when the
-// queries start at the first token); the row walk is at most Tq steps.
+// queries start at the first token): rows tq < cap hold tq + c0 + 1 pairs
+// (cap = Tk - c0 - 1, the first row that reaches Tk), the rest Tk each.
 __device__ __forceinline__ void tile_pair(int p, bool causal, int Tq, int Tk, int c0, int& tq, int& tk) {
   if (!causal) {
     tq = p / Tk;
     tk = p % Tk;
     return;
   }
-  int base = 0;
-  for (tq = 0; tq < Tq - 1; ++tq) {
-    const int n = min(Tk, tq + c0 + 1);
-    if (p < base + n) break;
-    base += n;
+  const int cap = max(0, min(Tq, Tk - c0 - 1));
+  const int p1 = cap * (cap + 1) / 2 + c0 * cap;  // pairs in the rows below cap
+  if (p >= p1) {
+    tq = cap + (p - p1) / Tk;
+    tk = (p - p1) % Tk;
+    return;
   }
-  tk = p - base;
+  // largest x with x (x + 1) / 2 + c0 x <= p
+  const float b = 2.f * (float)c0 + 1.f;
+  int x = (int)((sqrtf(b * b + 8.f * (float)p) - b) * 0.5f);
+  while ((x + 1) * (x + 2) / 2 + c0 * (x + 1) <= p) ++x;
+  while (x * (x + 1) / 2 + c0 * x > p) --x;
+  tq = x;
+  tk = p - (x * (x + 1) / 2 + c0 * x);
 }
 
-template <int C, int RB, bool CAUSAL>
+// TAIL: Mq or Mk is not a multiple of S, so the last stride group of Q or K is
+// partial (a separate instantiation keeps the common loop branch-free).
+template <int C, int RB, bool CAUSAL, bool TAIL>
 __global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a) {
   static_assert(RB == 2 || RB == 4 || RB == 8 || RB == 16 || RB == 32, "r");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * SC_OP];
@@ -146,7 +156,7 @@ __global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a)
   auto load_chunk = [&](int c, Stage& r) {
     const int srow = (SC_KC * c) / C, col0 = (SC_KC * c) % C;
     const int koff = kdir * srow * C + col0, qoff = srow * C + col0;
-    if (!a.tail) {
+    if constexpr (!TAIL) {
 #pragma unroll
       for (int p = 0; p < LPT; ++p) {
         r[p] = *reinterpret_cast<const u32x4*>(kp[p] + koff);
@@ -341,14 +351,19 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
 
 // ------------------------------------------------------------------ launchers
 
-template <int C, int RB>
-static hipError_t launch_partials_cr(const Shape& s, const ScoreArgs& a, hipStream_t st) {
+template <int C, int RB, bool TAIL>
+static hipError_t launch_partials_crt(const Shape& s, const ScoreArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((size_t)s.B * s.Hq * a.pairs);
   if (s.causal)
-    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, true>), dim3(grid), dim3(SC_NT), 0, st, a);
+    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, true, TAIL>), dim3(grid), dim3(SC_NT), 0, st, a);
   else
-    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, false>), dim3(grid), dim3(SC_NT), 0, st, a);
+    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, false, TAIL>), dim3(grid), dim3(SC_NT), 0, st, a);
   return hipGetLastError();
+}
+
+template <int C, int RB>
+static hipError_t launch_partials_cr(const Shape& s, const ScoreArgs& a, hipStream_t st) {
+  return a.tail ? launch_partials_crt<C, RB, true>(s, a, st) : launch_partials_crt<C, RB, false>(s, a, st);
 }
 
 template <int C>

@@ -30,9 +30,12 @@ __device__ __forceinline__ void block_score_row(const float* L, int n_cand, int 
   for (int t = 0; t < RB; ++t) { m[t] = -INFINITY; s[t] = 0.f; }
   for (int J = tid; J < n_cand; J += 256) {
     const float* p = L + (size_t)J * RB;
+    float xs[RB];
+#pragma unroll
+    for (int t = 0; t < RB; ++t) xs[t] = p[t];  // unconditional, so the loads stay vectorised
 #pragma unroll
     for (int t = 0; t < RB; ++t) {
-      const float x = t < rows ? p[t] : -INFINITY;  // rows past the end were never written
+      const float x = t < rows ? xs[t] : -INFINITY;  // rows past the end were never written
       const float mn = fmaxf(m[t], x);
       if (mn != -INFINITY) {
         s[t] = s[t] * fast_exp2(m[t] - mn) + fast_exp2(x - mn);
@@ -73,9 +76,14 @@ __device__ __forceinline__ void block_score_row(const float* L, int n_cand, int 
     float sc = 0.f;
     if (J < n_cand) {
       const float* p = L + (size_t)J * RB;
+      float xs[RB];
 #pragma unroll
-      for (int t = 0; t < RB; ++t)
-        if (t < rows) sc += fast_exp2(p[t] - sh.lse[t]);
+      for (int t = 0; t < RB; ++t) xs[t] = p[t];
+#pragma unroll
+      for (int t = 0; t < RB; ++t) {
+        const float e = fast_exp2(xs[t] - sh.lse[t]);
+        sc += t < rows ? e : 0.f;
+      }
       sc *= inv_r;
     }
     emit(J, sc);
