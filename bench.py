@@ -316,7 +316,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip timing the selection and scoring variants on the headline layer")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain elementwise kernel of known size (1 GiB read, 1 GiB "
+                         "written), the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     a = ap.parse_args()
+
+    if a.copy_calibration:
+        import torch
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.mul(x, 2.0, out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "torch.mul(x, 2.0, out=y)", "launches": 3,
+                          "bytes_read_per_launch": 1 << 30, "bytes_written_per_launch": 1 << 30}))
+        return
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path is measured on a single MI355X "

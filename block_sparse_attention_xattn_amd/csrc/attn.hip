@@ -31,13 +31,25 @@
 #ifndef XATTN_ATTN_SETPRIO
 #define XATTN_ATTN_SETPRIO 0
 #endif
-// 1: sparse workgroups pair neighbouring rows of a head; 0: one row each
-#ifndef XATTN_SPARSE_PAIR_ROWS
-#define XATTN_SPARSE_PAIR_ROWS 0
+// Sparse workgroups pair neighbouring rows of a head (one K/V tile load serves
+// both rows of the union list) once a head has at least this many query blocks;
+// shorter rows keep one row per workgroup.
+#ifndef XATTN_SPARSE_PAIR_ROWS_MIN_NB
+#define XATTN_SPARSE_PAIR_ROWS_MIN_NB 1024
 #endif
 // 1: the sparse workgroups of one KV group share an XCD; 0: spread them
 #ifndef XATTN_SPARSE_GROUP_ON_XCD
 #define XATTN_SPARSE_GROUP_ON_XCD 1
+#endif
+// 1: sparse items are ordered KV group by KV group (all rows of one group
+// before the next), so the device works on one KV head's K/V at a time and the
+// infinity cache keeps it; 0: row by row across all heads
+#ifndef XATTN_SPARSE_GROUP_MAJOR
+#define XATTN_SPARSE_GROUP_MAJOR 1
+#endif
+// consecutive items (rows, with GROUP_MAJOR) handed to one XCD together
+#ifndef XATTN_SPARSE_ROWS_PER_CHUNK
+#define XATTN_SPARSE_ROWS_PER_CHUNK 1
 #endif
 // log2 of the neighbouring query-block rows a KV group keeps on one XCD in the
 // sparse kernel (see xcd_map)
@@ -164,10 +176,19 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   const int GW = (int)its.GW;
   const int pw = item % GW;
   uint32_t rest = item / GW;
-  const int g = rest % a.Hkv;
-  rest /= a.Hkv;
-  const int b = rest % a.B;
-  const int P = NP - 1 - (int)(rest / a.B);
+  int g, b, P;
+  if (SPARSE && XATTN_SPARSE_GROUP_MAJOR) {
+    // KV-group-major: every row of one KV group before the next group
+    P = NP - 1 - (int)(rest % NP);
+    rest /= NP;
+    b = rest % a.B;
+    g = rest / a.B;
+  } else {
+    g = rest % a.Hkv;
+    rest /= a.Hkv;
+    b = rest % a.B;
+    P = NP - 1 - (int)(rest / a.B);
+  }
   // slot s covers head slot_h(s) and query block slot_I(s)
   auto slot_h = [&](int s2) { return g * G + (MODE == MODE_SIBLINGS ? 2 * pw + s2 : pw); };
   auto slot_I = [&](int s2) { return MODE == MODE_ROWS ? 2 * P + s2 : P; };
@@ -505,7 +526,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
     attn_item<C, BLK, CAUSAL, SPARSE, MODE, KTAIL>(a, xcd_map(blockIdx.x, its.n, its.GW, 0), smem, scan_s);
   } else {
     __shared__ uint32_t item_s;
-    const uint32_t K = XATTN_SPARSE_GROUP_ON_XCD ? its.GW : 1;
+    const uint32_t K = (XATTN_SPARSE_GROUP_ON_XCD ? its.GW : 1) * XATTN_SPARSE_ROWS_PER_CHUNK;
     const uint32_t x0 = xcc_id();
     uint32_t q = 0;
     for (;;) {
@@ -639,10 +660,12 @@ static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t
 
 // 128-row blocks: dense attention pairs GQA siblings (identical block lists)
 // when the group size is even, and so does sparse attention over GQA-union
-// lists. Other sparse lists run one (head, row) per workgroup: sibling heads
-// keep very different numbers of blocks, so a sibling pair would leave one
-// half idle (pairing neighbouring rows of a head is available behind
-// XATTN_SPARSE_PAIR_ROWS). 64-row blocks use one (head, row) per workgroup.
+// lists. Other sparse lists pair neighbouring rows of one head on long
+// sequences (their lists share most blocks, so the union costs little and each
+// K/V tile is fetched once for both rows) and run one (head, row) per
+// workgroup otherwise; sibling heads keep very different numbers of blocks, so
+// a sibling pair would leave one half idle. 64-row blocks use one (head, row)
+// per workgroup.
 template <int C, int BLK>
 static hipError_t launch_bf16_cb(const Shape& s, const AttnArgs& a, hipStream_t st) {
   if (BLK == 128) {
@@ -651,7 +674,8 @@ static hipError_t launch_bf16_cb(const Shape& s, const AttnArgs& a, hipStream_t 
     // GQA-union lists are shared by the siblings: one tile load serves both
     if (a.kv_idx != nullptr && pairs && s.selection == SEL_GQA_UNION)
       return launch_bf16_cbm<C, BLK, MODE_SIBLINGS>(s, a, st);
-    if (a.kv_idx != nullptr && XATTN_SPARSE_PAIR_ROWS) return launch_bf16_cbm<C, BLK, MODE_ROWS>(s, a, st);
+    if (a.kv_idx != nullptr && s.NBq() >= XATTN_SPARSE_PAIR_ROWS_MIN_NB)
+      return launch_bf16_cbm<C, BLK, MODE_ROWS>(s, a, st);
   }
   return launch_bf16_cbm<C, BLK, MODE_SINGLE>(s, a, st);
 }

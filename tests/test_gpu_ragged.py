@@ -222,3 +222,35 @@ def test_ragged_outputs_stay_inside_buffers(xa, case):
                        (lse_all, -7.0), (ws_all, 0x5A)):
         assert (full[:guard] == fill).all() and (full[-guard:] == fill).all()
     assert torch.isfinite(out.float()).all()
+
+
+@pytest.mark.parametrize("mk,chunk_blocks", [(131149, 0), (262221, 512)])
+def test_paired_rows_long_ragged_sampled(xa, mk, chunk_blocks):
+    # long rows run two neighbouring query blocks per workgroup over the union
+    # of their lists; an odd number of query blocks leaves the last pair with
+    # an empty slot. Sampled rows (incl. the last) against the oracle.
+    import workloads as wl
+    w = wl.WORKLOADS["llama128k"].scaled(M=mk, Hq=2, Hkv=1)
+    x = wl.make_inputs(w, device=DEV)
+    off = 128 * chunk_blocks
+    q = x["q"][:, :, off:].contiguous()
+    k, v = x["k"], x["v"]
+    mq = mk - off
+    nbq, nbk = -(-mq // 128), -(-mk // 128)
+    assert nbq >= 1024 and nbq % 2 == 1
+    print(f"[paired] Mq={mq} Mk={mk} NBq={nbq}", flush=True)
+    ss, sm = wl.default_scales(w)
+    bufs = xa.xattn_prefill(q, k, v, x["tau"], 128, w.stride, ss, sm, True)
+    torch.cuda.synchronize()
+    kh, vh = f64(k[0, 0]), f64(v[0, 0])
+    for h, big_i in ((0, 0), (1, nbq // 2), (0, nbq - 2), (1, nbq - 1)):
+        qh = f64(q[0, h])
+        ref = oracle.block_score_row(qh, kh, big_i, 128, w.stride, ss, True)
+        got = f64(bufs.block_scores[0, h, big_i])
+        assert (np.abs(got - ref) <= score_tol(ref)).all(), (h, big_i)
+        keep = bufs.mask[0, h, big_i].cpu().numpy().astype(bool)
+        o_ref, l_ref = oracle.attend_row(qh, kh, vh, keep, big_i, 128, sm, True)
+        o_got = f64(bufs.out[0, h, big_i * 128:big_i * 128 + o_ref.shape[0]])
+        err = np.abs(o_got - o_ref).max()
+        assert err <= 2e-2, (h, big_i, err)
+        print(f"[paired] h={h} I={big_i} kept={int(keep.sum())} err={err:.2e}", flush=True)
