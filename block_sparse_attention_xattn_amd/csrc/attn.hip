@@ -298,18 +298,35 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  auto key_start = [&](int t) -> int {
-    const int jb = SPARSE ? (int)idx_s[t / SUB] : t / SUB;
-    return jb * BLK + (t % SUB) * L::KT;
+  // List entry of sub-tile t, packed as (key block | slot bits << 16). Entries
+  // are held 64 at a time, one per lane of a VGPR window, and picked out with
+  // v_readlane: no LDS round trip sits in front of a tile fetch or its MFMAs.
+  // The loops ask for entries in increasing order, t + 2 or t + 3 ahead.
+  uint32_t ewin = 0;
+  int ebase = -64;
+  auto entry = [&](int t) -> uint32_t {
+    const int e = min(t / SUB, cnt > 0 ? cnt - 1 : 0);
+    if constexpr (!SPARSE) {
+      return (uint32_t)e;
+    } else {
+      if (e >= ebase + 64) {  // uniform: refresh the window
+        ebase = e & ~63;
+        const int el = min(ebase + lane, cnt > 0 ? cnt - 1 : 0);
+        ewin = SLOTS > 1 ? (uint32_t)idx_s[el] | ((uint32_t)memb_s[el] << 16) : (uint32_t)idx_s[el];
+      }
+      return (uint32_t)__builtin_amdgcn_readlane((int)ewin, e - ebase);
+    }
   };
-  auto mine_tile = [&](int t) -> bool {
-    if constexpr (SPARSE && SLOTS > 1) return (memb_s[t / SUB] >> hs) & 1;
+  auto key_start = [&](uint32_t en, int t) -> int {
+    return (int)(en & 0xFFFFu) * BLK + (t % SUB) * L::KT;
+  };
+  auto mine_tile = [&](uint32_t en) -> bool {
+    if constexpr (SPARSE && SLOTS > 1) return (en >> (16 + hs)) & 1u;
     return live;
   };
 
   typedef u32x4 Stage[2 * PER_T];  // K chunks then V chunks
-  auto load_tile = [&](int t, Stage& r) {
-    const int k0 = key_start(t);
+  auto load_tile = [&](int k0, Stage& r) {
 #pragma unroll
     for (int p = 0; p < PER_T; ++p) {
       const int c = tid + p * NT;
@@ -332,11 +349,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   };
 
   // one sub-tile of online-softmax attention for this wave
-  auto compute = [&](int t, int buf) {
-    const int k0 = key_start(t);
+  auto compute = [&](int k0, bool mine, int buf) {
     if (CAUSAL && (k0 > qa0 + 31)) return;      // whole sub-tile above this wave's rows
     if (KTAIL && k0 >= a.Mk) return;            // whole sub-tile past the last key
-    if (!mine_tile(t)) return;                  // selected only by the other head
+    if (!mine) return;                          // selected only by the other head
     const unsigned char* Kb = Ks + buf * L::TILE_B;
     const unsigned char* Vb = Vs + buf * L::TILE_B;
     // S^T tiles n = 0, 1: keys k0 + 32n + [8(r/4) + 4hh + r%4], query q0 + l32
@@ -431,31 +447,40 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   __syncthreads();  // block list visible
   if constexpr (DEPTH == 1) {
     Stage r0;
+    uint32_t e0 = entry(0), e1 = entry(1);  // entries of tiles t, t+1
     if (n_sub > 0) {
-      load_tile(0, r0);
+      load_tile(key_start(e0, 0), r0);
       store_tile(0, r0);
     }
     __syncthreads();
     for (int t = 0; t < n_sub; ++t) {
       const bool more = t + 1 < n_sub;
-      if (more) load_tile(t + 1, r0);
-      compute(t, t & 1);
+      const uint32_t e2 = entry(t + 2);
+      if (more) load_tile(key_start(e1, t + 1), r0);
+      compute(key_start(e0, t), mine_tile(e0), t & 1);
       if (more) store_tile((t + 1) & 1, r0);
       __syncthreads();
+      e0 = e1;
+      e1 = e2;
     }
   } else {
     // two sub-tiles in flight: tile t+2 is fetched while tile t is computed and
     // tile t+1 (fetched one iteration earlier) waits in registers
     Stage ra, rb;
-    if (n_sub > 0) load_tile(0, ra);
-    if (n_sub > 1) load_tile(1, rb);
+    uint32_t e0 = entry(0), e1 = entry(1), e2 = entry(2);  // entries of tiles t .. t+2
+    if (n_sub > 0) load_tile(key_start(e0, 0), ra);
+    if (n_sub > 1) load_tile(key_start(e1, 1), rb);
     if (n_sub > 0) store_tile(0, ra);
     __syncthreads();
     auto iter = [&](int t, Stage& ld, const Stage& st) {
-      if (t + 2 < n_sub) load_tile(t + 2, ld);
-      compute(t, t & 1);
+      const uint32_t e3 = entry(t + 3);
+      if (t + 2 < n_sub) load_tile(key_start(e2, t + 2), ld);
+      compute(key_start(e0, t), mine_tile(e0), t & 1);
       if (t + 1 < n_sub) store_tile((t + 1) & 1, st);
       __syncthreads();
+      e0 = e1;
+      e1 = e2;
+      e2 = e3;
     };
     for (int t = 0; t < n_sub; t += 2) {
       iter(t, ra, rb);
