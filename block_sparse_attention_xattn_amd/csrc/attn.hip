@@ -139,19 +139,24 @@ struct AttnItems {
 // barrier after its last LDS read, so consecutive items may reuse the LDS.
 // KTAIL: the last key block is partial (Mk % BLK != 0): key rows past the end
 // are clamped on load and masked out of the softmax.
-template <int C, int BLK, bool CAUSAL, bool SPARSE, int MODE, bool KTAIL>
+// RPW: query rows per wave, 32 or 64. With 64 a wave holds two 32-row q-tiles,
+// and every K and V^T fragment read from LDS feeds two MFMAs (half the LDS
+// traffic per FLOP); the wave then needs more than 256 registers, so it runs
+// alone on its SIMD.
+template <int C, int BLK, bool CAUSAL, bool SPARSE, int MODE, bool KTAIL, int RPW>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item,
                                           unsigned char* smem, int* scan_s) {
   using L = AttnLds<C>;
   constexpr int SLOTS = AttnMode<MODE>::SLOTS;
-  constexpr int WPH = BLK / 32;               // waves per slot (32 query rows each)
+  constexpr int WPH = BLK / RPW;              // waves per slot
+  constexpr int QT = RPW / 32;                // 32-row q-tiles per wave
   constexpr int NT = 64 * WPH * SLOTS;        // threads
   constexpr int SUB = BLK / L::KT;            // sub-tiles per key block
   constexpr int CHUNKS = L::KT * C / 8;       // 16-byte chunks per K (or V) sub-tile
   constexpr int PER_T = CHUNKS / NT;
   constexpr int KK = C / 16;                  // MFMA k-steps over the head dim
   constexpr int DN = C / 32;                  // 32-wide d tiles of O^T
-  constexpr int DEPTH = SLOTS == 2 ? 2 : 1;   // sub-tiles in flight in registers
+  constexpr int DEPTH = SLOTS == 2 && RPW == 32 ? 2 : 1;  // sub-tiles in flight in registers
   static_assert(CHUNKS % NT == 0, "tile load must divide evenly");
 
   unsigned char* Ks = smem;                      // [2][KT rows][2C bytes], swizzled
@@ -167,7 +172,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int hs = wave / WPH;                   // slot of this wave
-  const int slice = wave % WPH;                // 32-row slice of the query block
+  const int slice = wave % WPH;                // RPW-row slice of the query block
 
   // ---- decode the item: heavy query rows (large P) come first in item order
   const int G = a.Hq / a.Hkv;
@@ -273,30 +278,37 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   }
   const int n_sub = cnt * SUB;
 
-  // ---- Q fragments (B operand of S^T = K Q^T): Q[q0 + l32][16kk + 8hh .. +7]
-  const int q0 = I * BLK + slice * 32;           // first query row of this wave
+  // ---- Q fragments (B operand of S^T = K Q^T): Q[q0 + 32y + l32][16kk + 8hh .. +7]
+  const int q0 = I * BLK + slice * RPW;          // first query row of this wave
   const int qa0 = q0 + a.qoff * BLK;             // its position in the key sequence
-  bf16x8 qf[KK];
-  {
+  bf16x8 qf[QT][KK];
+#pragma unroll
+  for (int y = 0; y < QT; ++y) {
     // rows past the end (a partial last block, or a dead slot) read the last
     // query row instead; their outputs are never stored
-    const uint16_t* qrow = qh + (size_t)min(live ? q0 + l32 : l32, a.Mq - 1) * C + 8 * hh;
+    const uint16_t* qrow = qh + (size_t)min(live ? q0 + 32 * y + l32 : l32, a.Mq - 1) * C + 8 * hh;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qf[kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * kk));
-    // Complete the Q loads here. Otherwise the compiler may leave them in flight
-    // into the key loop, and since the load counter is in-order, every first use
-    // of qf per sub-tile would also wait for the next tile's prefetch issued just
-    // before it, serialising the prefetch with the compute.
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qf[kk]));
+      qf[y][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * kk));
   }
-
-  f32x16 o[DN];
+  // Complete the Q loads here. Otherwise the compiler may leave them in flight
+  // into the key loop, and since the load counter is in-order, every first use
+  // of qf per sub-tile would also wait for the next tile's prefetch issued just
+  // before it, serialising the prefetch with the compute.
 #pragma unroll
-  for (int d = 0; d < DN; ++d) o[d] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  for (int y = 0; y < QT; ++y)
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" ::"v"(qf[y][kk]));
+
+  f32x16 o[QT][DN];
+  float m_run[QT], l_run[QT];
+#pragma unroll
+  for (int y = 0; y < QT; ++y) {
+#pragma unroll
+    for (int d = 0; d < DN; ++d) o[y][d] = f32x16{};
+    m_run[y] = -INFINITY;
+    l_run[y] = 0.f;
+  }
 
   // List entry of sub-tile t, packed as (key block | slot bits << 16). Entries
   // are held 64 at a time, one per lane of a VGPR window, and picked out with
@@ -350,13 +362,15 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
 
   // one sub-tile of online-softmax attention for this wave
   auto compute = [&](int k0, bool mine, int buf) {
-    if (CAUSAL && (k0 > qa0 + 31)) return;      // whole sub-tile above this wave's rows
+    if (CAUSAL && (k0 > qa0 + RPW - 1)) return; // whole sub-tile above this wave's rows
     if (KTAIL && k0 >= a.Mk) return;            // whole sub-tile past the last key
     if (!mine) return;                          // selected only by the other head
     const unsigned char* Kb = Ks + buf * L::TILE_B;
     const unsigned char* Vb = Vs + buf * L::TILE_B;
-    // S^T tiles n = 0, 1: keys k0 + 32n + [8(r/4) + 4hh + r%4], query q0 + l32
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    // S^T tiles (y, n): keys k0 + 32n + [8(r/4) + 4hh + r%4], query q0 + 32y + l32
+    f32x16 sacc[QT][2];
+#pragma unroll
+    for (int y = 0; y < QT; ++y) sacc[y][0] = sacc[y][1] = f32x16{};
     if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);  // MFMA issue first on the SIMD
     // K fragments are read XATTN_KBATCH k-steps at a time ahead of their MFMAs
     constexpr int KB = XATTN_KBATCH < KK ? XATTN_KBATCH : KK;
@@ -375,55 +389,60 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
 #pragma unroll
       for (int u = 0; u < KB; ++u)
 #pragma unroll
-        for (int n = 0; n < 2; ++n) sacc[n] = mfma32x32x16(ka[u][n], qf[k0b + u], sacc[n]);
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int y = 0; y < QT; ++y) sacc[y][n] = mfma32x32x16(ka[u][n], qf[y][k0b + u], sacc[y][n]);
     }
     if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
-    if ((CAUSAL && (k0 + L::KT - 1 > qa0)) || (KTAIL && k0 + L::KT > a.Mk)) {
-      const int qi = qa0 + l32;
-      const int kmax = !KTAIL ? qi : (CAUSAL ? min(qi, a.Mk - 1) : a.Mk - 1);  // last visible key
+    bf16x8 pb[QT][4];
+#pragma unroll
+    for (int y = 0; y < QT; ++y) {
+      const int qay = qa0 + 32 * y;  // first query of q-tile y (key-sequence position)
+      if ((CAUSAL && (k0 + L::KT - 1 > qay)) || (KTAIL && k0 + L::KT > a.Mk)) {
+        const int qi = qay + l32;
+        const int kmax = !KTAIL ? qi : (CAUSAL ? min(qi, a.Mk - 1) : a.Mk - 1);  // last visible key
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * n + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key > kmax) sacc[y][n][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[y][n][r]);
+      mx = halves_max(mx);
+      // Lazy rescaling (exact): O and l share the reference m_run, so the
+      // reference may lag the true running max as long as 2^(s*c - m_run) stays
+      // small. It is raised only when the tile max exceeds it by more than 8
+      // (in log2 units), which bounds P by 256 (fine for bf16 and fp32); the
+      // final O / l is unchanged. The branch is uniform per wave.
+      const float m_tile = mx * a.scale_log2;
+      const bool raise = m_tile > m_run[y] + 8.f;
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = fmaxf(m_run[y], m_tile);
+        // 0 on a lane's first visible tile; 1 while a lane has seen no key
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[y] - m_new);
+        m_run[y] = m_new;
+        l_run[y] *= alpha;
+#pragma unroll
+        for (int d = 0; d < DN; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[y][d][r] *= alpha;
+      }
+      const float m_use = (m_run[y] == -INFINITY) ? 0.f : m_run[y];
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * n + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (key > kmax) sacc[n][r] = -INFINITY;
+          const float pr = fast_exp2(fmaf(sacc[y][n][r], a.scale_log2, -m_use));
+          l_run[y] += pr;
+          pb[y][2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
         }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[n][r]);
-    mx = halves_max(mx);
-    // Lazy rescaling (exact): O and l share the reference m_run, so the
-    // reference may lag the true running max as long as 2^(s*c - m_run) stays
-    // small. It is raised only when the tile max exceeds it by more than 8
-    // (in log2 units), which bounds P by 256 (fine for bf16 and fp32); the
-    // final O / l is unchanged. The branch is uniform per wave.
-    const float m_tile = mx * a.scale_log2;
-    const bool raise = m_tile > m_run + 8.f;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float m_new = fmaxf(m_run, m_tile);
-      // 0 on a lane's first visible tile; 1 while a lane has seen no key
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < DN; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
-    }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-    bf16x8 pb[4];
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(fmaf(sacc[n][r], a.scale_log2, -m_use));
-        l_run += pr;
-        pb[2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
-      }
 
     // O^T[d][q] += V^T[d][key] P^T[key][q] over 16-key chunks tc
     const int G16 = lane >> 4, s16 = lane & 15;
@@ -437,8 +456,9 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
         const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow, vbyte)));
         const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow + 8, vbyte)));
         typedef short i16x8 __attribute__((ext_vector_type(8)));
-        const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[d] = mfma32x32x16(__builtin_bit_cast(bf16x8, both), pb[tc], o[d]);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int y = 0; y < QT; ++y) o[y][d] = mfma32x32x16(vf, pb[y][tc], o[y][d]);
       }
     }
     if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
@@ -490,24 +510,28 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) * ln 2
   if (!live) return;
-  const float l_tot = halves_sum(l_run);
-  const float inv = 1.f / l_tot;
-  const int qi = q0 + l32;
-  if (qi >= a.Mq) return;  // padding rows of a partial last block
-  uint16_t* orow = a.out + (bh * a.Mq + qi) * C;
 #pragma unroll
-  for (int d = 0; d < DN; ++d)
+  for (int y = 0; y < QT; ++y) {
+    const float l_tot = halves_sum(l_run[y]);
+    const float inv = 1.f / l_tot;
+    const int qi = q0 + 32 * y + l32;
+    if (qi < a.Mq) {  // rows past the end of a partial last block are not written
+      uint16_t* orow = a.out + (bh * a.Mq + qi) * C;
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int dc = 32 * d + 8 * g4 + 4 * hh;
-      u32x2 w;
-      w[0] = (uint32_t)f32_to_bf16(o[d][4 * g4 + 0] * inv) |
-             ((uint32_t)f32_to_bf16(o[d][4 * g4 + 1] * inv) << 16);
-      w[1] = (uint32_t)f32_to_bf16(o[d][4 * g4 + 2] * inv) |
-             ((uint32_t)f32_to_bf16(o[d][4 * g4 + 3] * inv) << 16);
-      *reinterpret_cast<u32x2*>(orow + dc) = w;
+      for (int d = 0; d < DN; ++d)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dc = 32 * d + 8 * g4 + 4 * hh;
+          u32x2 w;
+          w[0] = (uint32_t)f32_to_bf16(o[y][d][4 * g4 + 0] * inv) |
+                 ((uint32_t)f32_to_bf16(o[y][d][4 * g4 + 1] * inv) << 16);
+          w[1] = (uint32_t)f32_to_bf16(o[y][d][4 * g4 + 2] * inv) |
+                 ((uint32_t)f32_to_bf16(o[y][d][4 * g4 + 3] * inv) << 16);
+          *reinterpret_cast<u32x2*>(orow + dc) = w;
+        }
+      if (a.lse && hh == 0) a.lse[bh * a.Mq + qi] = (m_run[y] + log2f(l_tot)) * kLn2;
     }
-  if (a.lse && hh == 0) a.lse[bh * a.Mq + qi] = (m_run + log2f(l_tot)) * kLn2;
+  }
 }
 
 // Claims the next item for a persistent workgroup. queue[32 x] counts the
@@ -538,17 +562,17 @@ __device__ __forceinline__ uint32_t claim_item(uint32_t* queue, const uint32_t n
 // one-workgroup-per-item launch parks the long rows of a dense head on one
 // engine and stalls the others behind it. Pulling from a queue keeps every
 // workgroup slot busy until the queues run dry.
-template <int C, int BLK, bool CAUSAL, bool SPARSE, int MODE, bool KTAIL>
-__global__ __launch_bounds__(BLK * 2 * AttnMode<MODE>::SLOTS, MODE == MODE_SINGLE ? 2 : 1)
+template <int C, int BLK, bool CAUSAL, bool SPARSE, int MODE, bool KTAIL, int RPW>
+__global__ __launch_bounds__(64 * (BLK / RPW) * AttnMode<MODE>::SLOTS, MODE == MODE_SINGLE ? 2 : 1)
 void attn_fwd_bf16_kernel(AttnArgs a) {
   using L = AttnLds<C>;
   constexpr int SLOTS = AttnMode<MODE>::SLOTS;
-  constexpr int NT = 64 * (BLK / 32) * SLOTS;
+  constexpr int NT = 64 * (BLK / RPW) * SLOTS;
   __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes(SLOTS)];
   __shared__ int scan_s[SLOTS > 1 ? NT / 64 : 1];
   const AttnItems its(a, MODE);
   if constexpr (!SPARSE) {
-    attn_item<C, BLK, CAUSAL, SPARSE, MODE, KTAIL>(a, xcd_map(blockIdx.x, its.n, its.GW, 0), smem, scan_s);
+    attn_item<C, BLK, CAUSAL, SPARSE, MODE, KTAIL, RPW>(a, xcd_map(blockIdx.x, its.n, its.GW, 0), smem, scan_s);
   } else {
     __shared__ uint32_t item_s;
     const uint32_t K = (XATTN_SPARSE_GROUP_ON_XCD ? its.GW : 1) * XATTN_SPARSE_ROWS_PER_CHUNK;
@@ -561,7 +585,7 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
       if (item == kNoItem) break;  // uniform over the workgroup
       // every thread reads item_s before the barriers inside attn_item, and
       // thread 0 rewrites it only after them
-      attn_item<C, BLK, CAUSAL, SPARSE, MODE, KTAIL>(a, item, smem, scan_s);
+      attn_item<C, BLK, CAUSAL, SPARSE, MODE, KTAIL, RPW>(a, item, smem, scan_s);
     }
   }
 }
@@ -649,24 +673,24 @@ static int resident_workgroups(Kern kern, int threads) {
   return cus * per_cu;
 }
 
-template <int C, int BLK, int MODE, bool KTAIL>
+template <int C, int BLK, int MODE, bool KTAIL, int RPW>
 static hipError_t launch_bf16_cbmt(const Shape& s, const AttnArgs& a, hipStream_t st) {
   const int G = s.Hq / s.Hkv;
   const int NP = MODE == MODE_ROWS ? (s.NBq() + 1) / 2 : s.NBq();
   const int GW = MODE == MODE_SIBLINGS ? G / 2 : G;
   const size_t n_items = (size_t)s.B * s.Hkv * GW * NP;
-  const int threads = BLK * 2 * AttnMode<MODE>::SLOTS;
+  const int threads = 64 * (BLK / RPW) * AttnMode<MODE>::SLOTS;
   if (a.kv_idx == nullptr) {
     const dim3 grid((unsigned)n_items);
     if (s.causal)
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, false, MODE, KTAIL>), grid, dim3(threads), 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, true, false, MODE, KTAIL, RPW>), grid, dim3(threads), 0, st, a);
     else
-      hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, false, MODE, KTAIL>), grid, dim3(threads), 0, st, a);
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<C, BLK, false, false, MODE, KTAIL, RPW>), grid, dim3(threads), 0, st, a);
     return hipGetLastError();
   }
   if (a.queue == nullptr) return hipErrorInvalidValue;
-  auto kern = s.causal ? attn_fwd_bf16_kernel<C, BLK, true, true, MODE, KTAIL>
-                       : attn_fwd_bf16_kernel<C, BLK, false, true, MODE, KTAIL>;
+  auto kern = s.causal ? attn_fwd_bf16_kernel<C, BLK, true, true, MODE, KTAIL, RPW>
+                       : attn_fwd_bf16_kernel<C, BLK, false, true, MODE, KTAIL, RPW>;
   const int slots = resident_workgroups(kern, threads);
   if (slots <= 0) return hipErrorInvalidDeviceFunction;
   hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(kQueueWords), 0, st, a.queue);
@@ -677,10 +701,27 @@ static hipError_t launch_bf16_cbmt(const Shape& s, const AttnArgs& a, hipStream_
   return hipGetLastError();
 }
 
+// Sparse launches use XATTN_SPARSE_RPW query rows per wave, dense ones
+// XATTN_DENSE_RPW.
+#ifndef XATTN_SPARSE_RPW
+#define XATTN_SPARSE_RPW 32
+#endif
+#ifndef XATTN_DENSE_RPW
+#define XATTN_DENSE_RPW 32
+#endif
+
+template <int C, int BLK, int MODE, int RPW>
+static hipError_t launch_bf16_cbmr(const Shape& s, const AttnArgs& a, hipStream_t st) {
+  return s.Mk % BLK ? launch_bf16_cbmt<C, BLK, MODE, true, RPW>(s, a, st)
+                    : launch_bf16_cbmt<C, BLK, MODE, false, RPW>(s, a, st);
+}
+
 template <int C, int BLK, int MODE>
 static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t st) {
-  return s.Mk % BLK ? launch_bf16_cbmt<C, BLK, MODE, true>(s, a, st)
-                    : launch_bf16_cbmt<C, BLK, MODE, false>(s, a, st);
+  constexpr int SR = BLK >= XATTN_SPARSE_RPW ? XATTN_SPARSE_RPW : 32;
+  constexpr int DR = BLK >= XATTN_DENSE_RPW ? XATTN_DENSE_RPW : 32;
+  return a.kv_idx != nullptr ? launch_bf16_cbmr<C, BLK, MODE, SR>(s, a, st)
+                             : launch_bf16_cbmr<C, BLK, MODE, DR>(s, a, st);
 }
 
 // 128-row blocks: dense attention pairs GQA siblings (identical block lists)
