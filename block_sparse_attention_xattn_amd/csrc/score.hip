@@ -54,8 +54,17 @@ struct ScoreArgs {
 #define XATTN_SCORE_TILE 256
 #endif
 constexpr int SC_TILE = XATTN_SCORE_TILE;   // strided keys x strided queries per tile
-constexpr int SC_WN = SC_TILE / 64;         // waves per tile side (64 x 64 per wave)
+// output sub-tile of one wave: 64 x 64 (2 x 2 MFMA tiles, four waves per SIMD)
+// or 128 x 128 (4 x 4 MFMA tiles, one wave per SIMD with its accumulators in
+// AGPRs; half the LDS fragment reads per MFMA)
+#ifndef XATTN_SCORE_WT
+#define XATTN_SCORE_WT 64
+#endif
+constexpr int SC_WT = XATTN_SCORE_WT;
+constexpr int SC_MT = SC_WT / 32;           // MFMA tiles per wave side
+constexpr int SC_WN = SC_TILE / SC_WT;      // waves per tile side
 constexpr int SC_NT = 64 * SC_WN * SC_WN;   // threads per workgroup
+constexpr int SC_MINW = SC_WT == 64 ? 4 : 1;  // waves per SIMD the kernel is built for
 #ifndef XATTN_SCORE_KC
 #define XATTN_SCORE_KC 64
 #endif
@@ -101,7 +110,7 @@ __device__ __forceinline__ void tile_pair(int p, bool causal, int Tq, int Tk, in
 // TAIL: Mq or Mk is not a multiple of S, so the last stride group of Q or K is
 // partial (a separate instantiation keeps the common loop branch-free).
 template <int C, int RB, bool CAUSAL, bool TAIL>
-__global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_bf16_kernel(ScoreArgs a) {
   static_assert(RB == 2 || RB == 4 || RB == 8 || RB == 16 || RB == 32, "r");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * SC_OP];
   uint16_t* Ks = smem;               // [2][SC_TILE rows] strided keys (A operand)
@@ -186,29 +195,29 @@ __global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a)
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[SC_MT][SC_MT];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < SC_MT; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[x][y] = f32x16{};
+    for (int y = 0; y < SC_MT; ++y) acc[x][y] = f32x16{};
 
   auto mma_chunk = [&](int buf) {
     const uint16_t* Kb = Ks + buf * SC_OP;
     const uint16_t* Qb = Qs + buf * SC_OP;
 #pragma unroll
     for (int ks = 0; ks < SC_KC / 16; ++ks) {
-      bf16x8 af[2], bfr[2];
+      bf16x8 af[SC_MT], bfr[SC_MT];
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
+      for (int x = 0; x < SC_MT; ++x) {
         af[x] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(Kb + sc_off(64 * wk + 32 * x + l32, 2 * ks + hh)));
+            bf16x8, *reinterpret_cast<const u32x4*>(Kb + sc_off(SC_WT * wk + 32 * x + l32, 2 * ks + hh)));
         bfr[x] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(Qb + sc_off(64 * wq + 32 * x + l32, 2 * ks + hh)));
+            bf16x8, *reinterpret_cast<const u32x4*>(Qb + sc_off(SC_WT * wq + 32 * x + l32, 2 * ks + hh)));
       }
 #pragma unroll
-      for (int x = 0; x < 2; ++x)
+      for (int x = 0; x < SC_MT; ++x)
 #pragma unroll
-        for (int y = 0; y < 2; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
+        for (int y = 0; y < SC_MT; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
     }
   };
 
@@ -225,16 +234,16 @@ __global__ __launch_bounds__(SC_NT) void score_partials_bf16_kernel(ScoreArgs a)
     __syncthreads();
   }
 
-  // ---- epilogue: acc[x][y][r] is strided key j = j0 + 64wk + 32x + 8(r/4) + 4hh + r%4,
-  //      strided query i = i0 + 64wq + 32y + l32. Reduce each run of RB keys.
+  // ---- epilogue: acc[x][y][r] is strided key j = j0 + WT wk + 32x + 8(r/4) + 4hh + r%4,
+  //      strided query i = i0 + WT wq + 32y + l32. Reduce each run of RB keys.
   float* wsh = a.ws + bh * (size_t)a.NBq * a.NBk * RB;
 #pragma unroll
-  for (int y = 0; y < 2; ++y) {
-    const int i = i0 + 64 * wq + 32 * y + l32;
+  for (int y = 0; y < SC_MT; ++y) {
+    const int i = i0 + SC_WT * wq + 32 * y + l32;
     const int ia = i + a.qoff_s;  // absolute strided row
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const int jb = j0 + 64 * wk + 32 * x;  // first strided key of this 32-key sub-tile
+    for (int x = 0; x < SC_MT; ++x) {
+      const int jb = j0 + SC_WT * wk + 32 * x;  // first strided key of this 32-key sub-tile
       float v[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
