@@ -22,12 +22,15 @@
 // is contiguous and the second pass reads it with unit stride.
 //
 // GEMM (bf16, gfx950 MFMA 32x32x16): S^T = K~' Q'^T on 256 x 256 output tiles,
-// 16 waves in a 4x4 grid of 64 x 64 sub-tiles, the S*C contraction streamed in
-// 64-element chunks through a double-buffered 144 KiB LDS tile. The tile size is
-// set by L2 bandwidth: a 256 x 256 tile moves half the L2 bytes per FLOP of a
-// 128 x 128 one (128 vs 64 FLOP per byte). K~' row j, chunk c is the contiguous run
-// k[j*S + S-1 - (64c)/C][(64c)%C ...] — the stride group read in reverse, so
-// the reversal costs only address arithmetic.
+// 8 waves in a 4 x 2 grid of 64 x 128 sub-tiles. The tile size is set by L2
+// bandwidth: a 256 x 256 tile moves half the L2 bytes per FLOP of a 128 x 128
+// one (128 vs 64 FLOP per byte), and its fp32 accumulators already take half the
+// register file. The S*C contraction is streamed in chunks: with complete
+// stride groups straight from global memory into a four-stage LDS ring (see
+// score_partials_dma_kernel); with a partial last stride group through
+// registers (zero fill) into a double-buffered LDS tile of 64-element chunks.
+// K~' row j, element e is k[j*S + S-1 - e/C][e%C] — the stride group read in
+// reverse, so the reversal costs only address arithmetic.
 #include <algorithm>
 
 #include "common.h"
@@ -54,17 +57,22 @@ struct ScoreArgs {
 #define XATTN_SCORE_TILE 256
 #endif
 constexpr int SC_TILE = XATTN_SCORE_TILE;   // strided keys x strided queries per tile
-// output sub-tile of one wave: 64 x 64 (2 x 2 MFMA tiles, four waves per SIMD)
-// or 128 x 128 (4 x 4 MFMA tiles, one wave per SIMD with its accumulators in
-// AGPRs; half the LDS fragment reads per MFMA)
-#ifndef XATTN_SCORE_WT
-#define XATTN_SCORE_WT 64
+// output sub-tile of one wave, strided keys x strided queries: 64 x 128 (2 x 4
+// MFMA tiles, two waves per SIMD; the default), 64 x 64 (2 x 2, four waves per
+// SIMD; 4/3 of the LDS fragment reads per MFMA) or 128 x 128 (4 x 4, one wave
+// per SIMD with its accumulators in AGPRs). Measured on the 256K layer: 64 x 64
+// about 2% and 128 x 128 about 6% slower than 64 x 128.
+#ifndef XATTN_SCORE_WK
+#define XATTN_SCORE_WK 64
 #endif
-constexpr int SC_WT = XATTN_SCORE_WT;
-constexpr int SC_MT = SC_WT / 32;           // MFMA tiles per wave side
-constexpr int SC_WN = SC_TILE / SC_WT;      // waves per tile side
-constexpr int SC_NT = 64 * SC_WN * SC_WN;   // threads per workgroup
-constexpr int SC_MINW = SC_WT == 64 ? 4 : 1;  // waves per SIMD the kernel is built for
+#ifndef XATTN_SCORE_WQ
+#define XATTN_SCORE_WQ 128
+#endif
+constexpr int SC_WK = XATTN_SCORE_WK, SC_WQ = XATTN_SCORE_WQ;
+constexpr int SC_MTK = SC_WK / 32, SC_MTQ = SC_WQ / 32;      // MFMA tiles per wave, each side
+constexpr int SC_WNK = SC_TILE / SC_WK, SC_WNQ = SC_TILE / SC_WQ;  // waves per tile side
+constexpr int SC_NT = 64 * SC_WNK * SC_WNQ;  // threads per workgroup
+constexpr int SC_MINW = SC_NT / 256;         // waves per SIMD the kernel is built for
 #ifndef XATTN_SCORE_KC
 #define XATTN_SCORE_KC 64
 #endif
@@ -107,8 +115,101 @@ __device__ __forceinline__ void tile_pair(int p, bool causal, int Tq, int Tk, in
   tk = p - (x * (x + 1) / 2 + c0 * x);
 }
 
-// TAIL: Mq or Mk is not a multiple of S, so the last stride group of Q or K is
-// partial (a separate instantiation keeps the common loop branch-free).
+// The (b, h, query tile, key tile) of this workgroup. Consecutive items are the
+// query heads of one KV group on one tile pair, and groups of four items share
+// an XCD, so the strided-key tile is read through one L2.
+struct ScoreTile {
+  size_t bh, bg;
+  int i0, j0;  // first strided query row / strided key of the tile
+  __device__ ScoreTile(const ScoreArgs& a, bool causal) {
+    const uint32_t n_items = (uint32_t)a.B * a.Hq * a.pairs;
+    const uint32_t item = xcd_group4(blockIdx.x, n_items);
+    const int G = a.Hq / a.Hkv;
+    const int hq_in = item % G;
+    uint32_t rest = item / G;
+    const int pair = rest % a.pairs;
+    rest /= a.pairs;
+    const int g = rest % a.Hkv;
+    const int b = rest / a.Hkv;
+    const int h = g * G + hq_in;
+    int tq, tk;
+    tile_pair(pair, causal, a.Tq, a.Tk, a.c0, tq, tk);
+    bh = (size_t)b * a.Hq + h;
+    bg = (size_t)b * a.Hkv + g;
+    i0 = tq * SC_TILE;
+    j0 = tk * SC_TILE;
+  }
+};
+
+// Tile epilogue: per (strided row i, run of RB strided keys) the partial
+// log2-sum-exp of the scaled logits, masked causally and past the last key.
+template <int RB, bool CAUSAL>
+__device__ __forceinline__ void score_epilogue(const ScoreArgs& a, const f32x16 (&acc)[SC_MTK][SC_MTQ],
+                                               size_t bh, int i0, int j0, int wk, int wq, int l32, int hh) {
+  // acc[x][y][r] is strided key j = j0 + WK wk + 32x + 8(r/4) + 4hh + r%4 and
+  // strided query i = i0 + WQ wq + 32y + l32; each run of RB keys is reduced.
+  float* wsh = a.ws + bh * (size_t)a.NBq * a.NBk * RB;
+#pragma unroll
+  for (int y = 0; y < SC_MTQ; ++y) {
+    const int i = i0 + SC_WQ * wq + 32 * y + l32;
+    const int ia = i + a.qoff_s;  // absolute strided row
+#pragma unroll
+    for (int x = 0; x < SC_MTK; ++x) {
+      const int jb = j0 + SC_WK * wk + 32 * x;  // first strided key of this 32-key sub-tile
+      float v[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = jb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        float xv = acc[x][y][r] * a.scale2;
+        if ((CAUSAL && j > ia) || j >= a.Rk) xv = -INFINITY;
+        v[r] = xv;
+      }
+      if constexpr (RB <= 4) {
+        // each run of RB keys lies inside one lane's group of 4 registers
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += RB) {
+          float m = v[r0];
+#pragma unroll
+          for (int u = 1; u < RB; ++u) m = fmaxf(m, v[r0 + u]);
+          float s = 0.f;
+          if (m != -INFINITY) {
+#pragma unroll
+            for (int u = 0; u < RB; ++u) s += fast_exp2(v[r0 + u] - m);
+          }
+          const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
+          const int j = jb + 8 * (r0 >> 2) + 4 * hh + (r0 & 3);
+          const int J = j / RB;
+          if (i < a.Rq && j < a.Rk) wsh[((size_t)(i / RB) * a.NBk + J) * RB + i % RB] = Lv;
+        }
+      } else {
+        // a run of RB >= 8 keys = registers [4q .. 4q + RB/2) in both wave halves
+        constexpr int NR = RB / 2;  // registers per half per run
+#pragma unroll
+        for (int r0 = 0; r0 < 16; r0 += NR) {
+          float m = v[r0];
+#pragma unroll
+          for (int u = 1; u < NR; ++u) m = fmaxf(m, v[r0 + u]);
+          m = halves_max(m);
+          float s = 0.f;
+          if (m != -INFINITY) {
+#pragma unroll
+            for (int u = 0; u < NR; ++u) s += fast_exp2(v[r0 + u] - m);
+          }
+          s = halves_sum(s);
+          const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
+          const int j = jb + 8 * (r0 >> 2);
+          const int J = j / RB;
+          if (hh == 0 && i < a.Rq && j < a.Rk) wsh[((size_t)(i / RB) * a.NBk + J) * RB + i % RB] = Lv;
+        }
+      }
+    }
+  }
+}
+
+// Register-staged pipeline, used when Mq or Mk is not a multiple of S (TAIL:
+// the last stride group of Q or K is partial and reads as zeros; a separate
+// instantiation keeps the common loop branch-free) or when the DMA kernel is
+// switched off.
 template <int C, int RB, bool CAUSAL, bool TAIL>
 __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_bf16_kernel(ScoreArgs a) {
   static_assert(RB == 2 || RB == 4 || RB == 8 || RB == 16 || RB == 32, "r");
@@ -118,25 +219,13 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_bf16_kernel(Sco
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int wk = wave / SC_WN, wq = wave % SC_WN;
+  const int wk = wave / SC_WNQ, wq = wave % SC_WNQ;
 
-  const uint32_t n_items = (uint32_t)a.B * a.Hq * a.pairs;
-  const uint32_t item = xcd_group4(blockIdx.x, n_items);
-  const int G = a.Hq / a.Hkv;
-  const int hq_in = item % G;
-  uint32_t rest = item / G;
-  const int pair = rest % a.pairs;
-  rest /= a.pairs;
-  const int g = rest % a.Hkv;
-  const int b = rest / a.Hkv;
-  const int h = g * G + hq_in;
-  int tq, tk;
-  tile_pair(pair, CAUSAL, a.Tq, a.Tk, a.c0, tq, tk);
-
-  const size_t bh = (size_t)b * a.Hq + h, bg = (size_t)b * a.Hkv + g;
-  const uint16_t* qh = a.q + bh * a.Mq * C;
-  const uint16_t* kh = a.k + bg * a.Mk * C;
-  const int i0 = tq * SC_TILE, j0 = tk * SC_TILE;  // strided row / key origin
+  const ScoreTile tl(a, CAUSAL);
+  const size_t bh = tl.bh;
+  const uint16_t* qh = a.q + tl.bh * a.Mq * C;
+  const uint16_t* kh = a.k + tl.bg * a.Mk * C;
+  const int i0 = tl.i0, j0 = tl.j0;  // strided row / key origin
   const int S = a.S;
   const int n_chunks = S * C / SC_KC;
 
@@ -195,29 +284,30 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_bf16_kernel(Sco
     }
   };
 
-  f32x16 acc[SC_MT][SC_MT];
+  f32x16 acc[SC_MTK][SC_MTQ];
 #pragma unroll
-  for (int x = 0; x < SC_MT; ++x)
+  for (int x = 0; x < SC_MTK; ++x)
 #pragma unroll
-    for (int y = 0; y < SC_MT; ++y) acc[x][y] = f32x16{};
+    for (int y = 0; y < SC_MTQ; ++y) acc[x][y] = f32x16{};
 
   auto mma_chunk = [&](int buf) {
     const uint16_t* Kb = Ks + buf * SC_OP;
     const uint16_t* Qb = Qs + buf * SC_OP;
 #pragma unroll
     for (int ks = 0; ks < SC_KC / 16; ++ks) {
-      bf16x8 af[SC_MT], bfr[SC_MT];
+      bf16x8 af[SC_MTK], bfr[SC_MTQ];
 #pragma unroll
-      for (int x = 0; x < SC_MT; ++x) {
+      for (int x = 0; x < SC_MTK; ++x)
         af[x] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(Kb + sc_off(SC_WT * wk + 32 * x + l32, 2 * ks + hh)));
-        bfr[x] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(Qb + sc_off(SC_WT * wq + 32 * x + l32, 2 * ks + hh)));
-      }
+            bf16x8, *reinterpret_cast<const u32x4*>(Kb + sc_off(SC_WK * wk + 32 * x + l32, 2 * ks + hh)));
 #pragma unroll
-      for (int x = 0; x < SC_MT; ++x)
+      for (int y = 0; y < SC_MTQ; ++y)
+        bfr[y] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(Qb + sc_off(SC_WQ * wq + 32 * y + l32, 2 * ks + hh)));
 #pragma unroll
-        for (int y = 0; y < SC_MT; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
+      for (int x = 0; x < SC_MTK; ++x)
+#pragma unroll
+        for (int y = 0; y < SC_MTQ; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
     }
   };
 
@@ -234,64 +324,127 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_bf16_kernel(Sco
     __syncthreads();
   }
 
-  // ---- epilogue: acc[x][y][r] is strided key j = j0 + WT wk + 32x + 8(r/4) + 4hh + r%4,
-  //      strided query i = i0 + WT wq + 32y + l32. Reduce each run of RB keys.
-  float* wsh = a.ws + bh * (size_t)a.NBq * a.NBk * RB;
+  score_epilogue<RB, CAUSAL>(a, acc, bh, i0, j0, wk, wq, l32, hh);
+}
+
+// Complete stride groups (Mq and Mk multiples of S): the operand tiles go from
+// global memory straight into LDS (global_load_lds_dwordx4, no register
+// staging), three contraction chunks ahead of the MFMAs through a ring of four
+// LDS stages. Register staging could keep only one chunk in flight (the
+// accumulators fill the register budget of four waves per SIMD), which left the
+// waves waiting on L2 misses about a quarter of the time.
+//   * chunk: 32 contraction elements; a stage holds SC_TILE strided-key rows
+//     then SC_TILE strided-query rows of 64 bytes, the four 16-byte pieces of a
+//     row XOR-permuted by (row / 4) % 4 (conflict-free fragment reads);
+//   * a DMA instruction fills 1 KiB of LDS, 16 lanes' bytes per row in lane
+//     order, so each lane fetches the global piece that belongs at its slot;
+//   * per chunk: wait for this wave's DMA of the chunk, barrier (every wave's
+//     DMA has landed, and every wave is done with the stage to be refilled),
+//     issue the DMA three chunks ahead, multiply. The stages are distinct LDS
+//     objects and the loop is unrolled over them, so the compiler tracks which
+//     DMA each fragment read depends on and adds no waits of its own.
+constexpr int SD_KC = 32;                     // contraction elements per chunk
+constexpr int SD_ROW = SD_KC;                 // elements per LDS row
+constexpr int SD_STAGE = 2 * SC_TILE * SD_ROW;  // elements per stage (keys, then queries)
+constexpr int SD_BLK = 1024 / (2 * SD_ROW);   // rows per 1 KiB DMA block (16)
+constexpr int SD_BPW = (SC_TILE / SD_BLK) / (SC_NT / 64);  // DMA blocks per operand per wave
+static_assert(SD_BPW >= 1 && SD_BPW * (SC_NT / 64) * SD_BLK == SC_TILE, "DMA blocks must cover the tile");
+
+__device__ __forceinline__ int sd_off(int row, int chunk) { return row * SD_ROW + 8 * (chunk ^ ((row >> 2) & 3)); }
+
+// s_waitcnt with only the vector-memory counter: at most n loads outstanding.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+template <int C, int RB, bool CAUSAL>
+__global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_dma_kernel(ScoreArgs a) {
+  static_assert(RB == 2 || RB == 4 || RB == 8 || RB == 16 || RB == 32, "r");
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[SD_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[SD_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[SD_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[SD_STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wk = wave / SC_WNQ, wq = wave % SC_WNQ;
+  const ScoreTile tl(a, CAUSAL);
+  const uint16_t* qh = a.q + tl.bh * a.Mq * C;
+  const uint16_t* kh = a.k + tl.bg * a.Mk * C;
+  const int S = a.S;
+  const int n_chunks = S * C / SD_KC;
+
+  // this lane's piece of DMA block (wave + (SC_NT/64) u): row 16 blk + lane/4,
+  // LDS slot lane % 4, holding the row's piece (lane % 4) ^ ((row / 4) % 4);
+  // rows past the last strided row are clamped (never stored)
+  const int piece = (lane & 3) ^ ((lane >> 4) & 3);
+  const uint16_t* kp[SD_BPW];
+  const uint16_t* qp[SD_BPW];
 #pragma unroll
-  for (int y = 0; y < SC_MT; ++y) {
-    const int i = i0 + SC_WT * wq + 32 * y + l32;
-    const int ia = i + a.qoff_s;  // absolute strided row
-#pragma unroll
-    for (int x = 0; x < SC_MT; ++x) {
-      const int jb = j0 + SC_WT * wk + 32 * x;  // first strided key of this 32-key sub-tile
-      float v[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = jb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        float xv = acc[x][y][r] * a.scale2;
-        if ((CAUSAL && j > ia) || j >= a.Rk) xv = -INFINITY;
-        v[r] = xv;
-      }
-      if constexpr (RB <= 4) {
-        // each run of RB keys lies inside one lane's group of 4 registers
-#pragma unroll
-        for (int r0 = 0; r0 < 16; r0 += RB) {
-          float m = v[r0];
-#pragma unroll
-          for (int u = 1; u < RB; ++u) m = fmaxf(m, v[r0 + u]);
-          float s = 0.f;
-          if (m != -INFINITY) {
-#pragma unroll
-            for (int u = 0; u < RB; ++u) s += fast_exp2(v[r0 + u] - m);
-          }
-          const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
-          const int j = jb + 8 * (r0 >> 2) + 4 * hh + (r0 & 3);
-          const int J = j / RB;
-          if (i < a.Rq && j < a.Rk) wsh[((size_t)(i / RB) * a.NBk + J) * RB + i % RB] = Lv;
-        }
-      } else {
-        // a run of RB >= 8 keys = registers [4q .. 4q + RB/2) in both wave halves
-        constexpr int NR = RB / 2;  // registers per half per run
-#pragma unroll
-        for (int r0 = 0; r0 < 16; r0 += NR) {
-          float m = v[r0];
-#pragma unroll
-          for (int u = 1; u < NR; ++u) m = fmaxf(m, v[r0 + u]);
-          m = halves_max(m);
-          float s = 0.f;
-          if (m != -INFINITY) {
-#pragma unroll
-            for (int u = 0; u < NR; ++u) s += fast_exp2(v[r0 + u] - m);
-          }
-          s = halves_sum(s);
-          const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
-          const int j = jb + 8 * (r0 >> 2);
-          const int J = j / RB;
-          if (hh == 0 && i < a.Rq && j < a.Rk) wsh[((size_t)(i / RB) * a.NBk + J) * RB + i % RB] = Lv;
-        }
-      }
-    }
+  for (int u = 0; u < SD_BPW; ++u) {
+    const int row = SD_BLK * (wave + (SC_NT / 64) * u) + (lane >> 2);
+    const int j = min(tl.j0 + row, a.Rk - 1), i = min(tl.i0 + row, a.Rq - 1);
+    // antidiagonal: the stride group is read in reverse (row j*S + S-1-s)
+    kp[u] = kh + ((size_t)j * S + (a.diagonal ? 0 : S - 1)) * C + 8 * piece;
+    qp[u] = qh + (size_t)i * S * C + 8 * piece;
   }
+  const int kdir = a.diagonal ? 1 : -1;
+  auto issue = [&](int c, uint16_t* stg) {
+    const int srow = (SD_KC * c) / C, col0 = (SD_KC * c) % C;
+    const ptrdiff_t koff = (ptrdiff_t)kdir * srow * C + col0, qoff = (ptrdiff_t)srow * C + col0;
+#pragma unroll
+    for (int u = 0; u < SD_BPW; ++u) {
+      const int blk = wave + (SC_NT / 64) * u;
+      __builtin_amdgcn_global_load_lds(kp[u] + koff, (__attribute__((address_space(3))) void*)(stg + blk * 1024 / 2),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(qp[u] + qoff,
+                                       (__attribute__((address_space(3))) void*)(stg + SC_TILE * SD_ROW + blk * 1024 / 2),
+                                       16, 0, 0);
+    }
+  };
+
+  f32x16 acc[SC_MTK][SC_MTQ];
+#pragma unroll
+  for (int x = 0; x < SC_MTK; ++x)
+#pragma unroll
+    for (int y = 0; y < SC_MTQ; ++y) acc[x][y] = f32x16{};
+
+  // chunk c sits in stage cur; the stage nxt (chunk c - 1, done) is refilled
+  // with chunk c + 3 (past the end: the last chunk again, never read)
+  auto step = [&](int c, const uint16_t* cur, uint16_t* nxt) {
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * 2 * SD_BPW));  // chunks c+1, c+2 may be in flight
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    issue(min(c + 3, n_chunks - 1), nxt);
+    __builtin_amdgcn_sched_barrier(0);  // keep the refill ahead of this chunk's work
+#pragma unroll
+    for (int ks = 0; ks < SD_KC / 16; ++ks) {
+      bf16x8 af[SC_MTK], bfr[SC_MTQ];
+#pragma unroll
+      for (int x = 0; x < SC_MTK; ++x)
+        af[x] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + sd_off(SC_WK * wk + 32 * x + l32, 2 * ks + hh)));
+#pragma unroll
+      for (int y = 0; y < SC_MTQ; ++y)
+        bfr[y] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + SC_TILE * SD_ROW +
+                                                                           sd_off(SC_WQ * wq + 32 * y + l32, 2 * ks + hh)));
+#pragma unroll
+      for (int x = 0; x < SC_MTK; ++x)
+#pragma unroll
+        for (int y = 0; y < SC_MTQ; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
+    }
+  };
+
+  issue(0, st0);
+  issue(min(1, n_chunks - 1), st1);
+  issue(min(2, n_chunks - 1), st2);
+  // n_chunks is a multiple of 4 (checked by the launcher)
+  for (int c = 0; c < n_chunks; c += 4) {
+    step(c, st0, st3);
+    step(c + 1, st1, st0);
+    step(c + 2, st2, st1);
+    step(c + 3, st3, st2);
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing refills have landed
+  score_epilogue<RB, CAUSAL>(a, acc, tl.bh, tl.i0, tl.j0, wk, wq, l32, hh);
 }
 
 // fp32 inputs: one thread per (strided row i, key block J), plain FMA.
@@ -360,9 +513,20 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
 
 // ------------------------------------------------------------------ launchers
 
+#ifndef XATTN_SCORE_DMA
+#define XATTN_SCORE_DMA 1
+#endif
+
 template <int C, int RB, bool TAIL>
 static hipError_t launch_partials_crt(const Shape& s, const ScoreArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((size_t)s.B * s.Hq * a.pairs);
+  if (XATTN_SCORE_DMA && !TAIL && (s.stride * C / SD_KC) % 4 == 0) {
+    if (s.causal)
+      hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, true>), dim3(grid), dim3(SC_NT), 0, st, a);
+    else
+      hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, false>), dim3(grid), dim3(SC_NT), 0, st, a);
+    return hipGetLastError();
+  }
   if (s.causal)
     hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, true, TAIL>), dim3(grid), dim3(SC_NT), 0, st, a);
   else
