@@ -181,8 +181,12 @@ def run_workload(xa, wl, torch, name, steps, warmup, dense_steps):
 
 
 def cpu_baseline(wl, torch, res, budget_s):
-    """The oracle, as it stands, on evenly spaced query-block rows of head 0,
-    extrapolated to the whole layer (rows x heads)."""
+    """The oracle, as it stands, on a bounded sample of the layer: query-block
+    rows in a stratified order (bit-reversed positions, so every prefix spreads
+    over the sequence) of the query heads of KV group 0 in turn, until budget_s
+    seconds of oracle time; the per-row cost is fitted as a + b*I (causal
+    scoring and attention grow with the row index) and extrapolated to every
+    row of every head."""
     import numpy as np
     import oracle
     try:
@@ -193,27 +197,31 @@ def cpu_baseline(wl, torch, res, budget_s):
     w = res["workload"]
     q, k, v, tau, _, _ = res["_tensors"]
     sscale, smscale = wl.default_scales(w)
-    h, g = 0, 0
-    kh = k[0, g].float().cpu().numpy().astype(np.float64)
-    vh = v[0, g].float().cpu().numpy().astype(np.float64)
+    G = w.Hq // w.Hkv
+    kh = k[0, 0].float().cpu().numpy().astype(np.float64)
+    vh = v[0, 0].float().cpu().numpy().astype(np.float64)
     nb = w.nb
-    order = [int((j + 0.5) * nb / 8) for j in (3, 7, 1, 5, 0, 2, 4, 6)]
+    bits = max(1, (nb - 1).bit_length())
+    order = [r for r in (int(format(x, f"0{bits}b")[::-1], 2) for x in range(1 << bits)) if r < nb]
+    qh = np.zeros((w.M, w.C))
     times = []
-    t_start = time.time()
-    for big_i in order:
-        qh = np.zeros((w.M, w.C))
+    spent = 0.0
+    for j, big_i in enumerate(order):
+        h = j % G
         rows = slice(big_i * w.block, (big_i + 1) * w.block)
         qh[rows] = q[0, h, rows].float().cpu().numpy()
         t0 = time.perf_counter()
         sc = oracle.block_score_row(qh, kh, big_i, w.block, w.stride, sscale, w.causal)
         keep = oracle.select_row(sc, big_i, float(tau[h]), w.causal)
         oracle.attend_row(qh, kh, vh, keep, big_i, w.block, smscale, w.causal)
-        times.append((big_i, time.perf_counter() - t0))
-        if time.time() - t_start > budget_s and len(times) >= 2:
+        dt = time.perf_counter() - t0
+        qh[rows] = 0.0
+        times.append((big_i, h, dt))
+        spent += dt
+        if spent > budget_s and len(times) >= 2:
             break
-    # causal cost grows ~linearly with I: fit t = a + b*I on the sample
     Is = np.array([t[0] for t in times], dtype=np.float64)
-    ts = np.array([t[1] for t in times])
+    ts = np.array([t[2] for t in times])
     if w.causal and len(times) >= 2 and np.ptp(Is) > 0:
         b, a = np.polyfit(Is, ts, 1)
         per_head = max(a * nb + b * nb * (nb - 1) / 2, ts.mean() * nb)
@@ -225,9 +233,10 @@ def cpu_baseline(wl, torch, res, budget_s):
         "unit": "TFLOP/s (dense-equivalent)",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{len(times)} query-block rows of head 0 (I={[t[0] for t in times]}) of {w.name}, "
-                   f"score+select+attend in float64 NumPy, {ts.sum():.1f}s; extrapolated to "
-                   f"{nb} rows x {w.Hq} heads = {total_s:.0f}s per layer"),
+        "sample": (f"{len(times)} query-block rows (stratified over I = 0..{nb - 1}, query heads 0..{G - 1} in "
+                   f"turn) of {w.name}, score+select+attend in float64 NumPy, {ts.sum():.1f}s of oracle time; "
+                   f"per-row cost fitted as a + b*I and extrapolated to {nb} rows x {w.Hq} heads = "
+                   f"{total_s:.0f}s per layer"),
         "ms_per_step_extrapolated": total_s * 1e3,
     }
 

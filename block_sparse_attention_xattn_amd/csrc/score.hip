@@ -57,22 +57,35 @@ struct ScoreArgs {
 #define XATTN_SCORE_TILE 256
 #endif
 constexpr int SC_TILE = XATTN_SCORE_TILE;   // strided keys x strided queries per tile
-// output sub-tile of one wave, strided keys x strided queries: 64 x 128 (2 x 4
-// MFMA tiles, two waves per SIMD; the default), 64 x 64 (2 x 2, four waves per
-// SIMD; 4/3 of the LDS fragment reads per MFMA) or 128 x 128 (4 x 4, one wave
-// per SIMD with its accumulators in AGPRs). Measured on the 256K layer: 64 x 64
-// about 2% and 128 x 128 about 6% slower than 64 x 128.
-#ifndef XATTN_SCORE_WK
-#define XATTN_SCORE_WK 64
+// Output sub-tile of one wave, strided keys x strided queries (WK x WQ): 64 x 128
+// (2 x 4 MFMA tiles, two waves per SIMD), 64 x 64 (2 x 2, four waves per SIMD;
+// 4/3 of the LDS fragment reads per MFMA) or 128 x 128 (4 x 4, one wave per SIMD
+// with its accumulators in AGPRs). Measured on the 256K layer: the DMA kernel is
+// fastest with 64 x 128 (64 x 64 about 2% and 128 x 128 about 6% slower); the
+// register-staged kernel with 64 x 64 (64 x 128 about 3% slower: its staging
+// registers leave two waves per SIMD too little room).
+#ifndef XATTN_SCORE_DMA_WK
+#define XATTN_SCORE_DMA_WK 64
 #endif
-#ifndef XATTN_SCORE_WQ
-#define XATTN_SCORE_WQ 128
+#ifndef XATTN_SCORE_DMA_WQ
+#define XATTN_SCORE_DMA_WQ 128
 #endif
-constexpr int SC_WK = XATTN_SCORE_WK, SC_WQ = XATTN_SCORE_WQ;
-constexpr int SC_MTK = SC_WK / 32, SC_MTQ = SC_WQ / 32;      // MFMA tiles per wave, each side
-constexpr int SC_WNK = SC_TILE / SC_WK, SC_WNQ = SC_TILE / SC_WQ;  // waves per tile side
-constexpr int SC_NT = 64 * SC_WNK * SC_WNQ;  // threads per workgroup
-constexpr int SC_MINW = SC_NT / 256;         // waves per SIMD the kernel is built for
+#ifndef XATTN_SCORE_REG_WK
+#define XATTN_SCORE_REG_WK 64
+#endif
+#ifndef XATTN_SCORE_REG_WQ
+#define XATTN_SCORE_REG_WQ 64
+#endif
+template <int WK_, int WQ_>
+struct ScWave {
+  static constexpr int WK = WK_, WQ = WQ_;
+  static constexpr int MTK = WK / 32, MTQ = WQ / 32;            // MFMA tiles per wave, each side
+  static constexpr int WNK = SC_TILE / WK, WNQ = SC_TILE / WQ;  // waves per tile side
+  static constexpr int NT = 64 * WNK * WNQ;                     // threads per workgroup
+  static constexpr int MINW = NT / 256;                         // waves per SIMD the kernel is built for
+};
+using ScDma = ScWave<XATTN_SCORE_DMA_WK, XATTN_SCORE_DMA_WQ>;
+using ScReg = ScWave<XATTN_SCORE_REG_WK, XATTN_SCORE_REG_WQ>;
 #ifndef XATTN_SCORE_KC
 #define XATTN_SCORE_KC 64
 #endif
@@ -143,19 +156,19 @@ struct ScoreTile {
 
 // Tile epilogue: per (strided row i, run of RB strided keys) the partial
 // log2-sum-exp of the scaled logits, masked causally and past the last key.
-template <int RB, bool CAUSAL>
-__device__ __forceinline__ void score_epilogue(const ScoreArgs& a, const f32x16 (&acc)[SC_MTK][SC_MTQ],
+template <int RB, bool CAUSAL, class W>
+__device__ __forceinline__ void score_epilogue(const ScoreArgs& a, const f32x16 (&acc)[W::MTK][W::MTQ],
                                                size_t bh, int i0, int j0, int wk, int wq, int l32, int hh) {
   // acc[x][y][r] is strided key j = j0 + WK wk + 32x + 8(r/4) + 4hh + r%4 and
   // strided query i = i0 + WQ wq + 32y + l32; each run of RB keys is reduced.
   float* wsh = a.ws + bh * (size_t)a.NBq * a.NBk * RB;
 #pragma unroll
-  for (int y = 0; y < SC_MTQ; ++y) {
-    const int i = i0 + SC_WQ * wq + 32 * y + l32;
+  for (int y = 0; y < W::MTQ; ++y) {
+    const int i = i0 + W::WQ * wq + 32 * y + l32;
     const int ia = i + a.qoff_s;  // absolute strided row
 #pragma unroll
-    for (int x = 0; x < SC_MTK; ++x) {
-      const int jb = j0 + SC_WK * wk + 32 * x;  // first strided key of this 32-key sub-tile
+    for (int x = 0; x < W::MTK; ++x) {
+      const int jb = j0 + W::WK * wk + 32 * x;  // first strided key of this 32-key sub-tile
       float v[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -211,7 +224,8 @@ __device__ __forceinline__ void score_epilogue(const ScoreArgs& a, const f32x16 
 // instantiation keeps the common loop branch-free) or when the DMA kernel is
 // switched off.
 template <int C, int RB, bool CAUSAL, bool TAIL>
-__global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_bf16_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(ScReg::NT, ScReg::MINW) void score_partials_bf16_kernel(ScoreArgs a) {
+  using W = ScReg;
   static_assert(RB == 2 || RB == 4 || RB == 8 || RB == 16 || RB == 32, "r");
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * SC_OP];
   uint16_t* Ks = smem;               // [2][SC_TILE rows] strided keys (A operand)
@@ -219,7 +233,7 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_bf16_kernel(Sco
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int wk = wave / SC_WNQ, wq = wave % SC_WNQ;
+  const int wk = wave / W::WNQ, wq = wave % W::WNQ;
 
   const ScoreTile tl(a, CAUSAL);
   const size_t bh = tl.bh;
@@ -233,14 +247,14 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_bf16_kernel(Sco
   // Row pointers are formed once; per chunk only a uniform offset changes.
   // Rows past the last strided row (a ragged last tile) are clamped to it: they
   // load valid memory and their outputs are never stored.
-  constexpr int LPT = SC_TILE * SC_CPR / SC_NT;  // 16-byte loads per thread per operand
-  static_assert(LPT * SC_NT == SC_TILE * SC_CPR, "tile load must divide evenly");
+  constexpr int LPT = SC_TILE * SC_CPR / W::NT;  // 16-byte loads per thread per operand
+  static_assert(LPT * W::NT == SC_TILE * SC_CPR, "tile load must divide evenly");
   const uint16_t* kp[LPT];
   const uint16_t* qp[LPT];
   int ktok[LPT], qtok[LPT];  // token of the row's first (Q) / base (K) element
 #pragma unroll
   for (int p = 0; p < LPT; ++p) {
-    const int id = tid + SC_NT * p;
+    const int id = tid + W::NT * p;
     const int row = id / SC_CPR, col = (id % SC_CPR) * 8;
     const int j = min(j0 + row, a.Rk - 1), i = min(i0 + row, a.Rq - 1);
     // antidiagonal: the stride group is read in reverse (row j*S + S-1-s)
@@ -277,37 +291,37 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_bf16_kernel(Sco
   auto store_chunk = [&](int buf, const Stage& r) {
 #pragma unroll
     for (int p = 0; p < LPT; ++p) {
-      const int id = tid + SC_NT * p;
+      const int id = tid + W::NT * p;
       const int row = id / SC_CPR, chunk = id % SC_CPR;
       *reinterpret_cast<u32x4*>(Ks + buf * SC_OP + sc_off(row, chunk)) = r[p];
       *reinterpret_cast<u32x4*>(Qs + buf * SC_OP + sc_off(row, chunk)) = r[LPT + p];
     }
   };
 
-  f32x16 acc[SC_MTK][SC_MTQ];
+  f32x16 acc[W::MTK][W::MTQ];
 #pragma unroll
-  for (int x = 0; x < SC_MTK; ++x)
+  for (int x = 0; x < W::MTK; ++x)
 #pragma unroll
-    for (int y = 0; y < SC_MTQ; ++y) acc[x][y] = f32x16{};
+    for (int y = 0; y < W::MTQ; ++y) acc[x][y] = f32x16{};
 
   auto mma_chunk = [&](int buf) {
     const uint16_t* Kb = Ks + buf * SC_OP;
     const uint16_t* Qb = Qs + buf * SC_OP;
 #pragma unroll
     for (int ks = 0; ks < SC_KC / 16; ++ks) {
-      bf16x8 af[SC_MTK], bfr[SC_MTQ];
+      bf16x8 af[W::MTK], bfr[W::MTQ];
 #pragma unroll
-      for (int x = 0; x < SC_MTK; ++x)
+      for (int x = 0; x < W::MTK; ++x)
         af[x] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(Kb + sc_off(SC_WK * wk + 32 * x + l32, 2 * ks + hh)));
+            bf16x8, *reinterpret_cast<const u32x4*>(Kb + sc_off(W::WK * wk + 32 * x + l32, 2 * ks + hh)));
 #pragma unroll
-      for (int y = 0; y < SC_MTQ; ++y)
+      for (int y = 0; y < W::MTQ; ++y)
         bfr[y] = __builtin_bit_cast(
-            bf16x8, *reinterpret_cast<const u32x4*>(Qb + sc_off(SC_WQ * wq + 32 * y + l32, 2 * ks + hh)));
+            bf16x8, *reinterpret_cast<const u32x4*>(Qb + sc_off(W::WQ * wq + 32 * y + l32, 2 * ks + hh)));
 #pragma unroll
-      for (int x = 0; x < SC_MTK; ++x)
+      for (int x = 0; x < W::MTK; ++x)
 #pragma unroll
-        for (int y = 0; y < SC_MTQ; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
+        for (int y = 0; y < W::MTQ; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
     }
   };
 
@@ -324,7 +338,7 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_bf16_kernel(Sco
     __syncthreads();
   }
 
-  score_epilogue<RB, CAUSAL>(a, acc, bh, i0, j0, wk, wq, l32, hh);
+  score_epilogue<RB, CAUSAL, W>(a, acc, bh, i0, j0, wk, wq, l32, hh);
 }
 
 // Complete stride groups (Mq and Mk multiples of S): the operand tiles go from
@@ -347,8 +361,8 @@ constexpr int SD_KC = 32;                     // contraction elements per chunk
 constexpr int SD_ROW = SD_KC;                 // elements per LDS row
 constexpr int SD_STAGE = 2 * SC_TILE * SD_ROW;  // elements per stage (keys, then queries)
 constexpr int SD_BLK = 1024 / (2 * SD_ROW);   // rows per 1 KiB DMA block (16)
-constexpr int SD_BPW = (SC_TILE / SD_BLK) / (SC_NT / 64);  // DMA blocks per operand per wave
-static_assert(SD_BPW >= 1 && SD_BPW * (SC_NT / 64) * SD_BLK == SC_TILE, "DMA blocks must cover the tile");
+constexpr int SD_BPW = (SC_TILE / SD_BLK) / (ScDma::NT / 64);  // DMA blocks per operand per wave
+static_assert(SD_BPW >= 1 && SD_BPW * (ScDma::NT / 64) * SD_BLK == SC_TILE, "DMA blocks must cover the tile");
 
 __device__ __forceinline__ int sd_off(int row, int chunk) { return row * SD_ROW + 8 * (chunk ^ ((row >> 2) & 3)); }
 
@@ -356,7 +370,8 @@ __device__ __forceinline__ int sd_off(int row, int chunk) { return row * SD_ROW 
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <int C, int RB, bool CAUSAL>
-__global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_dma_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_kernel(ScoreArgs a) {
+  using W = ScDma;
   static_assert(RB == 2 || RB == 4 || RB == 8 || RB == 16 || RB == 32, "r");
   __shared__ __attribute__((aligned(1024))) uint16_t st0[SD_STAGE];
   __shared__ __attribute__((aligned(1024))) uint16_t st1[SD_STAGE];
@@ -365,14 +380,14 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_dma_kernel(Scor
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int wk = wave / SC_WNQ, wq = wave % SC_WNQ;
+  const int wk = wave / W::WNQ, wq = wave % W::WNQ;
   const ScoreTile tl(a, CAUSAL);
   const uint16_t* qh = a.q + tl.bh * a.Mq * C;
   const uint16_t* kh = a.k + tl.bg * a.Mk * C;
   const int S = a.S;
   const int n_chunks = S * C / SD_KC;
 
-  // this lane's piece of DMA block (wave + (SC_NT/64) u): row 16 blk + lane/4,
+  // this lane's piece of DMA block (wave + (NT/64) u): row 16 blk + lane/4,
   // LDS slot lane % 4, holding the row's piece (lane % 4) ^ ((row / 4) % 4);
   // rows past the last strided row are clamped (never stored)
   const int piece = (lane & 3) ^ ((lane >> 4) & 3);
@@ -380,7 +395,7 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_dma_kernel(Scor
   const uint16_t* qp[SD_BPW];
 #pragma unroll
   for (int u = 0; u < SD_BPW; ++u) {
-    const int row = SD_BLK * (wave + (SC_NT / 64) * u) + (lane >> 2);
+    const int row = SD_BLK * (wave + (W::NT / 64) * u) + (lane >> 2);
     const int j = min(tl.j0 + row, a.Rk - 1), i = min(tl.i0 + row, a.Rq - 1);
     // antidiagonal: the stride group is read in reverse (row j*S + S-1-s)
     kp[u] = kh + ((size_t)j * S + (a.diagonal ? 0 : S - 1)) * C + 8 * piece;
@@ -392,7 +407,7 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_dma_kernel(Scor
     const ptrdiff_t koff = (ptrdiff_t)kdir * srow * C + col0, qoff = (ptrdiff_t)srow * C + col0;
 #pragma unroll
     for (int u = 0; u < SD_BPW; ++u) {
-      const int blk = wave + (SC_NT / 64) * u;
+      const int blk = wave + (W::NT / 64) * u;
       __builtin_amdgcn_global_load_lds(kp[u] + koff, (__attribute__((address_space(3))) void*)(stg + blk * 1024 / 2),
                                        16, 0, 0);
       __builtin_amdgcn_global_load_lds(qp[u] + qoff,
@@ -401,11 +416,11 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_dma_kernel(Scor
     }
   };
 
-  f32x16 acc[SC_MTK][SC_MTQ];
+  f32x16 acc[W::MTK][W::MTQ];
 #pragma unroll
-  for (int x = 0; x < SC_MTK; ++x)
+  for (int x = 0; x < W::MTK; ++x)
 #pragma unroll
-    for (int y = 0; y < SC_MTQ; ++y) acc[x][y] = f32x16{};
+    for (int y = 0; y < W::MTQ; ++y) acc[x][y] = f32x16{};
 
   // chunk c sits in stage cur; the stage nxt (chunk c - 1, done) is refilled
   // with chunk c + 3 (past the end: the last chunk again, never read)
@@ -418,18 +433,18 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_dma_kernel(Scor
     __builtin_amdgcn_sched_barrier(0);  // keep the refill ahead of this chunk's work
 #pragma unroll
     for (int ks = 0; ks < SD_KC / 16; ++ks) {
-      bf16x8 af[SC_MTK], bfr[SC_MTQ];
+      bf16x8 af[W::MTK], bfr[W::MTQ];
 #pragma unroll
-      for (int x = 0; x < SC_MTK; ++x)
-        af[x] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + sd_off(SC_WK * wk + 32 * x + l32, 2 * ks + hh)));
+      for (int x = 0; x < W::MTK; ++x)
+        af[x] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + sd_off(W::WK * wk + 32 * x + l32, 2 * ks + hh)));
 #pragma unroll
-      for (int y = 0; y < SC_MTQ; ++y)
+      for (int y = 0; y < W::MTQ; ++y)
         bfr[y] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + SC_TILE * SD_ROW +
-                                                                           sd_off(SC_WQ * wq + 32 * y + l32, 2 * ks + hh)));
+                                                                           sd_off(W::WQ * wq + 32 * y + l32, 2 * ks + hh)));
 #pragma unroll
-      for (int x = 0; x < SC_MTK; ++x)
+      for (int x = 0; x < W::MTK; ++x)
 #pragma unroll
-        for (int y = 0; y < SC_MTQ; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
+        for (int y = 0; y < W::MTQ; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
     }
   };
 
@@ -444,7 +459,7 @@ __global__ __launch_bounds__(SC_NT, SC_MINW) void score_partials_dma_kernel(Scor
     step(c + 3, st3, st2);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing refills have landed
-  score_epilogue<RB, CAUSAL>(a, acc, tl.bh, tl.i0, tl.j0, wk, wq, l32, hh);
+  score_epilogue<RB, CAUSAL, W>(a, acc, tl.bh, tl.i0, tl.j0, wk, wq, l32, hh);
 }
 
 // fp32 inputs: one thread per (strided row i, key block J), plain FMA.
@@ -522,15 +537,15 @@ static hipError_t launch_partials_crt(const Shape& s, const ScoreArgs& a, hipStr
   const unsigned grid = (unsigned)((size_t)s.B * s.Hq * a.pairs);
   if (XATTN_SCORE_DMA && !TAIL && (s.stride * C / SD_KC) % 4 == 0) {
     if (s.causal)
-      hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, true>), dim3(grid), dim3(SC_NT), 0, st, a);
+      hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, true>), dim3(grid), dim3(ScDma::NT), 0, st, a);
     else
-      hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, false>), dim3(grid), dim3(SC_NT), 0, st, a);
+      hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, false>), dim3(grid), dim3(ScDma::NT), 0, st, a);
     return hipGetLastError();
   }
   if (s.causal)
-    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, true, TAIL>), dim3(grid), dim3(SC_NT), 0, st, a);
+    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, true, TAIL>), dim3(grid), dim3(ScReg::NT), 0, st, a);
   else
-    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, false, TAIL>), dim3(grid), dim3(SC_NT), 0, st, a);
+    hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, false, TAIL>), dim3(grid), dim3(ScReg::NT), 0, st, a);
   return hipGetLastError();
 }
 
