@@ -94,4 +94,8 @@ __device__ __forceinline__ uint32_t xcc_id() {
 
 __device__ __forceinline__ uint32_t xcd_group4(uint32_t w, uint32_t n) { return xcd_map(w, n, 4); }
 
+// s_waitcnt immediate that waits on the vector-memory counter only: at most n
+// loads (including LDS DMA) of this wave outstanding.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 }  // namespace xattn

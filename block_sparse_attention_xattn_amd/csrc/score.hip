@@ -366,9 +366,6 @@ static_assert(SD_BPW >= 1 && SD_BPW * (ScDma::NT / 64) * SD_BLK == SC_TILE, "DMA
 
 __device__ __forceinline__ int sd_off(int row, int chunk) { return row * SD_ROW + 8 * (chunk ^ ((row >> 2) & 3)); }
 
-// s_waitcnt with only the vector-memory counter: at most n loads outstanding.
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 template <int C, int RB, bool CAUSAL>
 __global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_kernel(ScoreArgs a) {
   using W = ScDma;
