@@ -8,12 +8,22 @@
 //   ascending; prefix masses c_k in float64, T = c_n; keep the first
 //   k* = min{k >= 0 : c_k >= tau * T} (tau >= 1 keeps all); then add J = I.
 //
-// Implementation: each candidate becomes a 64-bit key (score bits << 32 |
-// ~J); block scores are non-negative, so their IEEE bits order like the
-// values and one descending integer sort yields (score desc, J asc). Bitonic
-// sort in LDS, float64 prefix sums (per-thread runs + wave shuffles + a
-// 4-wave combine), a count of prefixes below tau*T, then flags and an
-// ascending compaction to kv_idx.
+// Implementation (default): a radix select of the cut, no sort. The kept set is
+// the prefix of the (score desc, J asc) order that first reaches tau * T, so it
+// is every candidate scoring above the cut score v* plus the first t* (by J)
+// of those scoring exactly v*, where v* is the largest score whose tail mass
+// F(v*) = mass(score >= v*) reaches tau * T. Block scores are non-negative,
+// so their IEEE bits order like the values: four passes over 8-bit digits of
+// the bits (most significant first) histogram the candidate mass per digit
+// within the digits chosen so far, and pick the digit where the mass counted
+// from the top first reaches tau * T. Masses are 64-bit fixed-point integers
+// (score * 2^50), so the sums are exact and independent of the order of the
+// atomic adds; they differ from float64 prefix sums by at most about 1e-12 of
+// the row total, so a decision can differ only for a block whose cumulative
+// mass lies that close to tau * T. Then t* = ceil((tau*T - mass above v*) /
+// v*), the ties ranked by a scan over J, flags, and an ascending compaction.
+// Build option XATTN_SELECT_SORT=1: a bitonic sort of (score bits << 32 | ~J)
+// keys with float64 prefix sums instead.
 #include "common.h"
 #include "kernels.h"
 #include "score_row.h"
@@ -51,8 +61,21 @@ __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
   return x;
 }
 
+#ifndef XATTN_SELECT_SORT
+#define XATTN_SELECT_SORT 0
+#endif
+
 struct SelectLds {
+#if XATTN_SELECT_SORT
   uint64_t keys[SEL_MAX];
+#else
+  float sc[SEL_MAX];              // candidate scores by J
+  unsigned long long hist[256];   // fixed-point mass per digit
+  unsigned int hcnt[256];         // candidates per digit (last pass)
+  unsigned long long wsum64[4];
+  unsigned int cut[2];            // digits chosen so far; tie count
+  unsigned long long cut_above;   // mass above the digits chosen so far
+#endif
   uint8_t flags[SEL_MAX];
   double wsum[4];
   int wcnt[4];
@@ -91,6 +114,7 @@ __device__ void compact_row(const uint8_t* flags, int NB, size_t row, uint8_t* m
   if (tid == 0) kv_cnt[row] = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
 }
 
+#if XATTN_SELECT_SORT
 // With keys[0, npad) filled (keys[p] = 0 for p >= n), flags[0, NB) zeroed and
 // a barrier passed: sort, cut at tau, add the diagonal, write the row.
 __device__ void select_from_keys(SelectLds& sh, int n, int npad, int NB, int I, float tau, size_t row,
@@ -150,6 +174,111 @@ __device__ void select_from_keys(SelectLds& sh, int n, int npad, int NB, int I, 
   compact_row(flags, NB, row, mask, kv_idx, kv_cnt, sh.wcnt);
 }
 
+#endif
+
+#if !XATTN_SELECT_SORT
+__device__ __forceinline__ unsigned long long sel_fx(float s) {
+  return __double2ull_rz((double)s * 0x1p50);  // scores are in [0, 1]
+}
+
+// Inclusive scan of a 64-bit value over the 256 threads; every thread also
+// gets the total. Ends with a barrier, so wsum may be reused afterwards.
+__device__ __forceinline__ unsigned long long block_scan_u64(unsigned long long x, unsigned long long* wsum,
+                                                             unsigned long long& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) x += wsum[w];
+  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return x;
+}
+
+// With sc[0, n) filled, flags[0, NB) zeroed and a barrier passed: find the
+// cut, set the kept flags, add the diagonal, write the row.
+__device__ void select_radix(SelectLds& sh, int n, int NB, int I, float tau, size_t row, uint8_t* mask,
+                             int32_t* kv_idx, int32_t* kv_cnt) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint8_t* flags = sh.flags;
+  if (tau >= 1.f) {
+    for (int p = tid; p < n; p += 256) flags[p] = 1;
+  } else {
+    unsigned long long thr = 0;  // ceil(tau * T) in fixed point
+    unsigned int prefix = 0;
+    unsigned long long above = 0;
+    bool none = false;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      sh.hist[tid] = 0ull;
+      sh.hcnt[tid] = 0u;
+      __syncthreads();
+      for (int p = tid; p < n; p += 256) {
+        const float v = sh.sc[p];
+        const unsigned int u = __float_as_uint(v);
+        if (pass == 0 || (u >> (shift + 8)) == prefix) {
+          const int d = (u >> shift) & 255;
+          atomicAdd(&sh.hist[d], sel_fx(v));
+          if (pass == 3) atomicAdd(&sh.hcnt[d], 1u);
+        }
+      }
+      __syncthreads();
+      // thread t holds digit 255 - t: the inclusive scan is the mass of the
+      // digits from the top down to this one
+      const int d = 255 - tid;
+      const unsigned long long h = sh.hist[d];
+      unsigned long long total;
+      const unsigned long long incl = block_scan_u64(h, sh.wsum64, total);
+      if (pass == 0) {
+        // total = T; tau * T <= 0 keeps no candidate
+        thr = (unsigned long long)ceil((double)tau * (double)total);
+        if (tau <= 0.f || total == 0ull || thr == 0ull) {
+          none = true;
+          break;
+        }
+      }
+      if (above + incl >= thr && above + incl - h < thr) {
+        sh.cut[0] = (prefix << 8) | (unsigned int)d;
+        sh.cut_above = above + incl - h;
+        if (pass == 3) sh.cut[1] = sh.hcnt[d];
+      }
+      __syncthreads();
+      prefix = sh.cut[0];
+      above = sh.cut_above;
+    }
+    if (!none) {
+      // v* = prefix; keep the first t* ties by J
+      const unsigned long long fv = sel_fx(__uint_as_float(prefix));
+      const unsigned int ties = sh.cut[1];
+      const unsigned long long need = thr - above;  // > 0
+      unsigned int tstar = fv ? (unsigned int)((need + fv - 1) / fv) : ties;
+      tstar = tstar > ties ? ties : tstar;
+      const int per = (n + 255) / 256;
+      const int p0 = min(tid * per, n), p1 = min(p0 + per, n);
+      int mine = 0;
+      for (int p = p0; p < p1; ++p) mine += __float_as_uint(sh.sc[p]) == prefix;
+      const int incl_t = wave_incl_scan_i(mine, lane);
+      if (lane == 63) sh.wcnt[wave] = incl_t;
+      __syncthreads();
+      int rank = incl_t - mine;
+      for (int w = 0; w < wave; ++w) rank += sh.wcnt[w];
+      for (int p = p0; p < p1; ++p) {
+        const unsigned int u = __float_as_uint(sh.sc[p]);
+        if (u > prefix) flags[p] = 1;
+        else if (u == prefix) flags[p] = (unsigned int)(rank++) < tstar;
+      }
+    }
+  }
+  if (tid == 0) flags[I] = 1;  // diagonal block
+  __syncthreads();
+  compact_row(flags, NB, row, mask, kv_idx, kv_cnt, sh.wcnt);
+}
+#endif
+
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   __shared__ SelectLds sh;
   const int tid = threadIdx.x;
@@ -162,10 +291,18 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   int npad = 1;
   while (npad < n) npad <<= 1;
   const float* srow = a.scores + row * NB;
+#if XATTN_SELECT_SORT
   for (int p = tid; p < npad; p += 256) sh.keys[p] = p < n ? sel_key(srow[p], p) : 0;
   for (int p = tid; p < NB; p += 256) sh.flags[p] = 0;
   __syncthreads();
   select_from_keys(sh, n, npad, NB, Ia, a.tau.v[h], row, a.mask, a.kv_idx, a.kv_cnt);
+#else
+  (void)npad;
+  for (int p = tid; p < n; p += 256) sh.sc[p] = srow[p];
+  for (int p = tid; p < NB; p += 256) sh.flags[p] = 0;
+  __syncthreads();
+  select_radix(sh, n, NB, Ia, a.tau.v[h], row, a.mask, a.kv_idx, a.kv_cnt);
+#endif
 }
 
 // Fused stage 2 + 3: the row's block scores are computed from the partials
@@ -199,6 +336,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(FusedArgs a) {
   const float* L = a.ws + (bh * (size_t)a.NBq + I) * (size_t)NB * RB;
   float* orow = a.scores + row * NB;
   for (int p = tid; p < NB; p += 256) sh.flags[p] = 0;
+#if XATTN_SELECT_SORT
   for (int p = n + tid; p < npad; p += 256) sh.keys[p] = 0;
   block_score_row<RB>(L, n, NB, rows, shs, [&](int J, float sc) {
     orow[J] = sc;
@@ -206,6 +344,15 @@ __global__ __launch_bounds__(256) void score_select_kernel(FusedArgs a) {
   });
   __syncthreads();
   select_from_keys(sh, n, npad, NB, Ia, a.tau.v[h], row, a.mask, a.kv_idx, a.kv_cnt);
+#else
+  (void)npad;
+  block_score_row<RB>(L, n, NB, rows, shs, [&](int J, float sc) {
+    orow[J] = sc;
+    if (J < n) sh.sc[J] = sc;
+  });
+  __syncthreads();
+  select_radix(sh, n, NB, Ia, a.tau.v[h], row, a.mask, a.kv_idx, a.kv_cnt);
+#endif
 }
 
 hipError_t launch_score_select(const Shape& s, const float* ws, float* block_scores, const TauArray& tau,
