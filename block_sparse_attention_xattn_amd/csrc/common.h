@@ -92,8 +92,6 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 7u;
 }
 
-__device__ __forceinline__ uint32_t xcd_group4(uint32_t w, uint32_t n) { return xcd_map(w, n, 4); }
-
 // s_waitcnt immediate that waits on the vector-memory counter only: at most n
 // loads (including LDS DMA) of this wave outstanding.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
