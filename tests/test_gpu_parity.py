@@ -153,6 +153,49 @@ def test_select_matches_oracle_on_same_scores(xa, tau, causal):
     check_index(m, idx.cpu().numpy(), cnt.cpu().numpy())
 
 
+def _cut_case_rows(nb):
+    """Rows whose cut is decided exactly in float64 and in any exact fixed-point
+    sum (scores that are short binary fractions): ties, a cut landing exactly
+    on tau * T, one dominant block, scores far below 2^-50, an all-zero row."""
+    rows = []
+    rows.append(np.full(nb, 1.0 / nb))                   # all tied
+    r = np.full(nb, 0.125 / (nb - 1)); r[7] = 0.875       # one dominant block
+    rows.append(r)
+    r = np.zeros(nb); r[10:18] = 1.0 / 16; r[20:52] = 1.0 / 64   # big block run, then a tie run
+    rows.append(r)
+    r = np.where(np.arange(nb) % 2 == 0, 2.0 ** -60, 1.0 / 32)   # tiny scores beside large ones
+    rows.append(r)
+    rows.append(np.zeros(nb))                              # no mass: only the diagonal
+    return rows
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_select_exact_cuts(xa, causal):
+    # per-head tau: 0.5 and 0.625 land exactly on cumulative masses of these rows
+    # (c_k = tau * T), 0.51 and 0.85 between them, 0.99 near the total
+    nb = 64
+    taus = [0.5, 0.51, 0.625, 0.85, 0.99, 0.0, 1.0]
+    cases = _cut_case_rows(nb)
+    raw = np.zeros((1, len(taus), nb, nb))
+    for h in range(len(taus)):
+        for i in range(nb):
+            row = cases[(i + h) % len(cases)].copy()
+            if causal:
+                # the causal row I sees blocks 0..I: place the pattern's last
+                # I+1 entries there (tail mass dropped)
+                row = np.concatenate([row[nb - (i + 1):], np.zeros(nb - (i + 1))])
+            raw[0, h, i] = row
+    raw = raw.astype(np.float32).astype(np.float64)  # the oracle sees the GPU's float32 scores
+    scores = torch.from_numpy(raw.astype(np.float32))
+    mask, idx, cnt = xa.xattn_select(scores.to(DEV), taus, 128, 8, causal, Hkv=1)
+    torch.cuda.synchronize()
+    ref = oracle.select(raw, taus, causal)
+    m = mask.cpu().numpy()
+    bad = np.argwhere(m.astype(bool) != ref.astype(bool))
+    assert bad.size == 0, bad[:8]
+    check_index(m, idx.cpu().numpy(), cnt.cpu().numpy())
+
+
 # ------------------------------------------------------------------ end to end
 
 E2E_CASES = [
