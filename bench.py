@@ -145,6 +145,9 @@ def run_workload(xa, wl, torch, name, steps, warmup, dense_steps):
     density = float(kv_cnt.sum().item()) / cand
     attn_flops = useful_attn_flops(kv_cnt, w)
     dense_flops = w.dense_flops
+    # selection bytes (HBM-bound stage): the candidates' block scores read, the
+    # mask row, the kept indices and the count written
+    select_bytes = 4.0 * cand + B * Hq * nb * nb + 4.0 * float(kv_cnt.sum().item()) + 4.0 * B * Hq * nb
     log(f"[{name}] step {ms:.3f} ms (xattn_prefill)  stage calls " + " ".join(f"{k}={v:.3f}" for k, v in st.items())
         + f"  density={density * 100:.2f}%")
 
@@ -171,6 +174,7 @@ def run_workload(xa, wl, torch, name, steps, warmup, dense_steps):
         "density": density,
         "attn_flops": attn_flops,
         "score_flops": score_flops(w),
+        "select_bytes": select_bytes,
         "dense_flops": dense_flops,
         "tflops": dense_flops / ms / 1e9,
         "dense_ms": dense_ms,
@@ -393,7 +397,8 @@ def main():
              "stages_ms": {k: round(v, 4) for k, v in r["stages_ms"].items()},
              "density": round(r["density"], 5),
              "selected_tile_tflops": round(r["attn_flops"] / (r["stages_ms"]["bsa_fwd"] * 1e-3) / 1e12, 2),
-             "score_tflops": round(r["score_flops"] / (r["stages_ms"]["xattn_score"] * 1e-3) / 1e12, 2)}
+             "score_tflops": round(r["score_flops"] / (r["stages_ms"]["xattn_score"] * 1e-3) / 1e12, 2),
+             "select_gbs": round(r["select_bytes"] / (r["stages_ms"]["xattn_select"] * 1e-3) / 1e9, 1)}
         if r["dense_ms"]:
             d["dense_fwd_ms"] = round(r["dense_ms"], 3)
             d["dense_fwd_tflops"] = round(r["dense_flops"] / r["dense_ms"] / 1e9, 2)
