@@ -110,6 +110,8 @@ SCORE_CASES = [
     (1, 2, 1, 512, 128, 128, 4, True, torch.bfloat16, False),    # r = 32
     (1, 2, 1, 512, 64, 64, 32, True, torch.bfloat16, False),     # r = 2
     (1, 1, 1, 256, 128, 128, 32, False, torch.bfloat16, False),  # r = 4, R < one tile
+    (1, 2, 1, 512, 64, 64, 2, True, torch.bfloat16, False),      # S*C = 128: four 32-element chunks
+    (1, 2, 2, 768, 128, 64, 2, False, torch.bfloat16, False),    # S*C = 256, 1.5 tiles of strided rows
     (1, 1, 1, 1024, 64, 64, 8, True, torch.float32, True),       # the tiny fp32 workload
     (1, 2, 1, 512, 128, 128, 16, False, torch.float32, False),
 ]
