@@ -19,19 +19,13 @@
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 puts one query per lane, so the
 //    row max/sum is an in-lane reduction plus one exchange between the wave
 //    halves; P^T stays in registers and feeds O^T += V^T P^T directly, with V^T
-//    fragments taken from row-major LDS by the transposing LDS read (or, as a
-//    build option, from a V^T tile transposed on its way into LDS);
+//    fragments taken from row-major LDS by the transposing LDS read;
 //  * online softmax in the log2 domain in fp32; P rounded to bf16 for the PV
 //    product; O normalised once at the end and rounded to bf16 (RNE).
 // f32 path: one thread per query row with fp32 FMA (small problems only).
 #include "common.h"
 #include "kernels.h"
 
-// 1: raise wave priority around the MFMA blocks (s_setprio), so a wave issuing
-// matrix work is preferred over one in its softmax phase on the same SIMD
-#ifndef XATTN_ATTN_SETPRIO
-#define XATTN_ATTN_SETPRIO 0
-#endif
 // Sparse workgroups pair neighbouring rows of a head (one K/V tile load serves
 // both rows of the union list) once a head has at least this many query blocks;
 // shorter rows keep one row per workgroup.
@@ -56,16 +50,6 @@
 // sparse kernel (see xcd_map)
 #ifndef XATTN_SPARSE_ROWS_PER_XCD_LOG2
 #define XATTN_SPARSE_ROWS_PER_XCD_LOG2 0
-#endif
-
-// 1: V sub-tiles are transposed on their way into LDS (8 row dwords per lane,
-// repacked into two 16-byte V^T pieces), so each V^T fragment is one 16-byte
-// LDS read; 0: V stays row-major and fragments come from the transposing LDS
-// read (two 8-byte reads per fragment). Measured: 1 is about 10% slower here
-// (more, smaller global loads; the compiler waits on each wide read right at
-// its MFMA), so 0 is the default.
-#ifndef XATTN_VT_LDS
-#define XATTN_VT_LDS 0
 #endif
 
 // k-steps of K fragments read from LDS ahead of their MFMAs
@@ -114,16 +98,6 @@ struct AttnLds {
   __device__ static int v_off(int row, int byte_in_row) {
     return row * ROW_B + (byte_in_row ^ (64 * ((row / ROWS_PER_256) % (C / 32))));
   }
-  // Transposed V sub-tile (XATTN_VT_LDS): row c holds the KT keys of head
-  // dimension c (2 KT = 128 bytes), as 8 chunks of 16 bytes. Chunk ch holds the
-  // 8 keys that half ch % 2 of a wave feeds into one MFMA k-step of the 16-key
-  // group ch / 2: keys 16 (ch / 2) + 4 (ch % 2) + {0..3, 8..11}, the order in
-  // which the S^T accumulator rows reach a lane. Chunks are XOR-permuted by the
-  // row pair, so 16 consecutive rows at one chunk (a fragment read) cover 256
-  // distinct bytes.
-  static constexpr int VT_ROW_B = 2 * KT;
-  __device__ static int vt_off(int c, int ch) { return c * VT_ROW_B + 16 * (ch ^ ((c >> 1) & 7)); }
-  __device__ static int vt_key(int ch, int e) { return 16 * (ch >> 1) + 8 * (e >> 2) + 4 * (ch & 1) + (e & 3); }
 };
 
 // Workgroup modes: what the 4 or 8 waves of one workgroup cover.
@@ -179,12 +153,6 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   constexpr int DN = C / 32;                  // 32-wide d tiles of O^T
   constexpr int DEPTH = SLOTS == 2 && RPW == 32 ? 2 : 1;  // sub-tiles in flight in registers
   static_assert(CHUNKS % NT == 0, "tile load must divide evenly");
-  // transposed V: a unit is 8 keys x 2 head dims, fetched as 8 row dwords
-  constexpr int NCP = C / 2;                  // head-dim pairs
-  constexpr int VUNITS = 8 * NCP;             // units per sub-tile (8 chunks per V^T row)
-  constexpr int PER_V = (VUNITS + NT - 1) / NT;
-  constexpr bool VT = XATTN_VT_LDS != 0;
-  static_assert(L::KT == 64, "V^T chunks assume 64-key sub-tiles");
 
   unsigned char* Ks = smem;                      // [2][KT rows][2C bytes], swizzled
   unsigned char* Vs = smem + 2 * L::TILE_B;      // [2][KT rows][2C bytes], swizzled
@@ -364,12 +332,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
     return live;
   };
 
-  // K chunks (16 bytes of one key row) and V: the same chunks (row-major LDS)
-  // or, for V^T, per unit the head-dim pair's dword of 8 key rows
+  // this thread's 16-byte K and V chunks of a sub-tile
   struct Stage {
     u32x4 k[PER_T];
-    u32x4 v[VT ? 1 : PER_T];
-    uint32_t vt[VT ? PER_V : 1][8];
+    u32x4 v[PER_T];
   };
   auto load_tile = [&](int k0, Stage& r) {
 #pragma unroll
@@ -380,23 +346,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
       // masked out of the softmax
       const size_t kr = KTAIL ? (size_t)min(k0 + row, a.Mk - 1) : (size_t)(k0 + row);
       r.k[p] = *reinterpret_cast<const u32x4*>(kh + kr * C + col);
-      if constexpr (!VT) r.v[p] = *reinterpret_cast<const u32x4*>(vh + kr * C + col);
-    }
-    if constexpr (VT) {
-      // unit u = (chunk ch, head-dim pair i): the lanes of a wave read whole
-      // key rows (consecutive pairs i), one row per load
-#pragma unroll
-      for (int p = 0; p < PER_V; ++p) {
-        const int u = tid + p * NT;
-        if (VUNITS % NT != 0 && u >= VUNITS) continue;
-        const int i = u % NCP, ch = u / NCP;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = k0 + L::vt_key(ch, e);
-          const size_t kr = KTAIL ? (size_t)min(key, a.Mk - 1) : (size_t)key;
-          r.vt[p][e] = *reinterpret_cast<const uint32_t*>(vh + kr * C + 2 * i);
-        }
-      }
+      r.v[p] = *reinterpret_cast<const u32x4*>(vh + kr * C + col);
     }
   };
   auto store_tile = [&](int buf, const Stage& r) {
@@ -405,30 +355,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
       const int c = tid + p * NT;
       const int row = c / (C / 8), chunk = c % (C / 8);
       *reinterpret_cast<u32x4*>(Ks + buf * L::TILE_B + L::k_off(row, chunk)) = r.k[p];
-      if constexpr (!VT)
-        *reinterpret_cast<u32x4*>(Vs + buf * L::TILE_B + L::v_off(row, 16 * chunk)) = r.v[p];
-    }
-    if constexpr (VT) {
-#pragma unroll
-      for (int p = 0; p < PER_V; ++p) {
-        const int u = tid + p * NT;
-        if (VUNITS % NT != 0 && u >= VUNITS) continue;
-        const int i = u % NCP, ch = u / NCP;
-        // the low halves form V^T row 2i, the high halves row 2i + 1
-        u32x4 lo, hi;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t x = r.vt[p][2 * j], y = r.vt[p][2 * j + 1];
-          lo[j] = (x & 0xFFFFu) | (y << 16);
-          hi[j] = (x >> 16) | (y & 0xFFFF0000u);
-        }
-        // lanes 8..15 of each 16 write the odd row first, so every 16-lane
-        // group of a write covers 256 distinct bytes
-        const bool odd_first = (i >> 3) & 1;
-        unsigned char* Vb = Vs + buf * L::TILE_B;
-        *reinterpret_cast<u32x4*>(Vb + L::vt_off(2 * i + (odd_first ? 1 : 0), ch)) = odd_first ? hi : lo;
-        *reinterpret_cast<u32x4*>(Vb + L::vt_off(2 * i + (odd_first ? 0 : 1), ch)) = odd_first ? lo : hi;
-      }
+      *reinterpret_cast<u32x4*>(Vs + buf * L::TILE_B + L::v_off(row, 16 * chunk)) = r.v[p];
     }
   };
 
@@ -443,7 +370,6 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
     f32x16 sacc[QT][2];
 #pragma unroll
     for (int y = 0; y < QT; ++y) sacc[y][0] = sacc[y][1] = f32x16{};
-    if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);  // MFMA issue first on the SIMD
     // K fragments are read XATTN_KBATCH k-steps at a time ahead of their MFMAs
     constexpr int KB = XATTN_KBATCH < KK ? XATTN_KBATCH : KK;
 #pragma unroll
@@ -465,7 +391,6 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
 #pragma unroll
           for (int y = 0; y < QT; ++y) sacc[y][n] = mfma32x32x16(ka[u][n], qf[y][k0b + u], sacc[y][n]);
     }
-    if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
     bf16x8 pb[QT][4];
 #pragma unroll
     for (int y = 0; y < QT; ++y) {
@@ -518,27 +443,19 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
 
     // O^T[d][q] += V^T[d][key] P^T[key][q] over 16-key chunks tc
     const int G16 = lane >> 4, s16 = lane & 15;
-    if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int tc = 0; tc < 4; ++tc) {
 #pragma unroll
       for (int d = 0; d < DN; ++d) {
-        bf16x8 vf;
-        if constexpr (VT) {
-          // V^T[32d + l32][keys of chunk 2tc + hh]: one 16-byte read
-          vf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(Vb + L::vt_off(32 * d + l32, 2 * tc + hh)));
-        } else {
-          const int vrow = 16 * tc + 4 * (G16 >> 1) + (s16 >> 2);
-          const int vbyte = 2 * (32 * d + 16 * (G16 & 1) + 4 * (s16 & 3));
-          const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow, vbyte)));
-          const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow + 8, vbyte)));
-          vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
+        const int vrow = 16 * tc + 4 * (G16 >> 1) + (s16 >> 2);
+        const int vbyte = 2 * (32 * d + 16 * (G16 & 1) + 4 * (s16 & 3));
+        const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow, vbyte)));
+        const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow + 8, vbyte)));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int y = 0; y < QT; ++y) o[y][d] = mfma32x32x16(vf, pb[y][tc], o[y][d]);
       }
     }
-    if (XATTN_ATTN_SETPRIO) __builtin_amdgcn_s_setprio(0);
   };
 
   __syncthreads();  // block list visible
