@@ -6,8 +6,9 @@
 // strided rows are real (fewer than RB only in a partial last query block) and
 // candidates are J < n_cand.
 // lse_t = log2 sum_J 2^L[J][t]; score[J] = (1/rows) sum_{t<rows} 2^(L[J][t] - lse_t).
-// emit(J, score) is called once for every J in [0, NB) (0 for non-candidates).
-// Needs 256 threads and the given LDS scratch.
+// emit(J, score) is called once for every J in [0, NB) (0 for non-candidates),
+// from some thread of the workgroup. Needs 256 threads and the given LDS
+// scratch; callers synchronise before reading what emit wrote.
 #pragma once
 
 #include "common.h"
@@ -20,8 +21,11 @@ struct ScoreRowLds {
   float lse[32];
 };
 
+// Long rows: thread = key block J (strided by 256), the RB partials of J read
+// as one vector; per t an online log2-sum-exp over the thread's blocks, then
+// across the wave and the four waves.
 template <int RB, class Emit>
-__device__ __forceinline__ void block_score_row(const float* L, int n_cand, int NB, int rows,
+__device__ __forceinline__ void block_score_row_long(const float* L, int n_cand, int NB, int rows,
                                                 ScoreRowLds& sh, Emit&& emit) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // pass 1: per strided row t, log2-sum-exp over candidate blocks
@@ -88,6 +92,67 @@ __device__ __forceinline__ void block_score_row(const float* L, int n_cand, int 
     }
     emit(J, sc);
   }
+}
+
+// Short rows (the many early rows of a causal layer), where the fixed cost of
+// the long form's RB wave-wide reductions dominates. Thread layout: t = tid %
+// RB (strided row), jl = tid / RB (one of 256/RB key-block lanes); a wave reads
+// 64/RB consecutive key-block rows of RB floats, i.e. 256 contiguous bytes. The
+// per-t reductions over key blocks run over the lanes sharing t (shuffles at
+// offsets RB .. 32, then four waves through LDS) as a max and then a sum of
+// 2^(x - max), and the block sums over t run over RB adjacent lanes.
+template <int RB, class Emit>
+__device__ __forceinline__ void block_score_row_short(const float* L, int n_cand, int NB, int rows,
+                                                      ScoreRowLds& sh, Emit&& emit) {
+  static_assert(RB >= 2 && RB <= 32 && (RB & (RB - 1)) == 0, "RB");
+  constexpr int JL = 256 / RB;  // key-block lanes
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t = tid % RB, jl = tid / RB;
+  const bool live = t < rows;  // rows past the end were never written
+  // pass 1: lse_t = log2 sum_J 2^L[J][t], as a max then a sum of 2^(x - max)
+  float m = -INFINITY;
+  if (live)
+    for (int J = jl; J < n_cand; J += JL) m = fmaxf(m, L[(size_t)J * RB + t]);
+#pragma unroll
+  for (int off = RB; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if (lane < RB) sh.red_m[wave][lane] = m;
+  __syncthreads();
+  const float mt = fmaxf(fmaxf(sh.red_m[0][t], sh.red_m[1][t]), fmaxf(sh.red_m[2][t], sh.red_m[3][t]));
+  float s = 0.f;
+  if (live && mt != -INFINITY)
+    for (int J = jl; J < n_cand; J += JL) s += fast_exp2(L[(size_t)J * RB + t] - mt);
+#pragma unroll
+  for (int off = RB; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
+  if (lane < RB) sh.red_s[wave][lane] = s;
+  __syncthreads();
+  const float st = (sh.red_s[0][t] + sh.red_s[1][t]) + (sh.red_s[2][t] + sh.red_s[3][t]);
+  const float lse = (mt == -INFINITY) ? -INFINITY : mt + log2f(st);
+  // pass 2: score[J] = (1/rows) sum_t 2^(L[J][t] - lse_t), summed over the RB
+  // adjacent lanes of key block J (a uniform trip count keeps the shuffles
+  // converged)
+  const float inv_r = 1.f / (float)rows;
+  const int iters = (NB + JL - 1) / JL;
+  for (int it = 0; it < iters; ++it) {
+    const int J = jl + it * JL;
+    float e = 0.f;
+    if (J < n_cand && live && lse != -INFINITY) e = fast_exp2(L[(size_t)J * RB + t] - lse);
+#pragma unroll
+    for (int off = 1; off < RB; off <<= 1) e += __shfl_xor(e, off, 64);
+    if (t == 0 && J < NB) emit(J, J < n_cand ? e * inv_r : 0.f);
+  }
+}
+
+// Both forms compute the same sums in a different order; the choice depends
+// only on the row, so every caller gets the same bits for a given row.
+constexpr int kScoreRowShortMax = 256;
+
+template <int RB, class Emit>
+__device__ __forceinline__ void block_score_row(const float* L, int n_cand, int NB, int rows,
+                                                ScoreRowLds& sh, Emit&& emit) {
+  if (n_cand <= kScoreRowShortMax)
+    block_score_row_short<RB>(L, n_cand, NB, rows, sh, emit);
+  else
+    block_score_row_long<RB>(L, n_cand, NB, rows, sh, emit);
 }
 
 }  // namespace xattn
