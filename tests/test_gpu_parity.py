@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as wl
-from tests.gpu_util import check_index, f64, mask_mismatches, score_tol
+from tests.gpu_util import check_index, f64, mask_mismatches, near_tau_blocks, score_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -130,6 +130,47 @@ def test_score_matches_oracle(xa, case):
     viol = np.abs(g - ref) > score_tol(ref)
     assert not viol.any(), (np.argwhere(viol)[:5], np.abs(g - ref).max())
     np.testing.assert_allclose(g.sum(-1), 1.0, rtol=1e-4)
+
+
+ROW_FORM_CASES = [
+    # block, stride, C, causal, M: rows of up to 256 candidate blocks and longer
+    # rows are normalised by two different finalisation forms; these layers
+    # hold both, for r = block / stride of 2, 4, 16 and 32 strided rows
+    (64, 32, 64, True, 300 * 64),          # r = 2
+    (128, 32, 128, False, 300 * 128 - 37),  # r = 4, non-causal, ragged tail
+    (128, 8, 128, True, 300 * 128),        # r = 16
+    (128, 4, 64, True, 300 * 128),         # r = 32
+    (64, 4, 128, False, 257 * 64),         # r = 16, one candidate over the boundary
+]
+
+
+@pytest.mark.parametrize("case", ROW_FORM_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_short_and_long_score_rows(xa, case):
+    block, stride, C, causal, M = case
+    w = wl.WORKLOADS["llama8k"].scaled(Hq=2, Hkv=1, M=M, C=C, block=block, stride=stride, causal=causal)
+    x = wl.make_inputs(w, device=DEV)
+    sscale, smscale = wl.default_scales(w)
+    print(f"[row-forms] block={block} S={stride} C={C} causal={causal} M={M}", flush=True)
+    sep = xa.xattn_score(x["q"], x["k"], block, stride, sscale, causal)
+    bufs = xa.xattn_prefill(x["q"], x["k"], x["v"], x["tau"], block, stride, sscale, smscale, causal)
+    torch.cuda.synchronize()
+    nb = -(-M // block)
+    rows = [0, 200, 255, 256, nb - 1] if causal else [0, 255, nb - 1]
+    kh = f64(x["k"][0, 0])
+    tau = x["tau"].numpy().astype(np.float64)
+    for h in range(2):
+        qh = f64(x["q"][0, h])
+        for big_i in rows:
+            ref = oracle.block_score_row(qh, kh, big_i, block, stride, sscale, causal)
+            for label, got in (("score", f64(sep[0, h, big_i])), ("prefill", f64(bufs.block_scores[0, h, big_i]))):
+                bad = np.abs(got - ref) > score_tol(ref)
+                assert not bad.any(), (label, h, big_i, np.nonzero(bad)[0][:5], np.abs(got - ref).max())
+            got = f64(bufs.block_scores[0, h, big_i])
+            gmask = bufs.mask[0, h, big_i].cpu().numpy().astype(bool)
+            same = oracle.select_row(got, big_i, float(tau[h]), causal)
+            diff = np.nonzero(same != gmask)[0]
+            ok = near_tau_blocks(got, big_i, float(tau[h]), causal, 1e-5)
+            assert all(int(j) in ok for j in diff), (h, big_i, diff[:5])
 
 
 @pytest.mark.parametrize("tau", [0.0, 0.5, 0.9, 0.95, 1.0])
