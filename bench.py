@@ -380,7 +380,7 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS}
     else:
         ach = head["score_flops"] / (st[dom] * 1e-3) / 1e12
-        roof = {"kernel": "xattn_score (score_partials_bf16_kernel + finalize)", "bound": "mfma",
+        roof = {"kernel": "xattn_score (score_partials_dma_kernel + score_finalize_kernel)", "bound": "mfma",
                 "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS}
     roof["traffic"] = traffic_from_profile("bsa_fwd" if dom == "bsa_fwd" else "xattn_score", w.name)
 

@@ -169,23 +169,23 @@ __device__ __forceinline__ void score_epilogue(const ScoreArgs& a, const f32x16 
   // acc[x][y][r] is strided key j = j0 + WK wk + 32x + 8(r/4) + 4hh + r%4 and
   // strided query i = i0 + WQ wq + 32y + l32; each run of RB keys is reduced.
   float* wsh = a.ws + bh * (size_t)a.NBq * a.NBk * RB;
+  if constexpr (RB <= 4) {
+    // each run of RB keys lies inside one lane's group of 4 registers
 #pragma unroll
-  for (int y = 0; y < W::MTQ; ++y) {
-    const int i = i0 + W::WQ * wq + 32 * y + l32;
-    const int ia = i + a.qoff_s;  // absolute strided row
+    for (int y = 0; y < W::MTQ; ++y) {
+      const int i = i0 + W::WQ * wq + 32 * y + l32;
+      const int ia = i + a.qoff_s;  // absolute strided row
 #pragma unroll
-    for (int x = 0; x < W::MTK; ++x) {
-      const int jb = j0 + W::WK * wk + 32 * x;  // first strided key of this 32-key sub-tile
-      float v[16];
+      for (int x = 0; x < W::MTK; ++x) {
+        const int jb = j0 + W::WK * wk + 32 * x;  // first strided key of this 32-key sub-tile
+        float v[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = jb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        float xv = acc[x][y][r] * a.scale2;
-        if ((CAUSAL && j > ia) || j >= a.Rk) xv = -INFINITY;
-        v[r] = xv;
-      }
-      if constexpr (RB <= 4) {
-        // each run of RB keys lies inside one lane's group of 4 registers
+        for (int r = 0; r < 16; ++r) {
+          const int j = jb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          float xv = acc[x][y][r] * a.scale2;
+          if ((CAUSAL && j > ia) || j >= a.Rk) xv = -INFINITY;
+          v[r] = xv;
+        }
 #pragma unroll
         for (int r0 = 0; r0 < 16; r0 += RB) {
           float m = v[r0];
@@ -201,26 +201,60 @@ __device__ __forceinline__ void score_epilogue(const ScoreArgs& a, const f32x16 
           const int J = j / RB;
           if (i < a.Rq && j < a.Rk) wsh[((size_t)(i / RB) * a.NBk + J) * RB + i % RB] = Lv;
         }
-      } else {
-        // a run of RB >= 8 keys = registers [4q .. 4q + RB/2) in both wave halves
-        constexpr int NR = RB / 2;  // registers per half per run
+      }
+    }
+  } else {
+    // A run of RB >= 8 keys occupies registers [r0, r0 + RB/2) in both wave
+    // halves. Neighbouring runs A and B are exchanged between the halves with
+    // one v_permlane32_swap per register pair, after which each lane holds all
+    // RB logits of one run (the lower half run A, the upper half run B): max
+    // and sum need no cross-lane step, and every lane stores a result.
+    constexpr int NR = RB / 2;              // registers per half per run
+    constexpr int RUNS = 32 * W::MTK / RB;  // runs along this wave's keys (even)
+    // wave-uniform: only waves holding keys past a query's causal limit or past
+    // the last strided key mask anything
+    const int jw = j0 + W::WK * wk;         // first strided key of the wave
+    const bool need_mask = (CAUSAL && jw + W::WK - 1 > i0 + W::WQ * wq + a.qoff_s) || jw + W::WK > a.Rk;
 #pragma unroll
-        for (int r0 = 0; r0 < 16; r0 += NR) {
-          float m = v[r0];
+    for (int y = 0; y < W::MTQ; ++y) {
+      const int i = i0 + W::WQ * wq + 32 * y + l32;
+      const int ia = i + a.qoff_s;  // absolute strided row
 #pragma unroll
-          for (int u = 1; u < NR; ++u) m = fmaxf(m, v[r0 + u]);
-          m = halves_max(m);
-          float s = 0.f;
-          if (m != -INFINITY) {
+      for (int q = 0; q < RUNS; q += 2) {
+        const int xa = (q * RB) / 32, ra = ((q * RB) % 32) / 2;
+        const int xb = ((q + 1) * RB) / 32, rb = (((q + 1) * RB) % 32) / 2;
+        // lo[k], hi[k]: keys jr + 8(k/4) + k%4 and that + 4 of this lane's run
+        float lo[NR], hi[NR];
 #pragma unroll
-            for (int u = 0; u < NR; ++u) s += fast_exp2(v[r0 + u] - m);
-          }
-          s = halves_sum(s);
-          const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
-          const int j = jb + 8 * (r0 >> 2);
-          const int J = j / RB;
-          if (hh == 0 && i < a.Rq && j < a.Rk) wsh[((size_t)(i / RB) * a.NBk + J) * RB + i % RB] = Lv;
+        for (int k = 0; k < NR; ++k) {
+          const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[xa][y][ra + k]),
+                                                          __float_as_uint(acc[xb][y][rb + k]), false, false);
+          lo[k] = __uint_as_float(r[0]);
+          hi[k] = __uint_as_float(r[1]);
         }
+        const int jr = jw + (q + hh) * RB;  // first key of this lane's run
+        if (need_mask) {
+#pragma unroll
+          for (int k = 0; k < NR; ++k) {
+            const int jl = jr + 8 * (k >> 2) + (k & 3), jh = jl + 4;
+            if ((CAUSAL && jl > ia) || jl >= a.Rk) lo[k] = -INFINITY;
+            if ((CAUSAL && jh > ia) || jh >= a.Rk) hi[k] = -INFINITY;
+          }
+        }
+        float m = lo[0];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) m = fmaxf(fmaxf(m, lo[k]), hi[k]);
+        // scale2 > 0, so the max of the scaled logits is the scaled max; the
+        // scale is folded into one FMA per logit
+        const float ms = m * a.scale2;
+        const float mu = (ms == -INFINITY) ? 0.f : ms;
+        float sum = 0.f;
+#pragma unroll
+        for (int k = 0; k < NR; ++k)
+          sum += fast_exp2(fmaf(lo[k], a.scale2, -mu)) + fast_exp2(fmaf(hi[k], a.scale2, -mu));
+        // sum >= 1 (the max term), so the hardware log2 needs no denormal care
+        const float Lv = (ms == -INFINITY) ? -INFINITY : ms + __builtin_amdgcn_logf(sum);
+        if (i < a.Rq && jr < a.Rk) wsh[((size_t)(i / RB) * a.NBk + jr / RB) * RB + i % RB] = Lv;
       }
     }
   }
