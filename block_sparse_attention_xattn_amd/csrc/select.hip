@@ -65,21 +65,30 @@ __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
 #define XATTN_SELECT_SORT 0
 #endif
 
-struct SelectLds {
+// Per-row selection state for rows of up to CAP candidate blocks. Layers of
+// at most 256 key blocks use the small form: about 5 KiB instead of 24, so
+// registers (7 workgroups of 256 threads per CU) rather than LDS (6) cap the
+// rows in flight, and the latency-bound selection runs more of them at once.
+template <int CAP>
+struct SelectLdsT {
 #if XATTN_SELECT_SORT
-  uint64_t keys[SEL_MAX];
+  uint64_t keys[CAP];
 #else
-  float sc[SEL_MAX];              // candidate scores by J
+  float sc[CAP];                  // candidate scores by J
   unsigned long long hist[256];   // fixed-point mass per digit
   unsigned int hcnt[256];         // candidates per digit (last pass)
   unsigned long long wsum64[4];
   unsigned int cut[2];            // digits chosen so far; tie count
   unsigned long long cut_above;   // mass above the digits chosen so far
 #endif
-  uint8_t flags[SEL_MAX];
+  uint8_t flags[CAP];
   double wsum[4];
   int wcnt[4];
 };
+using SelectLds = SelectLdsT<SEL_MAX>;
+// the small form, where the sort option (which needs power-of-two padding up
+// to SEL_MAX keys) is off
+constexpr int SEL_SMALL = XATTN_SELECT_SORT ? SEL_MAX : 256;
 
 // Candidate p (score bits, index) as a descending-sortable key. Block scores
 // are non-negative, so their IEEE bits order like the values.
@@ -201,7 +210,8 @@ __device__ __forceinline__ unsigned long long block_scan_u64(unsigned long long 
 
 // With sc[0, n) filled, flags[0, NB) zeroed and a barrier passed: find the
 // cut, set the kept flags, add the diagonal, write the row.
-__device__ void select_radix(SelectLds& sh, int n, int NB, int I, float tau, size_t row, uint8_t* mask,
+template <class SL>
+__device__ void select_radix(SL& sh, int n, int NB, int I, float tau, size_t row, uint8_t* mask,
                              int32_t* kv_idx, int32_t* kv_cnt) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   uint8_t* flags = sh.flags;
@@ -266,10 +276,12 @@ __device__ void select_radix(SelectLds& sh, int n, int NB, int I, float tau, siz
       __syncthreads();
       int rank = incl_t - mine;
       for (int w = 0; w < wave; ++w) rank += sh.wcnt[w];
+      // only ever set flags (they start zeroed): the diagonal's flag, set by
+      // thread 0 without a barrier, must not be cleared by the thread that
+      // owns it as an unkept tie
       for (int p = p0; p < p1; ++p) {
         const unsigned int u = __float_as_uint(sh.sc[p]);
-        if (u > prefix) flags[p] = 1;
-        else if (u == prefix) flags[p] = (unsigned int)(rank++) < tstar;
+        if (u > prefix || (u == prefix && (unsigned int)(rank++) < tstar)) flags[p] = 1;
       }
     }
   }
@@ -279,8 +291,9 @@ __device__ void select_radix(SelectLds& sh, int n, int NB, int I, float tau, siz
 }
 #endif
 
+template <int CAP>
 __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
-  __shared__ SelectLds sh;
+  __shared__ SelectLdsT<CAP> sh;
   const int tid = threadIdx.x;
   const size_t row = blockIdx.x;  // (b*Hq + h)*NBq + I
   const int I = (int)(row % a.NBq);
@@ -318,9 +331,9 @@ struct FusedArgs {
   TauArray tau;
 };
 
-template <int RB>
+template <int RB, int CAP>
 __global__ __launch_bounds__(256) void score_select_kernel(FusedArgs a) {
-  __shared__ SelectLds sh;
+  __shared__ SelectLdsT<CAP> sh;
   __shared__ ScoreRowLds shs;
   const int tid = threadIdx.x;
   const size_t row = blockIdx.x;  // (b*Hq + h)*NBq + I
@@ -359,12 +372,21 @@ hipError_t launch_score_select(const Shape& s, const float* ws, float* block_sco
                                uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st) {
   FusedArgs a{ws, block_scores, mask, kv_idx, kv_cnt, s.Hq, s.NBq(), s.NBk(), s.qoff(), s.Rq(), s.causal, tau};
   const dim3 grid((unsigned)((size_t)s.B * s.Hq * s.NBq()));
+  const bool small = s.NBk() <= SEL_SMALL;
   switch (s.r()) {
-    case 2: hipLaunchKernelGGL(score_select_kernel<2>, grid, dim3(256), 0, st, a); break;
-    case 4: hipLaunchKernelGGL(score_select_kernel<4>, grid, dim3(256), 0, st, a); break;
-    case 8: hipLaunchKernelGGL(score_select_kernel<8>, grid, dim3(256), 0, st, a); break;
-    case 16: hipLaunchKernelGGL(score_select_kernel<16>, grid, dim3(256), 0, st, a); break;
-    case 32: hipLaunchKernelGGL(score_select_kernel<32>, grid, dim3(256), 0, st, a); break;
+#define XATTN_FUSED_CASE(R)                                                                   \
+  case R:                                                                                     \
+    if (small)                                                                                \
+      hipLaunchKernelGGL((score_select_kernel<R, SEL_SMALL>), grid, dim3(256), 0, st, a);     \
+    else                                                                                      \
+      hipLaunchKernelGGL((score_select_kernel<R, SEL_MAX>), grid, dim3(256), 0, st, a);       \
+    break;
+    XATTN_FUSED_CASE(2)
+    XATTN_FUSED_CASE(4)
+    XATTN_FUSED_CASE(8)
+    XATTN_FUSED_CASE(16)
+    XATTN_FUSED_CASE(32)
+#undef XATTN_FUSED_CASE
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -373,8 +395,11 @@ hipError_t launch_score_select(const Shape& s, const float* ws, float* block_sco
 hipError_t launch_select(const Shape& s, const float* block_scores, const TauArray& tau,
                          uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st) {
   SelectArgs a{block_scores, mask, kv_idx, kv_cnt, s.Hq, s.NBq(), s.NBk(), s.qoff(), s.causal, tau};
-  hipLaunchKernelGGL(select_kernel, dim3((unsigned)((size_t)s.B * s.Hq * s.NBq())), dim3(256), 0,
-                     st, a);
+  const dim3 grid((unsigned)((size_t)s.B * s.Hq * s.NBq()));
+  if (s.NBk() <= SEL_SMALL)
+    hipLaunchKernelGGL(select_kernel<SEL_SMALL>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(select_kernel<SEL_MAX>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

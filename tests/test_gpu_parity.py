@@ -239,6 +239,31 @@ def test_select_exact_cuts(xa, causal):
     check_index(m, idx.cpu().numpy(), cnt.cpu().numpy())
 
 
+@pytest.mark.parametrize("nb", [200, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_select_keeps_diagonal_that_is_an_unkept_tie(xa, nb, causal):
+    # Every candidate of a row tied: tau cuts through the ties, which are kept
+    # by ascending J, so the diagonal block (high J on the later rows) is an
+    # unkept tie and kept only by the diagonal rule. Its flag belongs to a
+    # thread of a later wave than the one that sets the diagonal. 200 blocks
+    # take the short-row selection, 300 the radix passes.
+    taus = [0.5, 0.25, 0.75]
+    rows = np.arange(nb)
+    raw = np.zeros((1, len(taus), nb, nb))
+    for i in rows:
+        n = i + 1 if causal else nb
+        raw[0, :, i, :n] = 1.0 / 256  # a binary fraction: sums are exact in float32 and float64
+    scores = torch.from_numpy(raw.astype(np.float32))
+    mask, idx, cnt = xa.xattn_select(scores.to(DEV), taus, 128, 8, causal, Hkv=1)
+    torch.cuda.synchronize()
+    ref = oracle.select(raw, taus, causal)
+    m = mask.cpu().numpy()
+    assert (m[0, :, rows, rows] == 1).all()
+    bad = np.argwhere(m.astype(bool) != ref.astype(bool))
+    assert bad.size == 0, bad[:8]
+    check_index(m, idx.cpu().numpy(), cnt.cpu().numpy())
+
+
 # ------------------------------------------------------------------ end to end
 
 E2E_CASES = [
