@@ -14,8 +14,9 @@
 //    for the whole row. Dense launches one workgroup per item; sparse runs
 //    persistent workgroups that pull items from per-XCD queues;
 //  * key blocks are consumed in 64-key sub-tiles: K and V rows are fetched from
-//    HBM into registers one sub-tile ahead and written to a double-buffered LDS
-//    tile, so one barrier per sub-tile orders reuse;
+//    HBM into registers one sub-tile ahead (two in the 8-wave modes) and
+//    written to a double-buffered LDS tile, so one barrier per sub-tile orders
+//    reuse;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 puts one query per lane, so the
 //    row max/sum is an in-lane reduction plus one exchange between the wave
 //    halves; P^T stays in registers and feeds O^T += V^T P^T directly, with V^T

@@ -14,7 +14,7 @@
 // last M of Mk tokens, strided query row i is absolute row i + (Mk - M) / S.
 //
 // Design: the strided logits are an R x R x (S*C) GEMM per head. The
-// (M/S)^2 logit matrix never reaches HBM. Each 128 x 128 output tile
+// (M/S)^2 logit matrix never reaches HBM. Each 256 x 256 output tile
 // reduces, in registers, every (strided row i, key block J) cell to a partial
 // log2-sum-exp L[J][i]; a second kernel turns each query-block row of partials
 // into normalised block scores. Partials are stored [I][J][t] (query block,
