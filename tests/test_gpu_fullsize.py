@@ -84,3 +84,39 @@ def test_fullsize_sampled_rows(xa, name):
         print(f"[fullsize] {name} h={h} I={big_i} kept={cnt} max_abs_err={err:.2e}", flush=True)
     del bufs, x
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_max_block_count_sampled_rows(xa, causal):
+    # The largest layer the interface takes: 4096 key blocks (64-token blocks
+    # over 262144 tokens). Row 4095 has 4096 candidates, which fills the
+    # selection's per-row state and the attention's cached block list exactly.
+    w = wl.WORKLOADS["llama256k"].scaled(Hq=2 if causal else 1, Hkv=1, block=64, stride=8, causal=causal)
+    assert w.nb == 4096
+    print(f"[maxblocks] causal={causal} M={w.M} block={w.block} S={w.stride}", flush=True)
+    x = wl.make_inputs(w, device=DEV)
+    sscale, smscale = wl.default_scales(w)
+    bufs = xa.xattn_prefill(x["q"], x["k"], x["v"], x["tau"], w.block, w.stride, sscale, smscale, w.causal)
+    torch.cuda.synchronize()
+    tau = x["tau"].numpy().astype(np.float64)
+    kh, vh = f64(x["k"][0, 0]), f64(x["v"][0, 0])
+    for h, big_i in ((0, 0), (w.Hq - 1, 2047), (0, 4094), (w.Hq - 1, 4095)):
+        qh = f64(x["q"][0, h])
+        ref = oracle.block_score_row(qh, kh, big_i, w.block, w.stride, sscale, w.causal)
+        got = f64(bufs.block_scores[0, h, big_i])
+        bad = np.abs(got - ref) > score_tol(ref)
+        assert not bad.any(), (h, big_i, np.nonzero(bad)[0][:5], np.abs(got - ref).max())
+        gmask = bufs.mask[0, h, big_i].cpu().numpy().astype(bool)
+        same = oracle.select_row(got, big_i, float(tau[h]), w.causal)
+        diff = np.nonzero(same != gmask)[0]
+        ok = near_tau_blocks(got, big_i, float(tau[h]), w.causal, 1e-5)
+        assert all(int(j) in ok for j in diff), (h, big_i, diff[:5])
+        cnt = int(bufs.kv_cnt[0, h, big_i])
+        np.testing.assert_array_equal(bufs.kv_idx[0, h, big_i, :cnt].cpu().numpy(), np.nonzero(gmask)[0])
+        o_ref, _ = oracle.attend_row(qh, kh, vh, gmask, big_i, w.block, smscale, w.causal)
+        o_got = f64(bufs.out[0, h, big_i * w.block:(big_i + 1) * w.block])
+        err = np.abs(o_got - o_ref).max()
+        assert err <= 2e-2, (h, big_i, err)
+        print(f"[maxblocks] h={h} I={big_i} kept={cnt} max_abs_err={err:.2e}", flush=True)
+    del bufs, x
+    torch.cuda.empty_cache()
