@@ -346,9 +346,9 @@ def main():
         return
 
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this path is measured on a single MI355X "
-              "(the layer shards by KV-head group with no communication; multi-GPU runs are "
-              "not part of this build).", file=sys.stderr)
+        print("bench.py measures one GPU only (--gpus 1): the library runs a layer on a single "
+              "MI355X; across GPUs a layer shards by KV-head group with no communication, which "
+              "this benchmark does not run.", file=sys.stderr)
         sys.exit(2)
 
     import torch
