@@ -31,7 +31,7 @@ Block size Bk, stride S, r = Bk // S strided rows per block,
 NBq = ceil(Mq / Bk) query blocks, NBk = ceil(Mk / Bk) key blocks; query block I
 is key block I + off // Bk. Lengths need not be multiples of S or Bk.
 
-Readings taken where the pages are silent (each one is listed in the design doc):
+Readings taken where the pages are silent:
   * score temperature: the caller passes ``score_scale`` explicitly;
   * the antidiagonal pairs query row i*S+s with key row j*S+S-1-s;
   * causal masking of the strided scores is at the strided level (j <= i);
