@@ -337,6 +337,39 @@ def test_repeat_runs_are_bitwise_identical(xa):
     assert torch.equal(a.out, b.out)
 
 
+def test_concurrent_streams_with_separate_buffers(xa):
+    # The library keeps no state: two different layers in flight at once on
+    # two streams, each with its own buffers and workspace, give bitwise what
+    # they give one after the other.
+    ws = [wl.WORKLOADS["llama32k"].scaled(M=4096, Hq=8, Hkv=2),
+          wl.WORKLOADS["llama128k"].scaled(M=6144, Hq=4, Hkv=1)]
+    xs = [wl.make_inputs(w, device=DEV) for w in ws]
+    args = []
+    for w, x in zip(ws, xs):
+        sscale, smscale = wl.default_scales(w)
+        args.append((x["q"], x["k"], x["v"], x["tau"], w.block, w.stride, sscale, smscale, w.causal))
+    refs = []
+    for a in args:
+        refs.append(xa.xattn_prefill(*a))
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    bufs = [None, None]
+    for _ in range(3):
+        torch.cuda.synchronize()
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                bufs[i] = xa.xattn_prefill(*args[i], buffers=bufs[i])
+        torch.cuda.synchronize()
+        for ref, got in zip(refs, bufs):
+            assert torch.equal(ref.block_scores, got.block_scores)
+            assert torch.equal(ref.mask, got.mask)
+            assert torch.equal(ref.kv_cnt, got.kv_cnt)
+            nb = ref.kv_idx.shape[-1]
+            valid = torch.arange(nb, device=DEV) < ref.kv_cnt[..., None]
+            assert torch.equal(ref.kv_idx[valid], got.kv_idx[valid])
+            assert torch.equal(ref.out, got.out)
+
+
 def test_outputs_stay_inside_buffers(xa):
     # guard regions around every output must be untouched
     B, Hq, Hkv, M, C, block = 1, 4, 1, 1024, 128, 128
