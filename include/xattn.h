@@ -43,7 +43,10 @@
  *    (each call clears what it needs on its stream); calls that may overlap
  *    in time (other streams) need distinct workspaces.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
- *    call only enqueues work on it and returns without synchronising.
+ *    call only enqueues work on it and returns without synchronising. The work
+ *    is kernels only (no memsets, copies or host waits), so a call can be
+ *    captured in a HIP graph and replayed; host arrays such as tau are read at
+ *    the call (at capture, for a graph).
  *  - Arguments are validated on the host before anything is enqueued. On any
  *    error the call returns a non-zero status and enqueues nothing; a failed
  *    kernel launch returns XATTN_ERR_HIP. xattn_last_error() gives a message

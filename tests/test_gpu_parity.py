@@ -370,6 +370,42 @@ def test_concurrent_streams_with_separate_buffers(xa):
             assert torch.equal(ref.out, got.out)
 
 
+@pytest.mark.parametrize("name,over", [("llama32k", dict(M=4096, Hq=8, Hkv=2)),
+                                       ("llama128k", dict(M=131072, Hq=2, Hkv=1))],
+                         ids=["llama32k-4096", "llama128k-2heads"])
+def test_prefill_replays_from_a_hip_graph(xa, name, over):
+    # xattn_prefill enqueues kernels only (the work queues are cleared by a
+    # kernel, not a memset), so it can be captured in a graph. Every replay,
+    # with eager work and synchronisations in between, equals the eager call.
+    w = wl.WORKLOADS[name].scaled(**over)
+    x = wl.make_inputs(w, device=DEV)
+    sscale, smscale = wl.default_scales(w)
+    args = (x["q"], x["k"], x["v"], x["tau"], w.block, w.stride, sscale, smscale, w.causal)
+    ref = xa.xattn_prefill(*args)
+    bufs = xa.PrefillBuffers(x["q"], x["k"], w.block, w.stride, w.causal)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        xa.xattn_prefill(*args, buffers=bufs)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        xa.xattn_prefill(*args, buffers=bufs)
+    torch.cuda.synchronize()
+    valid = torch.arange(ref.kv_idx.shape[-1], device=DEV) < ref.kv_cnt[..., None]
+    for _ in range(3):
+        for t, fill in ((bufs.out, 0.0), (bufs.block_scores, -1.0), (bufs.mask, 7), (bufs.kv_cnt, -3)):
+            t.fill_(fill)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ref.block_scores, bufs.block_scores)
+        assert torch.equal(ref.mask, bufs.mask)
+        assert torch.equal(ref.kv_cnt, bufs.kv_cnt)
+        assert torch.equal(ref.kv_idx[valid], bufs.kv_idx[valid])
+        assert torch.equal(ref.out, bufs.out)
+
+
 def test_outputs_stay_inside_buffers(xa):
     # guard regions around every output must be untouched
     B, Hq, Hkv, M, C, block = 1, 4, 1, 1024, 128, 128
