@@ -66,7 +66,7 @@ __device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
 #endif
 
 // Per-row selection state for rows of up to CAP candidate blocks. Layers of
-// at most 256 key blocks use the small form: about 5 KiB instead of 24, so
+// at most 2048 key blocks use the small form: about 13 KiB instead of 24, so
 // registers (7 workgroups of 256 threads per CU) rather than LDS (6) cap the
 // rows in flight, and the latency-bound selection runs more of them at once.
 template <int CAP>
@@ -88,7 +88,7 @@ struct SelectLdsT {
 using SelectLds = SelectLdsT<SEL_MAX>;
 // the small form, where the sort option (which needs power-of-two padding up
 // to SEL_MAX keys) is off
-constexpr int SEL_SMALL = XATTN_SELECT_SORT ? SEL_MAX : 256;
+constexpr int SEL_SMALL = XATTN_SELECT_SORT ? SEL_MAX : 2048;
 
 // Candidate p (score bits, index) as a descending-sortable key. Block scores
 // are non-negative, so their IEEE bits order like the values.
