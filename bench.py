@@ -10,7 +10,9 @@ already resident in HBM. A second timed loop through the stage entry points
 (xattn_score, xattn_select, bsa_fwd) gives the per-stage breakdown. Reported value: dense-equivalent TFLOP/s
 (2*Hq*M^2*C / step time). Also reported: per-stage times, measured density, our
 own dense_fwd time and the speedup over it, the roofline of the dominant kernel,
-and the CPU oracle timed on a bounded sample of the same workload.
+the CPU oracle timed on a bounded sample of the same workload, the 32K and 128K
+lengths, method variants on the headline layer, and the non-causal video-model
+layer (24/24 heads, 76,800 tokens, stride 8, tau 0.95) under other_configs.
 
 Prints ONE JSON line on stdout (progress goes to stderr).
 """
@@ -316,6 +318,75 @@ def run_variants(xa, torch, head, steps):
     return res
 
 
+def library_context(xa, wl, torch):
+    """Library routines on the path's shapes, for context only (never part of a
+    step): a plain hipBLASLt GEMM (torch.mm, bf16) of one head's strided
+    operands at 256K, the whole square where the scoring kernel computes the
+    causal triangle with its epilogue, and torch's flash SDPA backend on the
+    dense causal 32K and 128K layers next to dense_fwd."""
+    dev = "cuda:0"
+    out = {}
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    w = wl.WORKLOADS["llama256k"]
+    R, D = w.M // w.stride, w.stride * w.C
+    g = torch.Generator(device=dev).manual_seed(0)
+    kp = torch.randn((R, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    qt = torch.randn((D, R), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    c = torch.empty((R, R), device=dev, dtype=torch.bfloat16)
+    ms = timed(lambda: torch.mm(kp, qt, out=c), 10)
+    flops = 2.0 * R * R * D
+    out["gemm_strided_256k_one_head"] = {"routine": "torch.mm (hipBLASLt), bf16 in/out", "shape": [R, D, R],
+                                         "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1)}
+    log(f"[library] torch.mm {R}x{D}x{R}: {ms:.3f} ms, {flops / ms / 1e9:.0f} TFLOP/s")
+    del kp, qt, c
+    torch.cuda.empty_cache()
+
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import torch.nn.functional as F
+    for name in ("llama32k", "llama128k"):
+        w = wl.WORKLOADS[name]
+        x = wl.make_inputs(w, device=dev)
+        q, k, v = x["q"], x["k"], x["v"]
+        _, smscale = wl.default_scales(w)
+        g = w.Hq // w.Hkv
+        ke = k.repeat_interleave(g, dim=1).contiguous()
+        ve = v.repeat_interleave(g, dim=1).contiguous()
+        ours = torch.empty_like(q)
+        n = 3 if w.M <= 32768 else 1
+        ms_ours = timed(lambda: xa.dense_fwd(q, k, v, w.block, smscale, True, out=ours), n)
+        rec = {"dense_fwd_ms": round(ms_ours, 3), "dense_fwd_tflops": round(w.dense_flops / ms_ours / 1e9, 1)}
+        try:
+            with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+                ref = [None]
+
+                def sdpa():
+                    ref[0] = F.scaled_dot_product_attention(q, ke, ve, is_causal=True, scale=smscale)
+                ms = timed(sdpa, n)
+            diff = (ref[0].float() - ours.float()).abs().max().item()
+            rec.update({"routine": "torch SDPA, flash backend, K/V repeated to 32 heads",
+                        "sdpa_ms": round(ms, 3), "sdpa_tflops": round(w.dense_flops / ms / 1e9, 1),
+                        "max_abs_diff_vs_dense_fwd": diff})
+            log(f"[library] {name} SDPA flash {ms:.3f} ms, dense_fwd {ms_ours:.3f} ms, max|diff| {diff:.3g}")
+        except RuntimeError as e:
+            rec["sdpa_error"] = str(e).splitlines()[0][:200]
+            log(f"[library] {name} SDPA flash unavailable: {rec['sdpa_error']}")
+        out[name] = rec
+        del x, q, k, v, ke, ve, ours
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -324,6 +395,8 @@ def main():
     ap.add_argument("--workload", default="llama256k")
     ap.add_argument("--also", default="llama32k,llama128k",
                     help="other lengths reported under by_length (comma list, '' for none)")
+    ap.add_argument("--extra", default="video",
+                    help="other configurations reported under other_configs (comma list, '' for none)")
     ap.add_argument("--dense-steps", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -332,6 +405,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain elementwise kernel of known size (1 GiB read, 1 GiB "
                          "written), the reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--library-context", action="store_true",
+                    help="only time library routines on the path's shapes (hipBLASLt GEMM, torch's flash "
+                         "SDPA) next to dense_fwd, as context; prints one JSON line")
     a = ap.parse_args()
 
     if a.copy_calibration:
@@ -358,6 +434,16 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+
+    if a.library_context:
+        print(json.dumps({"library_context": library_context(xa, wl, torch)}))
+        return
+
+    others = {}
+    for n in [n for n in a.extra.split(",") if n and n != a.workload]:
+        others[n] = run_workload(xa, wl, torch, n, max(3, a.steps // 2), a.warmup, a.dense_steps)
+        others[n].pop("_tensors", None)
+        torch.cuda.empty_cache()
 
     names = [a.workload] + [n for n in a.also.split(",") if n and n != a.workload]
     results = {}
@@ -426,6 +512,10 @@ def main():
         "cpu_baseline": cpu,
         "by_length": {n: summary(r) for n, r in results.items()},
         "variants": variants,
+        "other_configs": {n: {"config": {"Hq": r["workload"].Hq, "Hkv": r["workload"].Hkv, "M": r["workload"].M,
+                                          "stride": r["workload"].stride, "tau": r["workload"].tau,
+                                          "causal": r["workload"].causal}, **summary(r)}
+                          for n, r in others.items()},
         "kernel_source_sha": kernel_source_sha(),
     }
     print(json.dumps(line))

@@ -33,6 +33,19 @@
 #ifndef XATTN_SPARSE_PAIR_ROWS_MIN_NB
 #define XATTN_SPARSE_PAIR_ROWS_MIN_NB 1024
 #endif
+// The same threshold for non-causal heads: every row draws on the whole key
+// range, so neighbouring rows' lists overlap more (7% off bsa_fwd on a
+// non-causal layer of 600 query blocks at 48% density; pairing the 256 rows of
+// a causal layer at 1.6% density was 20% slower).
+#ifndef XATTN_SPARSE_PAIR_ROWS_MIN_NB_NC
+#define XATTN_SPARSE_PAIR_ROWS_MIN_NB_NC 512
+#endif
+// 1: dense workgroups of an odd GQA group (no sibling pair) take two
+// neighbouring rows of one head, which read the same key blocks (all of them,
+// or all but the later row's diagonal); 0: one row per workgroup
+#ifndef XATTN_DENSE_PAIR_ROWS
+#define XATTN_DENSE_PAIR_ROWS 1
+#endif
 // 1: the sparse workgroups of one KV group share an XCD; 0: spread them
 #ifndef XATTN_SPARSE_GROUP_ON_XCD
 #define XATTN_SPARSE_GROUP_ON_XCD 1
@@ -42,6 +55,10 @@
 // infinity cache keeps it; 0: row by row across all heads
 #ifndef XATTN_SPARSE_GROUP_MAJOR
 #define XATTN_SPARSE_GROUP_MAJOR 1
+#endif
+// the same order for dense launches (1), or row by row across all heads (0)
+#ifndef XATTN_DENSE_GROUP_MAJOR
+#define XATTN_DENSE_GROUP_MAJOR 1
 #endif
 // consecutive items (rows, with GROUP_MAJOR) handed to one XCD together
 #ifndef XATTN_SPARSE_ROWS_PER_CHUNK
@@ -108,7 +125,9 @@ struct AttnLds {
 //   ROWS      one head, two neighbouring query blocks 2p and 2p+1; 8 waves over
 //             the union of the two block lists. Neighbouring rows of a head keep
 //             similar numbers of largely the same blocks, so the shared loads
-//             are rarely wasted and neither half idles for long (sparse).
+//             are rarely wasted and neither half idles for long (sparse; and
+//             dense when the GQA group is odd, where both rows read the same
+//             blocks, the earlier row skipping the later one's diagonal).
 // The 8-wave modes hold two sub-tiles in flight (registers), SINGLE one.
 enum { MODE_SINGLE = 0, MODE_SIBLINGS = 1, MODE_ROWS = 2 };
 
@@ -171,6 +190,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   const int slice = wave % WPH;                // RPW-row slice of the query block
 
   // ---- decode the item: heavy query rows (large P) come first in item order
+  // (within each KV group when the order is KV-group-major)
   const int G = a.Hq / a.Hkv;
   const AttnItems its(a, MODE);
   const int NP = (int)its.NP;
@@ -178,7 +198,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   const int pw = item % GW;
   uint32_t rest = item / GW;
   int g, b, P;
-  if (SPARSE && XATTN_SPARSE_GROUP_MAJOR) {
+  constexpr bool group_major = SPARSE ? XATTN_SPARSE_GROUP_MAJOR != 0 : XATTN_DENSE_GROUP_MAJOR != 0;
+  if (group_major) {
     // KV-group-major: every row of one KV group before the next group
     P = NP - 1 - (int)(rest % NP);
     rest /= NP;
@@ -720,13 +741,13 @@ static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t
 }
 
 // 128-row blocks: dense attention pairs GQA siblings (identical block lists)
-// when the group size is even, and so does sparse attention over GQA-union
-// lists. Other sparse lists pair neighbouring rows of one head on long
-// sequences (their lists share most blocks, so the union costs little and each
-// K/V tile is fetched once for both rows) and run one (head, row) per
-// workgroup otherwise; sibling heads keep very different numbers of blocks, so
-// a sibling pair would leave one half idle. 64-row blocks use one (head, row)
-// per workgroup.
+// when the group size is even and neighbouring rows of a head when it is odd;
+// sparse attention over GQA-union lists pairs siblings too. Other sparse lists
+// pair neighbouring rows of one head on long sequences (their lists share most
+// blocks, so the union costs little and each K/V tile is fetched once for both
+// rows) and run one (head, row) per workgroup otherwise; sibling heads keep
+// very different numbers of blocks, so a sibling pair would leave one half
+// idle. 64-row blocks use one (head, row) per workgroup.
 template <int C, int BLK>
 static hipError_t launch_bf16_cb(const Shape& s, const AttnArgs& a, hipStream_t st) {
   if (BLK == 128) {
@@ -735,8 +756,10 @@ static hipError_t launch_bf16_cb(const Shape& s, const AttnArgs& a, hipStream_t 
     // GQA-union lists are shared by the siblings: one tile load serves both
     if (a.kv_idx != nullptr && pairs && s.selection == SEL_GQA_UNION)
       return launch_bf16_cbm<C, BLK, MODE_SIBLINGS>(s, a, st);
-    if (a.kv_idx != nullptr && s.NBq() >= XATTN_SPARSE_PAIR_ROWS_MIN_NB)
+    if (a.kv_idx != nullptr &&
+        s.NBq() >= (s.causal ? XATTN_SPARSE_PAIR_ROWS_MIN_NB : XATTN_SPARSE_PAIR_ROWS_MIN_NB_NC))
       return launch_bf16_cbm<C, BLK, MODE_ROWS>(s, a, st);
+    if (a.kv_idx == nullptr && XATTN_DENSE_PAIR_ROWS) return launch_bf16_cbm<C, BLK, MODE_ROWS>(s, a, st);
   }
   return launch_bf16_cbm<C, BLK, MODE_SINGLE>(s, a, st);
 }

@@ -60,6 +60,8 @@ ATTN_CASES = [
     (1, 2, 2, 256, 64, 128, False, torch.bfloat16),
     (1, 8, 2, 128, 128, 128, True, torch.bfloat16),   # a single block
     (1, 2, 1, 256, 128, 64, True, torch.bfloat16),
+    (1, 3, 1, 640, 128, 128, True, torch.bfloat16),   # odd group, odd block count
+    (1, 2, 2, 896, 64, 128, True, torch.bfloat16),    # one query head per KV head
     (1, 1, 1, 512, 64, 64, True, torch.float32),
     (1, 2, 1, 256, 128, 128, False, torch.float32),
 ]

@@ -25,6 +25,7 @@ CASES = [
     (1, 4, 2, 512, 2048, 128, 128, 8, True, torch.bfloat16),      # chunk, aligned
     (1, 2, 1, 700, 1468, 128, 128, 16, True, torch.bfloat16),     # chunk, ragged both
     (1, 2, 1, 6952, 9000, 128, 128, 8, True, torch.bfloat16),     # trapezoid of score tiles
+    (1, 3, 1, 1000, 1768, 128, 128, 8, True, torch.bfloat16),     # odd group, chunk, ragged
     (1, 1, 1, 300, 556, 64, 64, 8, True, torch.float32),
     (1, 1, 1, 77, 77, 64, 64, 8, False, torch.float32),
 ]
@@ -129,7 +130,7 @@ def test_attention_ragged_chunked(xa, case):
 
 
 @pytest.mark.parametrize("selection", ["row", "global", "gqa_union"])
-@pytest.mark.parametrize("case", [CASES[1], CASES[4], CASES[6]], ids=_ids)
+@pytest.mark.parametrize("case", [CASES[1], CASES[4], CASES[7]], ids=_ids)
 def test_prefill_ragged_chunked_end_to_end(xa, case, selection):
     B, Hq, Hkv, Mq, Mk, C, block, stride, causal, dtype = case
     q, k, v = _inputs(case, 4)
@@ -187,7 +188,7 @@ def global_cut_ok_chunk(keep, scores, tau, causal, rel=1e-8):
     return False
 
 
-@pytest.mark.parametrize("case", [CASES[0], CASES[4], CASES[6]], ids=_ids)
+@pytest.mark.parametrize("case", [CASES[0], CASES[4], CASES[7]], ids=_ids)
 def test_ragged_outputs_stay_inside_buffers(xa, case):
     # every output and the workspace sit between guard regions that must stay
     # untouched (a store past the last query row would land in the tail guard)
