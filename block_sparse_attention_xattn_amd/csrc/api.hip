@@ -101,19 +101,12 @@ xattn_status do_partials(const xattn_problem* p, const void* q, const void* k, f
   return hip_status(e, "score partials launch");
 }
 
+// Partials, then the normalised block scores (the separate scoring stage).
 xattn_status do_score(const xattn_problem* p, const void* q, const void* k, float score_scale,
-                      float* block_scores, void* ws, size_t ws_bytes, hipStream_t st) {
-  const xattn::Shape s = shape_of(p);
-  hipError_t e;
-  if (p->dtype == XATTN_BF16)
-    e = xattn::launch_score_partials_bf16(s, static_cast<const uint16_t*>(q),
-                                          static_cast<const uint16_t*>(k), score_scale,
-                                          static_cast<float*>(ws), st);
-  else
-    e = xattn::launch_score_partials_f32(s, static_cast<const float*>(q), static_cast<const float*>(k),
-                                         score_scale, static_cast<float*>(ws), st);
-  if (e != hipSuccess) return hip_status(e, "score partials launch");
-  return hip_status(xattn::launch_score_finalize(s, static_cast<const float*>(ws), block_scores, st),
+                      float* block_scores, void* ws, hipStream_t st) {
+  const xattn_status r = do_partials(p, q, k, score_scale, ws, st);
+  if (r != XATTN_OK) return r;
+  return hip_status(xattn::launch_score_finalize(shape_of(p), static_cast<const float*>(ws), block_scores, st),
                     "score finalize launch");
 }
 
@@ -213,7 +206,7 @@ xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k, f
   if (!q || !k || !block_scores) return fail(XATTN_ERR_NULL, "q, k and block_scores must be non-NULL");
   if ((s = check_scale(score_scale, "score_scale")) != XATTN_OK) return s;
   if ((s = check_workspace(ws, ws_bytes, xattn_score_workspace_bytes(p))) != XATTN_OK) return s;
-  return do_score(p, q, k, score_scale, block_scores, ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return do_score(p, q, k, score_scale, block_scores, ws, static_cast<hipStream_t>(stream));
 }
 
 size_t xattn_select_workspace_bytes(const xattn_problem* p) {
