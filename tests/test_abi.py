@@ -56,6 +56,9 @@ FAKE = 0x1000  # never dereferenced: validation fails first
     (dict(dtype=7), 3), (dict(causal=2), 4), (dict(Hq=512, Hkv=1), 5), (dict(B=0), 2),
     (dict(M=4096 * 128 * 2), 5), (dict(pattern=2), 4), (dict(pattern=-1), 4),
     (dict(selection=3), 4), (dict(selection=-1), 4), (dict(Mk=4096 * 128 + 128), 5),
+    # empty problems are errors, not silent no-ops
+    (dict(M=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(C=0), 2), (dict(block=0), 2),
+    (dict(stride=0), 2), (dict(M=-5), 2),
 ])
 def test_score_rejects_bad_problems(xa, kw, status):
     p = _p(xa, **kw)
