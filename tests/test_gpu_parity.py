@@ -275,10 +275,17 @@ E2E_CASES = [
     ("llama32k", dict(M=2048, Hq=8, Hkv=2)),
     ("llama128k", dict(M=4096, Hq=4, Hkv=1)),
     ("video", dict(M=2560, Hq=2, Hkv=2)),
+    # other seeds of the same generators (other sink, band and column draws)
+    ("llama8k", dict(M=2048, Hq=8, Hkv=2, seed=101)),
+    ("llama8k", dict(M=2048, Hq=8, Hkv=2, seed=102)),
+    ("llama32k", dict(M=3072, Hq=4, Hkv=1, seed=103)),
+    ("llama128k", dict(M=4096, Hq=4, Hkv=2, seed=104)),
+    ("video", dict(M=2560, Hq=2, Hkv=2, seed=105)),
 ]
 
 
-@pytest.mark.parametrize("name,over", E2E_CASES, ids=[c[0] for c in E2E_CASES])
+@pytest.mark.parametrize("name,over", E2E_CASES,
+                         ids=[c[0] + (f"-seed{c[1]['seed']}" if "seed" in c[1] else "") for c in E2E_CASES])
 def test_prefill_end_to_end(xa, name, over):
     w = wl.WORKLOADS[name].scaled(**over)
     x = wl.make_inputs(w)
