@@ -24,6 +24,7 @@ import json
 import math
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -137,10 +138,12 @@ def run_workload(xa, wl, torch, name, steps, warmup, dense_steps):
     for i in range(steps):
         stages(evs[i])
     torch.cuda.synchronize()
+    # per-stage medians over the steps (the whole-step value above is the mean
+    # over exactly `steps` timed steps)
     st = {
-        "xattn_score": sum(e[0].elapsed_time(e[1]) for e in evs) / steps,
-        "xattn_select": sum(e[1].elapsed_time(e[2]) for e in evs) / steps,
-        "bsa_fwd": sum(e[2].elapsed_time(e[3]) for e in evs) / steps,
+        "xattn_score": statistics.median(e[0].elapsed_time(e[1]) for e in evs),
+        "xattn_select": statistics.median(e[1].elapsed_time(e[2]) for e in evs),
+        "bsa_fwd": statistics.median(e[2].elapsed_time(e[3]) for e in evs),
     }
     assert torch.equal(bufs.kv_cnt, kv_cnt), "fused and stage-wise selections differ"
     cand = B * Hq * (nb * (nb + 1) // 2 if w.causal else nb * nb)
