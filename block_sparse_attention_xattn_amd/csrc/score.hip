@@ -472,7 +472,7 @@ __global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_ker
     for (int y = 0; y < W::MTQ; ++y) acc[x][y] = f32x16{};
 
   // chunk c sits in stage cur; the stage nxt (chunk c - 1, done) is refilled
-  // with chunk c + 3 (past the end: the last chunk again, never read)
+  // with chunk c + 3
   auto mma = [&](const uint16_t* cur) {
 #pragma unroll
     for (int ks = 0; ks < SD_KC / 16; ++ks) {
@@ -495,21 +495,29 @@ __global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_ker
   // the shorter lookahead costs more than the barriers saved)
   auto step = [&](int c, const uint16_t* cur, uint16_t* nxt) {
     vm_wait_barrier<2 * 2 * SD_BPW>();  // chunks c+1, c+2 may be in flight
-    issue(min(c + 3, n_chunks - 1), nxt);
+    issue(c + 3, nxt);
     __builtin_amdgcn_sched_barrier(0);  // keep the refill ahead of this chunk's work
     mma(cur);
   };
   issue(0, st0);
-  issue(min(1, n_chunks - 1), st1);
-  issue(min(2, n_chunks - 1), st2);
-  // n_chunks is a multiple of 4 (checked by the launcher)
-  for (int c = 0; c < n_chunks; c += 4) {
+  issue(1, st1);
+  issue(2, st2);
+  // n_chunks is a multiple of 4, at least 4 (checked by the launcher); the
+  // last group refills only its first step's stage, and its waits count down
+  // as fewer chunks remain in flight
+  for (int c = 0; c < n_chunks - 4; c += 4) {
     step(c, st0, st3);
     step(c + 1, st1, st0);
     step(c + 2, st2, st1);
     step(c + 3, st3, st2);
   }
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the trailing refills have landed
+  step(n_chunks - 4, st0, st3);
+  vm_wait_barrier<2 * 2 * SD_BPW>();  // chunks n-2, n-1 may be in flight
+  mma(st1);
+  vm_wait_barrier<1 * 2 * SD_BPW>();  // chunk n-1 may be in flight
+  mma(st2);
+  vm_wait_barrier<0>();
+  mma(st3);
   score_epilogue<RB, CAUSAL, W>(a, acc, tl.bh, tl.i0, tl.j0, wk, wq, l32, hh);
 }
 
