@@ -22,7 +22,7 @@
 // is contiguous and the second pass reads it with unit stride.
 //
 // GEMM (bf16, gfx950 MFMA 32x32x16): S^T = K~' Q'^T on 256 x 256 output tiles,
-// 8 waves in a 4 x 2 grid of 64 x 128 sub-tiles. The tile size is set by L2
+// 8 waves in a 2 x 4 grid of 128 x 64 sub-tiles. The tile size is set by L2
 // bandwidth: a 256 x 256 tile moves half the L2 bytes per FLOP of a 128 x 128
 // one (128 vs 64 FLOP per byte), and its fp32 accumulators already take half the
 // register file. The S*C contraction is streamed in chunks: with complete
@@ -57,18 +57,19 @@ struct ScoreArgs {
 #define XATTN_SCORE_TILE 256
 #endif
 constexpr int SC_TILE = XATTN_SCORE_TILE;   // strided keys x strided queries per tile
-// Output sub-tile of one wave, strided keys x strided queries (WK x WQ): 64 x 128
-// (2 x 4 MFMA tiles, two waves per SIMD), 64 x 64 (2 x 2, four waves per SIMD;
-// 4/3 of the LDS fragment reads per MFMA) or 128 x 128 (4 x 4, one wave per SIMD
-// with its accumulators in AGPRs). Measured on the 256K layer: the DMA kernel is
-// fastest with 64 x 128 (64 x 64 about 2% and 128 x 128 about 6% slower); the
+// Output sub-tile of one wave, strided keys x strided queries (WK x WQ): 128 x 64
+// or 64 x 128 (4 x 2 or 2 x 4 MFMA tiles, two waves per SIMD), 64 x 64 (2 x 2,
+// four waves per SIMD; 4/3 of the LDS fragment reads per MFMA) or 128 x 128
+// (4 x 4, one wave per SIMD with its accumulators in AGPRs). Measured: the DMA
+// kernel is fastest with 128 x 64, 1.2% ahead of 64 x 128 at 32K, 128K and 256K
+// (64 x 64 about 2% and 128 x 128 about 6% behind 64 x 128 at 256K); the
 // register-staged kernel with 64 x 64 (64 x 128 about 3% slower: its staging
 // registers leave two waves per SIMD too little room).
 #ifndef XATTN_SCORE_DMA_WK
-#define XATTN_SCORE_DMA_WK 64
+#define XATTN_SCORE_DMA_WK 128
 #endif
 #ifndef XATTN_SCORE_DMA_WQ
-#define XATTN_SCORE_DMA_WQ 128
+#define XATTN_SCORE_DMA_WQ 64
 #endif
 #ifndef XATTN_SCORE_REG_WK
 #define XATTN_SCORE_REG_WK 64
