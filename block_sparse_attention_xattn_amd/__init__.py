@@ -29,11 +29,11 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 XATTN_BF16 = 0
 XATTN_F32 = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAX_HEADS = 256
 
 EXPORTS = (
-    "xattn_abi_version", "xattn_status_string", "xattn_last_error",
+    "xattn_abi_version", "xattn_status_string", "xattn_last_error", "xattn_workspace_bytes",
     "xattn_score_workspace_bytes", "xattn_select_workspace_bytes", "xattn_attn_workspace_bytes",
     "xattn_prefill_workspace_bytes", "xattn_score", "xattn_select", "bsa_fwd",
     "dense_fwd", "xattn_prefill",
@@ -62,6 +62,8 @@ _lib.xattn_abi_version.restype = ctypes.c_int32
 _lib.xattn_status_string.restype = ctypes.c_char_p
 _lib.xattn_status_string.argtypes = [ctypes.c_int]
 _lib.xattn_last_error.restype = ctypes.c_char_p
+_lib.xattn_workspace_bytes.restype = ctypes.c_size_t
+_lib.xattn_workspace_bytes.argtypes = [_P]
 _lib.xattn_score_workspace_bytes.restype = ctypes.c_size_t
 _lib.xattn_score_workspace_bytes.argtypes = [_P]
 _lib.xattn_select_workspace_bytes.restype = ctypes.c_size_t
@@ -114,13 +116,27 @@ def problem(B, Hq, Hkv, M, C, block, stride, causal, dtype, pattern=ANTIDIAGONAL
                    _selection(selection), Mk)
 
 
-def _problem_of(q, k, block, stride, causal, pattern=ANTIDIAGONAL, selection=SELECT_ROW) -> Problem:
-    """Sizes from q (B, Hq, M, C) and k (B, Hkv, Mk, C)."""
+def _problem_of(q, k, block, stride, causal, pattern=ANTIDIAGONAL, selection=SELECT_ROW, v=None) -> Problem:
+    """Sizes from q (B, Hq, M, C), k (B, Hkv, Mk, C) and, if given, v (k's shape)."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be 4-D (B, H, M, C)")
     B, Hq, M, C = q.shape
+    if k.shape[0] != B or k.shape[3] != C:
+        raise ValueError(f"k {tuple(k.shape)} does not match q {tuple(q.shape)} in batch or head dim")
+    if v is not None and v.shape != k.shape:
+        raise ValueError(f"v {tuple(v.shape)} must have k's shape {tuple(k.shape)}")
     return problem(B, Hq, k.shape[1], M, C, block, stride, causal, q.dtype, pattern, selection,
                    Mk=k.shape[2])
+
+
+def _expect(t, name, shape, dtype, device):
+    """Raise unless tensor t (if given) has this shape, dtype and device."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
 def _cdiv(a, b):
@@ -130,6 +146,8 @@ def _cdiv(a, b):
 def _ptr(t):
     if t is None:
         return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on a GPU device")
     if not t.is_contiguous():
         raise ValueError("tensors must be contiguous")
     return t.data_ptr()
@@ -140,9 +158,21 @@ def _stream(dev):
 
 
 def _same(q, *ts):
+    # (that they sit on a GPU is checked when their pointers are taken, after
+    # every shape check and before any launch)
     for t in ts:
         if t.dtype != q.dtype or t.device != q.device:
             raise ValueError("q, k, v must share dtype and device")
+
+
+def _blocks(q, k, block):
+    """(B, Hq, NBq, NBk) of the block tensors for q and k."""
+    return (q.shape[0], q.shape[1], _cdiv(q.shape[2], block), _cdiv(k.shape[2], block))
+
+
+def total_workspace_bytes(p: Problem) -> int:
+    """Workspace bytes that serve every entry point (xattn_workspace_bytes)."""
+    return int(_lib.xattn_workspace_bytes(ctypes.byref(p)))
 
 
 def workspace_bytes(p: Problem) -> int:
@@ -170,9 +200,10 @@ def xattn_score(q, k, block, stride, score_scale, causal=True, block_scores=None
     """Block scores (B, Hq, NBq, NBk) float32."""
     _same(q, k)
     p = _problem_of(q, k, block, stride, causal, pattern)
-    nbq, nbk = _cdiv(q.shape[2], block), _cdiv(k.shape[2], block)
+    shp = _blocks(q, k, block)
+    _expect(block_scores, "block_scores", shp, torch.float32, q.device)
     if block_scores is None:
-        block_scores = torch.empty((q.shape[0], q.shape[1], nbq, nbk), dtype=torch.float32, device=q.device)
+        block_scores = torch.empty(shp, dtype=torch.float32, device=q.device)
     need = workspace_bytes(p)
     if ws is None:
         ws = torch.empty(max(need, 4), dtype=torch.uint8, device=q.device)
@@ -194,10 +225,15 @@ def xattn_select(block_scores, tau, block, stride, causal=True, Hkv=None, C=128,
                  want_mask=True, mask=None, kv_idx=None, kv_cnt=None, selection=SELECT_ROW):
     """(mask u8 or None, kv_idx int32, kv_cnt int32) for block scores (B, Hq, NBq, NBk);
     NBk > NBq means the queries are the last NBq blocks of the NBk-block sequence."""
+    if block_scores.dim() != 4 or block_scores.dtype != torch.float32:
+        raise ValueError("block_scores must be float32 (B, Hq, NBq, NBk)")
     B, Hq, nbq, nbk = block_scores.shape
     p = problem(B, Hq, Hkv or Hq, nbq * block, C, block, stride, causal, dtype, selection=selection,
                 Mk=nbk * block)
     dev = block_scores.device
+    _expect(mask, "mask", (B, Hq, nbq, nbk), torch.uint8, dev)
+    _expect(kv_idx, "kv_idx", (B, Hq, nbq, nbk), torch.int32, dev)
+    _expect(kv_cnt, "kv_cnt", (B, Hq, nbq), torch.int32, dev)
     if mask is None and want_mask:
         mask = torch.empty((B, Hq, nbq, nbk), dtype=torch.uint8, device=dev)
     if kv_idx is None:
@@ -217,7 +253,11 @@ def bsa_fwd(q, k, v, kv_idx, kv_cnt, block, sm_scale, causal=True, out=None, wan
     """Block-sparse attention: (out, lse or None). selection=SELECT_GQA_UNION
     declares lists shared by sibling heads (any lists stay correct)."""
     _same(q, k, v)
-    p = _problem_of(q, k, block, 0, causal, selection=selection)
+    p = _problem_of(q, k, block, 0, causal, selection=selection, v=v)
+    B, Hq, nbq, nbk = _blocks(q, k, block)
+    _expect(kv_idx, "kv_idx", (B, Hq, nbq, nbk), torch.int32, q.device)
+    _expect(kv_cnt, "kv_cnt", (B, Hq, nbq), torch.int32, q.device)
+    _expect(out, "out", q.shape, q.dtype, q.device)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
     if ws is None:
@@ -231,7 +271,8 @@ def bsa_fwd(q, k, v, kv_idx, kv_cnt, block, sm_scale, causal=True, out=None, wan
 def dense_fwd(q, k, v, block, sm_scale, causal=True, out=None, want_lse=False):
     """Dense attention (every candidate block): (out, lse or None)."""
     _same(q, k, v)
-    p = _problem_of(q, k, block, 0, causal)
+    p = _problem_of(q, k, block, 0, causal, v=v)
+    _expect(out, "out", q.shape, q.dtype, q.device)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if want_lse else None
     _check(_lib.dense_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), float(sm_scale), _ptr(out),
@@ -240,29 +281,47 @@ def dense_fwd(q, k, v, block, sm_scale, causal=True, out=None, want_lse=False):
 
 
 class PrefillBuffers:
-    """Reusable device buffers for xattn_prefill (allocated once per shape)."""
+    """Reusable device buffers for xattn_prefill (allocated once per shape).
+
+    ``key`` records what the buffers were sized for; xattn_prefill refuses
+    inputs or arguments that differ from it. want_scores=False leaves the block
+    scores unwritten (not allowed with global selection)."""
 
     def __init__(self, q, k, block, stride, causal=True, want_mask=True, want_lse=False,
-                 pattern=ANTIDIAGONAL, selection=SELECT_ROW):
+                 pattern=ANTIDIAGONAL, selection=SELECT_ROW, want_scores=True, want_ws=True):
         p = _problem_of(q, k, block, stride, causal, pattern, selection)
         B, Hq, M, C = q.shape
         nbq, nbk = _cdiv(M, block), _cdiv(k.shape[2], block)
         dev = q.device
         self.problem = p
-        self.block_scores = torch.empty((B, Hq, nbq, nbk), dtype=torch.float32, device=dev)
+        self.key = _prefill_key(q, k, block, stride, causal, pattern, selection)
+        self.block_scores = (torch.empty((B, Hq, nbq, nbk), dtype=torch.float32, device=dev)
+                             if want_scores else None)
         self.mask = torch.empty((B, Hq, nbq, nbk), dtype=torch.uint8, device=dev) if want_mask else None
         self.kv_idx = torch.empty((B, Hq, nbq, nbk), dtype=torch.int32, device=dev)
         self.kv_cnt = torch.empty((B, Hq, nbq), dtype=torch.int32, device=dev)
-        self.ws = torch.empty(max(prefill_workspace_bytes(p), 4), dtype=torch.uint8, device=dev)
+        self.ws = (torch.empty(max(total_workspace_bytes(p), 4), dtype=torch.uint8, device=dev)
+                   if want_ws else None)
         self.out = torch.empty_like(q)
         self.lse = torch.empty((B, Hq, M), dtype=torch.float32, device=dev) if want_lse else None
 
 
+def _prefill_key(q, k, block, stride, causal, pattern, selection):
+    return (tuple(q.shape), tuple(k.shape), q.dtype, str(q.device), int(block), int(stride),
+            bool(causal), int(pattern), _selection(selection))
+
+
 def xattn_prefill(q, k, v, tau, block, stride, score_scale, sm_scale, causal=True, buffers=None,
-                  pattern=ANTIDIAGONAL, selection=SELECT_ROW):
-    """All three stages in one call. Returns the PrefillBuffers holding the results."""
+                  pattern=ANTIDIAGONAL, selection=SELECT_ROW, want_scores=True):
+    """All three stages in one call. Returns the PrefillBuffers holding the results
+    (block_scores is None when want_scores is False)."""
     _same(q, k, v)
-    bufs = buffers or PrefillBuffers(q, k, block, stride, causal, pattern=pattern, selection=selection)
+    _problem_of(q, k, block, stride, causal, pattern, selection, v=v)
+    if buffers is not None and buffers.key != _prefill_key(q, k, block, stride, causal, pattern, selection):
+        raise ValueError("buffers were made for other inputs or arguments: "
+                         f"{buffers.key} != {_prefill_key(q, k, block, stride, causal, pattern, selection)}")
+    bufs = buffers or PrefillBuffers(q, k, block, stride, causal, pattern=pattern, selection=selection,
+                                     want_scores=want_scores)
     tau_h = _tau_host(tau, q.shape[1])
     b = bufs
     _check(_lib.xattn_prefill(ctypes.byref(b.problem), _ptr(q), _ptr(k), _ptr(v), tau_h.data_ptr(),

@@ -54,6 +54,9 @@ xattn_status check_problem(const xattn_problem* p, bool need_stride = true) {
   const int nbk = (mk + p->block - 1) / p->block;
   if (nbk > XATTN_MAX_BLOCKS)
     return fail(XATTN_ERR_UNSUPPORTED, "%d key blocks exceed %d", nbk, XATTN_MAX_BLOCKS);
+  if (p->dtype == XATTN_F32 && mk > XATTN_F32_MAX_TOKENS)
+    return fail(XATTN_ERR_UNSUPPORTED, "float32 problems take at most %d key tokens (Mk=%d); use bf16",
+                XATTN_F32_MAX_TOKENS, mk);
   const size_t per_head = (size_t)mk * p->C;
   if ((size_t)p->B * p->Hq * per_head > ((size_t)1 << 40))
     return fail(XATTN_ERR_UNSUPPORTED, "problem too large");
@@ -199,6 +202,11 @@ size_t xattn_prefill_workspace_bytes(const xattn_problem* p) {
   return prefill_layout(p).total;
 }
 
+size_t xattn_workspace_bytes(const xattn_problem* p) {
+  // xattn_prefill's layout holds every other entry point's scratch
+  return xattn_prefill_workspace_bytes(p);
+}
+
 xattn_status xattn_score(const xattn_problem* p, const void* q, const void* k, float score_scale,
                          float* block_scores, void* ws, size_t ws_bytes, void* stream) {
   xattn_status s = check_problem(p);
@@ -256,8 +264,10 @@ xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
                            size_t ws_bytes, void* out, float* lse, void* stream) {
   xattn_status s = check_problem(p);
   if (s != XATTN_OK) return s;
-  if (!q || !k || !v || !block_scores || !kv_idx || !kv_cnt || !out)
-    return fail(XATTN_ERR_NULL, "q, k, v, block_scores, kv_idx, kv_cnt and out must be non-NULL");
+  if (!q || !k || !v || !kv_idx || !kv_cnt || !out)
+    return fail(XATTN_ERR_NULL, "q, k, v, kv_idx, kv_cnt and out must be non-NULL");
+  if (!block_scores && p->selection == XATTN_SELECT_GLOBAL)
+    return fail(XATTN_ERR_NULL, "global selection ranks the whole block-score matrix: block_scores must be non-NULL");
   if ((s = check_scale(score_scale, "score_scale")) != XATTN_OK) return s;
   if ((s = check_scale(sm_scale, "sm_scale")) != XATTN_OK) return s;
   xattn::TauArray t;

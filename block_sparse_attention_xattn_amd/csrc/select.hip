@@ -319,8 +319,8 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
 }
 
 // Fused stage 2 + 3: the row's block scores are computed from the partials
-// (written out as xattn_score would), kept in LDS as sort keys, and selected
-// without a round trip through HBM.
+// (written out as xattn_score would, unless the output pointer is null), kept
+// in LDS, and selected without a round trip through HBM.
 struct FusedArgs {
   const float* ws;
   float* scores;
@@ -347,12 +347,12 @@ __global__ __launch_bounds__(256) void score_select_kernel(FusedArgs a) {
   int npad = 1;
   while (npad < n) npad <<= 1;
   const float* L = a.ws + (bh * (size_t)a.NBq + I) * (size_t)NB * RB;
-  float* orow = a.scores + row * NB;
+  float* orow = a.scores ? a.scores + row * NB : nullptr;  // block scores are an optional output
   for (int p = tid; p < NB; p += 256) sh.flags[p] = 0;
 #if XATTN_SELECT_SORT
   for (int p = n + tid; p < npad; p += 256) sh.keys[p] = 0;
   block_score_row<RB>(L, n, NB, rows, shs, [&](int J, float sc) {
-    orow[J] = sc;
+    if (orow) orow[J] = sc;
     if (J < n) sh.keys[J] = sel_key(sc, J);
   });
   __syncthreads();
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(FusedArgs a) {
 #else
   (void)npad;
   block_score_row<RB>(L, n, NB, rows, shs, [&](int J, float sc) {
-    orow[J] = sc;
+    if (orow) orow[J] = sc;
     if (J < n) sh.sc[J] = sc;
   });
   __syncthreads();

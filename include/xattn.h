@@ -57,7 +57,15 @@
  * Supported shapes: dtype XATTN_BF16 or XATTN_F32; C in {64, 128};
  * block in {64, 128}; r = block/stride in {2, 4, 8, 16, 32};
  * 1 <= M <= Mk with Mk - M a multiple of block and NBk <= 4096;
- * 1 <= Hq <= 256; Hq a multiple of Hkv; causal in {0, 1}.
+ * 1 <= Hq <= 256; Hq a multiple of Hkv; causal in {0, 1}. XATTN_F32 runs
+ * scalar fp32 kernels meant for small layers at reference precision and
+ * accepts Mk <= XATTN_F32_MAX_TOKENS (otherwise XATTN_ERR_UNSUPPORTED); the
+ * bf16 path runs the MFMA kernels at every supported size.
+ *
+ * Workspaces: one size fits every call. xattn_workspace_bytes(p) is the
+ * scratch that xattn_prefill needs, and it is enough for each stage entry
+ * point on the same problem; the per-stage queries below return the smaller
+ * amounts each stage alone needs.
  */
 #ifndef XATTN_H
 #define XATTN_H
@@ -69,9 +77,12 @@
 extern "C" {
 #endif
 
-#define XATTN_ABI_VERSION 3
+#define XATTN_ABI_VERSION 4
 #define XATTN_MAX_HEADS 256
 #define XATTN_MAX_BLOCKS 4096
+/* XATTN_F32 problems run scalar fp32 kernels (reference precision for small
+ * layers) and take key lengths of at most this many tokens. */
+#define XATTN_F32_MAX_TOKENS 16384
 
 typedef enum {
   XATTN_OK = 0,
@@ -131,6 +142,10 @@ const char* xattn_status_string(xattn_status s);
 
 /* Message describing the calling thread's most recent failed call. */
 const char* xattn_last_error(void);
+
+/* Device workspace bytes that serve every entry point for problem p (equal
+ * to xattn_prefill_workspace_bytes(p)); 0 if p is invalid. */
+size_t xattn_workspace_bytes(const xattn_problem* p);
 
 /* Device workspace bytes xattn_score needs for problem p;
  * 0 if p is invalid. The workspace holds per-(strided row, key block) partial
@@ -223,7 +238,10 @@ xattn_status bsa_fwd(const xattn_problem* p, const void* q, const void* k,
 /*
  * Dense attention forward: bsa_fwd with every candidate block kept (all
  * J <= I + off/Bk when causal, all J otherwise). The reference point for
- * speedups.
+ * speedups: the pages measure the method's prefill speedup against dense
+ * FlashAttention ([XA-sum] "Key results": speedup relative to FlashInfer's
+ * FlashAttention at 256K tokens). Arguments as in bsa_fwd; no block lists and
+ * no workspace (one workgroup per query-block row or row pair, no queues).
  */
 xattn_status dense_fwd(const xattn_problem* p, const void* q, const void* k,
                        const void* v, float sm_scale, void* out, float* lse,
@@ -237,8 +255,11 @@ size_t xattn_prefill_workspace_bytes(const xattn_problem* p);
 /*
  * The three stages in one call ([Flex] R Q2: one call in place of standard
  * attention): xattn_score, then xattn_select, then bsa_fwd, all enqueued on
- * `stream`. Arguments as in those calls; mask and lse may be NULL; ws holds at
- * least xattn_prefill_workspace_bytes(p).
+ * `stream`. Arguments as in those calls; mask and lse may be NULL, and so may
+ * block_scores unless p->selection is XATTN_SELECT_GLOBAL (which ranks the
+ * head's whole block matrix): with per-row selection the scores of each row
+ * are normalised and selected in one pass and need not be written. ws holds
+ * at least xattn_prefill_workspace_bytes(p) (= xattn_workspace_bytes(p)).
  */
 xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
                            const void* v, const float* tau, float score_scale,

@@ -38,8 +38,9 @@ def near_tau_blocks(scores_row: np.ndarray, big_i: int, tau: float, causal: bool
 
 
 def mask_mismatches(mask_gpu: np.ndarray, mask_ref: np.ndarray, scores_for_band: np.ndarray,
-                    tau: np.ndarray, causal: bool, band: float, rows=None):
-    """Return (n_diff_blocks, n_unexplained) over (b, h, I) rows."""
+                    tau: np.ndarray, causal: bool, band: float, rows=None, qoff: int = 0):
+    """Return (n_diff_blocks, unexplained (b, h, I, J) list) over (b, h, I) rows;
+    query block I is key block I + qoff."""
     B, H, NB, _ = mask_gpu.shape
     n_diff = 0
     bad = []
@@ -49,11 +50,32 @@ def mask_mismatches(mask_gpu: np.ndarray, mask_ref: np.ndarray, scores_for_band:
         if d.size == 0:
             continue
         n_diff += d.size
-        ok = near_tau_blocks(scores_for_band[b, h, i], i, float(tau[h]), causal, band)
+        ok = near_tau_blocks(scores_for_band[b, h, i], i + qoff, float(tau[h]), causal, band)
         for J in d:
             if int(J) not in ok:
                 bad.append((b, h, i, int(J)))
     return n_diff, bad
+
+
+def check_mask(tag: str, mask_gpu: np.ndarray, mask_ref: np.ndarray, scores_for_band: np.ndarray,
+               tau: np.ndarray, causal: bool, band: float, rows=None, cap_frac: float = 0.02,
+               qoff: int = 0):
+    """Masks identical except near-tau blocks; print the count of such allowed
+    differences and cap the share of rows that hold any.
+
+    Returns (n_diff_blocks, n_rows_with_diffs, n_rows_compared).
+    """
+    B, H, NB, _ = mask_gpu.shape
+    it = list(rows) if rows is not None else [(b, h, i) for b in range(B) for h in range(H) for i in range(NB)]
+    n_diff, bad = mask_mismatches(mask_gpu, mask_ref, scores_for_band, tau, causal, band, it, qoff)
+    diff_rows = sum(1 for (b, h, i) in it
+                    if (mask_gpu[b, h, i].astype(bool) != mask_ref[b, h, i].astype(bool)).any())
+    print(f"[mask] {tag}: {len(it)} rows, {n_diff} near-tau block differences in {diff_rows} rows "
+          f"(band {band:.2e}), {len(bad)} unexplained", flush=True)
+    assert not bad, (tag, bad[:5])
+    cap = max(2, int(cap_frac * len(it)))
+    assert diff_rows <= cap, (tag, diff_rows, cap)
+    return n_diff, diff_rows, len(it)
 
 
 def check_index(mask: np.ndarray, kv_idx: np.ndarray, kv_cnt: np.ndarray):

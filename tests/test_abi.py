@@ -21,19 +21,23 @@ def xa():
 def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)   # preprocessor lines
     return sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)))
 
 
 def test_every_declared_symbol_is_exported(xa):
     names = _declared()
-    assert {"xattn_score", "xattn_select", "bsa_fwd", "dense_fwd", "xattn_prefill"} <= set(names)
+    # the boundary's calls: workspace size, the three stages, the dense
+    # baseline, the fused prefill and the housekeeping queries
+    assert {"xattn_workspace_bytes", "xattn_score", "xattn_select", "bsa_fwd", "dense_fwd", "xattn_prefill",
+            "xattn_status_string", "xattn_abi_version"} <= set(names)
     for n in names:
         assert hasattr(xa._lib, n), n
     assert set(xa.EXPORTS) == set(names)
 
 
 def test_version_and_strings(xa):
-    assert xa._lib.xattn_abi_version() == 3
+    assert xa._lib.xattn_abi_version() == 4
     for s in range(8):
         assert xa._lib.xattn_status_string(s)
     assert xa._lib.xattn_status_string(99) == b"unknown status"
@@ -145,3 +149,111 @@ def test_attention_ignores_stride(xa):
     L = xa._lib
     assert L.dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, 0.0, FAKE, None, None) == 4
     assert L.xattn_score(ctypes.byref(p), FAKE, FAKE, 0.01, FAKE, FAKE, 1 << 40, None) == 2
+
+
+def test_one_workspace_size_serves_every_entry_point(xa):
+    for kw in (dict(), dict(selection=1), dict(selection=2), dict(M=1000, Mk=1256), dict(stride=16),
+               dict(dtype=1, M=512)):
+        p = _p(xa, **kw)
+        total = xa.total_workspace_bytes(p)
+        assert total == xa.prefill_workspace_bytes(p) > 0
+        assert total >= max(xa.workspace_bytes(p), xa.select_workspace_bytes(p), xa.attn_workspace_bytes(p))
+    assert xa.total_workspace_bytes(_p(xa, Hkv=3)) == 0
+
+
+def test_f32_envelope(xa):
+    # the scalar fp32 kernels take at most 16384 key tokens; bf16 has no such limit
+    L = xa._lib
+    ok = _p(xa, dtype=1, M=16384)
+    big = _p(xa, dtype=1, M=16384 + 128)
+    chunk = _p(xa, dtype=1, M=128, Mk=16384 + 128)
+    assert xa.workspace_bytes(ok) > 0
+    for p in (big, chunk):
+        assert xa.workspace_bytes(p) == 0
+        assert L.xattn_score(ctypes.byref(p), FAKE, FAKE, 0.01, FAKE, FAKE, 1 << 40, None) == 5
+        assert L.dense_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, 0.1, FAKE, None, None) == 5
+        assert b"16384" in L.xattn_last_error()
+    assert xa.workspace_bytes(_p(xa, dtype=0, M=16384 + 128)) > 0
+
+
+def test_prefill_block_scores_optional_except_global(xa):
+    L = xa._lib
+    arr = (ctypes.c_float * 4)(0.9, 0.9, 0.9, 0.9)
+    g = _p(xa, selection=1)
+    need = xa.total_workspace_bytes(g)
+    assert L.xattn_prefill(ctypes.byref(g), FAKE, FAKE, FAKE, arr, 0.01, 0.1, None, None, FAKE, FAKE,
+                           FAKE, need, FAKE, None, None) == 1
+    assert b"global" in L.xattn_last_error()
+    # per-row selection: a NULL block_scores passes validation (the workspace
+    # check, which comes later, is what fails here)
+    p = _p(xa)
+    assert L.xattn_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, arr, 0.01, 0.1, None, None, FAKE, FAKE,
+                           FAKE, 16, FAKE, None, None) == 6
+
+
+# ---------------------------------------------------------------- the binding's own checks
+# Shapes, dtypes and devices are checked in Python before any pointer is taken
+# or any launch is made; CPU tensors reach the device check last.
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_rejects_mismatched_tensors_before_launch(xa):
+    import torch
+    q, k, v = _t(1, 4, 256, 128), _t(1, 2, 256, 128), _t(1, 2, 256, 128)
+    i32, f32, u8 = torch.int32, torch.float32, torch.uint8
+    with pytest.raises(ValueError, match="v "):
+        xa.bsa_fwd(q, k, _t(1, 2, 255, 128), _t(1, 4, 2, 2, dtype=i32), _t(1, 4, 2, dtype=i32), 128, 0.1)
+    with pytest.raises(ValueError, match="v "):
+        xa.dense_fwd(q, k, _t(1, 1, 256, 128), 128, 0.1)
+    with pytest.raises(ValueError, match="kv_idx"):
+        xa.bsa_fwd(q, k, v, _t(1, 4, 2, 3, dtype=i32), _t(1, 4, 2, dtype=i32), 128, 0.1)
+    with pytest.raises(ValueError, match="kv_idx"):
+        xa.bsa_fwd(q, k, v, _t(1, 4, 2, 2, dtype=torch.int64), _t(1, 4, 2, dtype=i32), 128, 0.1)
+    with pytest.raises(ValueError, match="kv_cnt"):
+        xa.bsa_fwd(q, k, v, _t(1, 4, 2, 2, dtype=i32), _t(1, 4, 3, dtype=i32), 128, 0.1)
+    with pytest.raises(ValueError, match="out"):
+        xa.bsa_fwd(q, k, v, _t(1, 4, 2, 2, dtype=i32), _t(1, 4, 2, dtype=i32), 128, 0.1,
+                   out=_t(1, 4, 256, 64))
+    with pytest.raises(ValueError, match="k "):
+        xa.xattn_score(q, _t(1, 2, 256, 64), 128, 8, 0.01)
+    with pytest.raises(ValueError, match="block_scores"):
+        xa.xattn_score(q, k, 128, 8, 0.01, block_scores=_t(1, 4, 2, 2, dtype=torch.float64))
+    with pytest.raises(ValueError, match="block_scores"):
+        xa.xattn_select(_t(1, 4, 2, 2), [0.9], 128, 8)
+    with pytest.raises(ValueError, match="kv_cnt"):
+        xa.xattn_select(_t(1, 4, 2, 2, dtype=f32), [0.9], 128, 8, kv_cnt=_t(1, 4, 2, dtype=torch.int16))
+    with pytest.raises(ValueError, match="mask"):
+        xa.xattn_select(_t(1, 4, 2, 2, dtype=f32), [0.9], 128, 8, mask=_t(1, 4, 2, 2, dtype=torch.bool))
+    with pytest.raises(ValueError, match="dtype"):
+        xa.dense_fwd(q, k.float(), v, 128, 0.1)
+    # well-formed CPU tensors reach the device check, still before any launch
+    with pytest.raises(ValueError, match="GPU"):
+        xa.dense_fwd(q, k, v, 128, 0.1)
+    with pytest.raises(ValueError, match="GPU"):
+        xa.bsa_fwd(q, k, v, _t(1, 4, 2, 2, dtype=i32), _t(1, 4, 2, dtype=i32), 128, 0.1)
+    del u8
+
+
+def test_prefill_buffers_refuse_other_inputs(xa):
+    q, k, v = _t(1, 4, 256, 128), _t(1, 2, 256, 128), _t(1, 2, 256, 128)
+    bufs = xa.PrefillBuffers(q, k, 128, 8, True)
+    assert bufs.key[0] == (1, 4, 256, 128)
+    q2, k2, v2 = _t(1, 4, 384, 128), _t(1, 2, 384, 128), _t(1, 2, 384, 128)
+    with pytest.raises(ValueError, match="buffers"):
+        xa.xattn_prefill(q2, k2, v2, 0.9, 128, 8, 0.01, 0.1, True, buffers=bufs)
+    for kw in (dict(stride=16), dict(causal=False), dict(selection="global"), dict(pattern=1)):
+        args = dict(stride=8, causal=True)
+        args.update({x: y for x, y in kw.items() if x in args})
+        extra = {x: y for x, y in kw.items() if x not in args}
+        with pytest.raises(ValueError, match="buffers"):
+            xa.xattn_prefill(q, k, v, 0.9, 128, args["stride"], 0.01, 0.1, args["causal"], buffers=bufs,
+                             **extra)
+    with pytest.raises(ValueError, match="v "):
+        xa.xattn_prefill(q, k, _t(1, 2, 128, 128), 0.9, 128, 8, 0.01, 0.1, True, buffers=bufs)
+    with pytest.raises(ValueError, match="GPU"):
+        xa.xattn_prefill(q, k, v, 0.9, 128, 8, 0.01, 0.1, True, buffers=bufs)
+    nos = xa.PrefillBuffers(q, k, 128, 8, True, want_scores=False)
+    assert nos.block_scores is None

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import workloads as wl
-from tests.gpu_util import check_index, f64, mask_mismatches, near_tau_blocks, score_tol
+from tests.gpu_util import check_index, check_mask, f64, near_tau_blocks, score_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -193,8 +193,7 @@ def test_select_matches_oracle_on_same_scores(xa, tau, causal):
     s64 = scores.numpy().astype(np.float64)
     ref = oracle.select(s64, taus, causal)
     m = mask.cpu().numpy()
-    n_diff, bad = mask_mismatches(m, ref, s64, np.array(taus), causal, 1e-5)
-    assert not bad, bad[:5]
+    check_mask(f"select tau={tau} causal={causal}", m, ref, s64, np.array(taus), causal, 1e-5)
     check_index(m, idx.cpu().numpy(), cnt.cpu().numpy())
 
 
@@ -301,13 +300,11 @@ def test_prefill_end_to_end(xa, name, over):
     g_mask = bufs.mask.cpu().numpy()
     # selection parity on the GPU's own scores
     same = oracle.select(g_sc, tau, w.causal)
-    _, bad = mask_mismatches(g_mask, same, g_sc, tau, w.causal, 1e-5)
-    assert not bad, bad[:5]
+    check_mask(f"{name} select on GPU scores", g_mask, same, g_sc, tau, w.causal, 1e-5)
     # end to end: differences only where the score tolerance can move the cut
     ref_mask = oracle.select(ref_sc, tau, w.causal)
     band = 1e-5 + 1e-4 + w.nb * 1e-7
-    _, bad = mask_mismatches(g_mask, ref_mask, ref_sc, tau, w.causal, band)
-    assert not bad, bad[:5]
+    check_mask(f"{name} end to end", g_mask, ref_mask, ref_sc, tau, w.causal, band)
     check_index(g_mask, bufs.kv_idx.cpu().numpy(), bufs.kv_cnt.cpu().numpy())
     # attention parity with the GPU's mask (isolates the attention stage)
     ref_out, _ = oracle.attend(q, k, v, g_mask, w.block, smscale, w.causal)
@@ -521,7 +518,44 @@ def test_diagonal_pattern_prefill_end_to_end(xa):
     ref_sc = oracle.block_scores(q, k, w.block, w.stride, sscale, w.causal, pattern="diagonal")
     assert not (np.abs(g_sc - ref_sc) > score_tol(ref_sc)).any()
     g_mask = bufs.mask.cpu().numpy()
-    _, bad = mask_mismatches(g_mask, oracle.select(g_sc, tau, w.causal), g_sc, tau, w.causal, 1e-5)
-    assert not bad
+    check_mask("diagonal pattern select on GPU scores", g_mask, oracle.select(g_sc, tau, w.causal), g_sc,
+               tau, w.causal, 1e-5)
     ref_out, _ = oracle.attend(q, k, v, g_mask, w.block, smscale, w.causal)
     assert np.abs(f64(bufs.out) - ref_out).max() <= 2e-2
+
+
+@pytest.mark.parametrize("name,over", [("llama32k", dict(M=4096, Hq=8, Hkv=2)),
+                                       ("video", dict(M=2560, Hq=2, Hkv=2)),
+                                       ("llama128k", dict(M=8192, Hq=4, Hkv=1, selection="gqa_union"))],
+                         ids=["llama32k-4096", "video-2560", "llama128k-8192-gqa-union"])
+def test_prefill_without_block_scores(xa, name, over):
+    # block scores are an optional output of xattn_prefill: with a NULL pointer
+    # the fused normalise+select pass skips their write, and the selection and
+    # output are bitwise those of the call that writes them
+    over = dict(over)
+    sel = over.pop("selection", "row")
+    w = wl.WORKLOADS[name].scaled(**over)
+    x = wl.make_inputs(w, device=DEV)
+    sscale, smscale = wl.default_scales(w)
+    args = (x["q"], x["k"], x["v"], x["tau"], w.block, w.stride, sscale, smscale, w.causal)
+    ref = xa.xattn_prefill(*args, selection=sel)
+    got = xa.xattn_prefill(*args, selection=sel, want_scores=False)
+    torch.cuda.synchronize()
+    assert got.block_scores is None
+    assert torch.equal(ref.mask, got.mask)
+    assert torch.equal(ref.kv_cnt, got.kv_cnt)
+    valid = torch.arange(ref.kv_idx.shape[-1], device=DEV) < ref.kv_cnt[..., None]
+    assert torch.equal(ref.kv_idx[valid], got.kv_idx[valid])
+    assert torch.equal(ref.out, got.out)
+    # and the selection is the oracle's on these scores
+    g_sc = f64(ref.block_scores)
+    tau = x["tau"].numpy().astype(np.float64)
+    rows = oracle.select(g_sc, tau, w.causal, mode=sel, hkv=w.Hkv)
+    if sel == "row":
+        check_mask(f"{name} no-scores prefill", got.mask.cpu().numpy(), rows, g_sc, tau, w.causal, 1e-5)
+    check_index(got.mask.cpu().numpy(), got.kv_idx.cpu().numpy(), got.kv_cnt.cpu().numpy())
+    q, k, v = f64(x["q"]), f64(x["k"]), f64(x["v"])
+    heads = [0, w.Hq - 1]
+    ref_out, _ = oracle.attend(q, k, v, got.mask.cpu().numpy(), w.block, smscale, w.causal, heads=heads)
+    err = max(np.abs(f64(got.out[:, h]) - ref_out[:, h]).max() for h in heads)
+    assert err <= 2e-2, err

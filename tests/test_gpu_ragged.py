@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_util import check_index, f64, near_tau_blocks, score_tol
+from tests.gpu_util import check_index, check_mask, f64, near_tau_blocks, score_tol
 
 pytestmark = pytest.mark.gpu
 
@@ -74,15 +74,8 @@ def test_scores_ragged_chunked(xa, case):
 
 
 def _check_rows(mask_gpu, scores_gpu, tau, causal, qoff):
-    B, H, NBq, _ = mask_gpu.shape
     ref = oracle.select(scores_gpu, tau, causal)
-    for b in range(B):
-        for h in range(H):
-            for i in range(NBq):
-                d = np.nonzero(mask_gpu[b, h, i].astype(bool) != ref[b, h, i].astype(bool))[0]
-                if d.size:
-                    ok = near_tau_blocks(scores_gpu[b, h, i], i + qoff, float(tau[h]), causal, 1e-5)
-                    assert all(int(J) in ok for J in d), (b, h, i, d)
+    check_mask(f"ragged/chunked select qoff={qoff}", mask_gpu, ref, scores_gpu, tau, causal, 1e-5, qoff=qoff)
 
 
 @pytest.mark.parametrize("case", CASES, ids=_ids)

@@ -10,6 +10,7 @@
   candidate and equals dense attention, monotonicity in tau, diagonal kept.
 """
 import itertools
+import math
 import os
 
 import numpy as np
@@ -121,6 +122,53 @@ def test_stride_one_equals_textbook_block_attention_mass(causal):
                                      big_j * block:(big_j + 1) * block].sum() / block
     got = oracle.block_scores(q[None, None], k[None, None], block, 1, scale, causal)[0, 0]
     np.testing.assert_allclose(got, expect, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("stride,r", [(2, 2), (2, 4), (4, 2), (4, 4)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_scores_bruteforce_composition(stride, r, causal):
+    # The whole scoring stage at S > 1 and r > 1, built from the token-level
+    # logit matrix with plain loops: every strided cell walks its S x S tile's
+    # antidiagonal (query row descending while the key column ascends), each
+    # strided query row is softmaxed over its strided keys (j <= i when causal),
+    # and every r x r tile of probabilities is summed and divided by r.
+    rng = _rng(100 + 10 * stride + r)
+    block = stride * r
+    nb, c = 3, 5
+    m = nb * block
+    q = rng.standard_normal((m, c))
+    k = rng.standard_normal((m, c))
+    scale = 0.37
+    big_r = m // stride
+    cell = [[0.0] * big_r for _ in range(big_r)]
+    for i in range(big_r):
+        for j in range(big_r):
+            tot = 0.0
+            for a in range(stride):
+                tot += float(q[i * stride + stride - 1 - a] @ k[j * stride + a])
+            cell[i][j] = scale * tot
+    expect = np.zeros((nb, nb))
+    for i in range(big_r):
+        keys = range(i + 1) if causal else range(big_r)
+        top = max(cell[i][j] for j in keys)
+        z = sum(math.exp(cell[i][j] - top) for j in keys)
+        for j in keys:
+            expect[i // r, j // r] += math.exp(cell[i][j] - top) / z / r
+    got = oracle.block_scores(q[None, None], k[None, None], block, stride, scale, causal)[0, 0]
+    np.testing.assert_allclose(got, expect, rtol=1e-12, atol=1e-15)
+    # the other score temperatures (the literal sum, and attention on the
+    # reshaped rows) only rescale the cells
+    for temp in (1.0, 1.0 / math.sqrt(stride)):
+        exp2 = np.zeros((nb, nb))
+        for i in range(big_r):
+            keys = range(i + 1) if causal else range(big_r)
+            vals = [temp * cell[i][j] / scale for j in keys]
+            top = max(vals)
+            z = sum(math.exp(x - top) for x in vals)
+            for j, x in zip(keys, vals):
+                exp2[i // r, j // r] += math.exp(x - top) / z / r
+        got2 = oracle.block_scores(q[None, None], k[None, None], block, stride, temp, causal)[0, 0]
+        np.testing.assert_allclose(got2, exp2, rtol=1e-12, atol=1e-15)
 
 
 @pytest.mark.parametrize("causal", [True, False])
