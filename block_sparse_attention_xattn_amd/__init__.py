@@ -36,7 +36,7 @@ EXPORTS = (
     "xattn_abi_version", "xattn_status_string", "xattn_last_error", "xattn_workspace_bytes",
     "xattn_score_workspace_bytes", "xattn_select_workspace_bytes", "xattn_attn_workspace_bytes",
     "xattn_prefill_workspace_bytes", "xattn_score", "xattn_select", "bsa_fwd",
-    "dense_fwd", "xattn_prefill",
+    "dense_fwd", "xattn_prefill", "xattn_prefill_noalloc",
 )
 
 
@@ -80,6 +80,8 @@ _lib.bsa_fwd.restype = ctypes.c_int
 _lib.bsa_fwd.argtypes = [_P, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.dense_fwd.restype = ctypes.c_int
 _lib.dense_fwd.argtypes = [_P, _vp, _vp, _vp, _f, _vp, _vp, _vp]
+_lib.xattn_prefill_noalloc.restype = ctypes.c_int
+_lib.xattn_prefill_noalloc.argtypes = [_P, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.xattn_prefill.restype = ctypes.c_int
 _lib.xattn_prefill.argtypes = [_P, _vp, _vp, _vp, _vp, _f, _f, _vp, _vp, _vp, _vp, _vp,
                                ctypes.c_size_t, _vp, _vp, _vp]
@@ -328,6 +330,30 @@ def xattn_prefill(q, k, v, tau, block, stride, score_scale, sm_scale, causal=Tru
                               float(score_scale), float(sm_scale), _ptr(b.block_scores), _ptr(b.mask),
                               _ptr(b.kv_idx), _ptr(b.kv_cnt), _ptr(b.ws),
                               b.ws.numel(), _ptr(b.out), _ptr(b.lse), _stream(q.device)))
+    return b
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def xattn_prefill_noalloc(q, k, v, tau, block, stride, score_scale, sm_scale, causal=True, buffers=None,
+                          pattern=ANTIDIAGONAL, selection=SELECT_ROW, want_scores=True):
+    """xattn_prefill on the library's own per-GPU scratch (no workspace), for
+    callers that cannot allocate device memory. Pass ``buffers`` (a
+    PrefillBuffers, e.g. made with want_ws=False) to allocate nothing here
+    either. Calls that overlap on one GPU share the scratch and race."""
+    _same(q, k, v)
+    _problem_of(q, k, block, stride, causal, pattern, selection, v=v)
+    if buffers is not None and buffers.key != _prefill_key(q, k, block, stride, causal, pattern, selection):
+        raise ValueError("buffers were made for other inputs or arguments")
+    bufs = buffers or PrefillBuffers(q, k, block, stride, causal, pattern=pattern, selection=selection,
+                                     want_scores=want_scores, want_ws=False)
+    tau_h = _tau_host(tau, q.shape[1])
+    b = bufs
+    _check(_lib.xattn_prefill_noalloc(ctypes.byref(b.problem), _ptr(q), _ptr(k), _ptr(v), tau_h.data_ptr(),
+                                      float(score_scale), float(sm_scale), _ptr(b.block_scores), _ptr(b.mask),
+                                      _ptr(b.kv_idx), _ptr(b.kv_cnt), _ptr(b.out), _ptr(b.lse),
+                                      _stream(q.device)))
     return b
 
 

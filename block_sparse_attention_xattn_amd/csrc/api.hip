@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/xattn.h"
 #include "kernels.h"
@@ -164,6 +165,34 @@ PrefillLayout prefill_layout(const xattn_problem* p) {
   return l;
 }
 
+// Scratch of xattn_prefill_noalloc: one file-scope device array (each GPU the
+// library runs on holds its own copy until the process ends). Host code never
+// uses the array's name as an address: it is a host-side stand-in. The device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept per device.
+static __device__ __align__(256) unsigned char scratch[XATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+xattn_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(XATTN_ERR_UNSUPPORTED, "device %d is beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(XATTN_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return XATTN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -298,6 +327,24 @@ xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
       return s;
   }
   return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, wsb + lay.queue_off, st);
+}
+
+xattn_status xattn_prefill_noalloc(const xattn_problem* p, const void* q, const void* k, const void* v,
+                                   const float* tau, float score_scale, float sm_scale, float* block_scores,
+                                   uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, void* out, float* lse,
+                                   void* stream) {
+  xattn_status s = check_problem(p);
+  if (s != XATTN_OK) return s;
+  const size_t need = xattn_prefill_workspace_bytes(p);
+  if (need > (size_t)XATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(XATTN_ERR_WORKSPACE,
+                "problem needs %zu bytes of scratch; xattn_prefill_noalloc holds %zu (use xattn_prefill with a "
+                "caller workspace)",
+                need, (size_t)XATTN_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((s = scratch_of_current_device(&ws)) != XATTN_OK) return s;
+  return xattn_prefill(p, q, k, v, tau, score_scale, sm_scale, block_scores, mask, kv_idx, kv_cnt, ws,
+                       (size_t)XATTN_NOALLOC_SCRATCH_BYTES, out, lse, stream);
 }
 
 }  // extern "C"

@@ -267,6 +267,32 @@ xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
                            int32_t* kv_idx, int32_t* kv_cnt, void* ws,
                            size_t ws_bytes, void* out, float* lse, void* stream);
 
+/* Scratch held by xattn_prefill_noalloc on each GPU it runs on. */
+#define XATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * xattn_prefill without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Its scratch is a library-owned array of
+ * XATTN_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held until the process ends;
+ * the call itself allocates nothing (no hipMalloc or allocating library
+ * routine). The caller still passes every input and output, with the
+ * meanings, layouts and NULL rules of xattn_prefill, and the results are
+ * those of xattn_prefill.
+ *
+ * Limits: problems whose xattn_workspace_bytes(p) exceeds
+ * XATTN_NOALLOC_SCRATCH_BYTES return XATTN_ERR_WORKSPACE before anything is
+ * enqueued (e.g. 32 query heads, r = 16: up to about 22K tokens). Every call on
+ * one GPU shares that GPU's array, and each call clears what must start at
+ * zero on its stream: calls that may overlap in time on one GPU (several
+ * streams or threads) race and give undefined results; serialise them.
+ */
+xattn_status xattn_prefill_noalloc(const xattn_problem* p, const void* q, const void* k,
+                                   const void* v, const float* tau, float score_scale,
+                                   float sm_scale, float* block_scores, uint8_t* mask,
+                                   int32_t* kv_idx, int32_t* kv_cnt, void* out, float* lse,
+                                   void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -257,3 +257,18 @@ def test_prefill_buffers_refuse_other_inputs(xa):
         xa.xattn_prefill(q, k, v, 0.9, 128, 8, 0.01, 0.1, True, buffers=bufs)
     nos = xa.PrefillBuffers(q, k, 128, 8, True, want_scores=False)
     assert nos.block_scores is None
+
+
+def test_noalloc_rejects_oversized_problems_on_the_host(xa):
+    # 32 heads at 32K tokens need 128 MiB of scratch, past the 64 MiB the
+    # no-allocation entry point holds: refused before the device is touched
+    L = xa._lib
+    arr = (ctypes.c_float * 32)(*([0.9] * 32))
+    p = _p(xa, Hq=32, Hkv=8, M=32768)
+    assert xa.total_workspace_bytes(p) > xa.NOALLOC_SCRATCH_BYTES == 64 << 20
+    rc = L.xattn_prefill_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, arr, 0.01, 0.1, FAKE, None, FAKE, FAKE,
+                                 FAKE, None, None)
+    assert rc == 6
+    assert b"scratch" in L.xattn_last_error()
+    assert L.xattn_prefill_noalloc(ctypes.byref(_p(xa, C=96)), FAKE, FAKE, FAKE, arr, 0.01, 0.1, FAKE, None,
+                                   FAKE, FAKE, FAKE, None, None) == 5
