@@ -74,6 +74,24 @@
 #ifndef XATTN_KBATCH
 #define XATTN_KBATCH 2
 #endif
+// 1: the 8-wave modes run the software-pipelined loop (K/V sub-tiles DMA'd
+// into a four-slot LDS ring; the S MFMAs of sub-tile t+1 interleaved with the
+// exponentials of sub-tile t, and the row maximum of t+1 with the PV MFMAs of
+// t); 0: the register-staged loop with one barrier per sub-tile
+#ifndef XATTN_ATTN_PIPE
+#define XATTN_ATTN_PIPE 1
+#endif
+// 1: the pipelined loop issues each sub-tile's DMA pieces spread over the S
+// MFMAs of the common path (one piece every four MFMAs) instead of all at once
+// after the barrier; 0: all at once
+#ifndef XATTN_DMA_SPREAD
+#define XATTN_DMA_SPREAD 1
+#endif
+// 1: Q is loaded and O stored with the non-temporal hint (read once and
+// written once, so they need not displace K/V from the caches)
+#ifndef XATTN_NT_QO
+#define XATTN_NT_QO 0
+#endif
 
 namespace xattn {
 
@@ -103,6 +121,9 @@ struct AttnLds {
   // K and V double buffers and the block list (u16); with several heads per
   // workgroup also per-entry head bits and a per-block flag scratch (u8 each)
   static constexpr int bytes(int hpw) { return 2 * 2 * TILE_B + 2 * IDX_MAX + (hpw > 1 ? 2 * IDX_MAX : 0); }
+  // the pipelined loop: a ring of RING sub-tile slots (K then V), then the lists
+  static constexpr int RING = 4;
+  static constexpr int bytes_pipe(int hpw) { return RING * 2 * TILE_B + 2 * IDX_MAX + (hpw > 1 ? 2 * IDX_MAX : 0); }
   // LDS serves 256 B per clock in 64 banks of 4 B. Rows are stored unpadded and
   // the 16-byte chunks (K) or 64-byte segments (V) of each row are XOR-permuted
   // by the row index so that
@@ -149,6 +170,38 @@ struct AttnItems {
   }
 };
 
+// LDS byte address of a pointer into a __shared__ array, made wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr_u(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// A 64-bit pointer that is the same in every lane, in scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// DMA of 16 bytes per lane from global memory (wave-uniform base plus a
+// per-lane byte offset) straight into LDS: the 64 lanes fill the 1 KiB at
+// lds_base in lane order. Written as asm so the compiler, which would treat
+// every LDS read after such a load as dependent on it, adds no waits of its
+// own: the loop that issues these waits for them explicitly (vm_wait) before
+// the barrier that publishes the data. It has no register results.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
+}
+
+// Waits until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
 // One work item: all rows of the slots it covers, from the block list to the
 // normalised output. Starts and ends with every wave of the workgroup past a
 // barrier after its last LDS read, so consecutive items may reuse the LDS.
@@ -174,12 +227,15 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   constexpr int DEPTH = SLOTS == 2 && RPW == 32 ? 2 : 1;  // sub-tiles in flight in registers
   static_assert(CHUNKS % NT == 0, "tile load must divide evenly");
 
+  // the pipelined loop serves the 8-wave modes
+  constexpr bool PIPE = XATTN_ATTN_PIPE != 0 && SLOTS == 2 && RPW == 32;
+  constexpr int TILES_B = (PIPE ? L::RING : 2) * 2 * L::TILE_B;  // bytes of K/V tiles
   unsigned char* Ks = smem;                      // [2][KT rows][2C bytes], swizzled
   unsigned char* Vs = smem + 2 * L::TILE_B;      // [2][KT rows][2C bytes], swizzled
   // block list (union over the workgroup's slots) and, per entry, a bit per
   // slot that selected it
-  uint16_t* idx_s = reinterpret_cast<uint16_t*>(smem + 4 * L::TILE_B);
-  uint8_t* memb_s = smem + 4 * L::TILE_B + 2 * L::IDX_MAX;
+  uint16_t* idx_s = reinterpret_cast<uint16_t*>(smem + TILES_B);
+  uint8_t* memb_s = smem + TILES_B + 2 * L::IDX_MAX;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -305,8 +361,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
     // query row instead; their outputs are never stored
     const uint16_t* qrow = qh + (size_t)min(live ? q0 + 32 * y + l32 : l32, a.Mq - 1) * C + 8 * hh;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qf[y][kk] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * kk));
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(qrow + 16 * kk);
+      qf[y][kk] = __builtin_bit_cast(bf16x8, XATTN_NT_QO ? __builtin_nontemporal_load(src) : *src);
+    }
   }
   // Complete the Q loads here. Otherwise the compiler may leave them in flight
   // into the key loop, and since the load counter is in-order, every first use
@@ -453,14 +511,18 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
           for (int r = 0; r < 16; ++r) o[y][d][r] *= alpha;
       }
       const float m_use = (m_run[y] == -INFINITY) ? 0.f : m_run[y];
+      // row sums in four partial sums, in the pipelined loop's order (the two
+      // loops then give bitwise the same output)
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float pr = fast_exp2(fmaf(sacc[y][n][r], a.scale_log2, -m_use));
-          l_run[y] += pr;
+          ls[r & 3] += pr;
           pb[y][2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
         }
+      l_run[y] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     }
 
     // O^T[d][q] += V^T[d][key] P^T[key][q] over 16-key chunks tc
@@ -480,47 +542,353 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
     }
   };
 
-  __syncthreads();  // block list visible
-  if constexpr (DEPTH == 1) {
-    Stage r0;
-    uint32_t e0 = entry(0), e1 = entry(1);  // entries of tiles t, t+1
+  if constexpr (PIPE) {
+    // ---- software-pipelined loop over the sub-tiles of the block list.
+    // K/V sub-tiles reach LDS by DMA (no staging registers) into a ring of
+    // four slots: tile t sits in slot t % 4. Iteration t, after one barrier:
+    //   * DMA of tile t+3 into the slot of tile t-1 (every wave is past it);
+    //   * lazy rescale for tile t (rare);
+    //   * S(t+1) = K(t+1) Q^T on the matrix cores, interleaved with the
+    //     exponentials of tile t (P(t), the row sums);
+    //   * O += V(t)^T P(t) on the matrix cores, interleaved with the masks and
+    //     the row maximum of tile t+1.
+    // So the softmax VALU work of a wave overlaps its own MFMAs, and the
+    // loads of tile t+3 have two iterations to land.
+    constexpr int BLKS = L::TILE_B / 1024;           // 1 KiB DMA blocks per K (or V) sub-tile
+    constexpr int BPW = BLKS / (NT / 64);            // ... per wave
+    static_assert(BPW >= 1 && BPW * (NT / 64) == BLKS, "DMA blocks must cover the sub-tile");
+    constexpr int DPT = 2 * BPW;                     // DMA loads per wave per sub-tile
+    constexpr int RPB = 1024 / L::ROW_B;             // key rows per DMA block
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    // lane's 16 bytes of each of its DMA blocks: the tile row, and the byte
+    // offset in that row of the global piece that belongs at its LDS position
+    // under the K and V swizzles of AttnLds
+    // (without a key tail: byte offsets from the sub-tile's first row; with
+    // one: the row and the in-row offsets, clamped per sub-tile)
+    uint32_t kcb[BPW], vcb[BPW];
+    int lrow[KTAIL ? BPW : 1];
+#pragma unroll
+    for (int b2 = 0; b2 < BPW; ++b2) {
+      const int row = (wv * BPW + b2) * RPB + (16 * lane) / L::ROW_B;
+      const int pos = (16 * lane) % L::ROW_B;
+      const int sw = row / L::ROWS_PER_256;
+      const uint32_t kc = 16 * ((pos / 16) ^ (sw % (C / 8)));
+      const uint32_t vc = pos ^ (64 * (sw % (C / 32)));
+      if constexpr (KTAIL) {
+        lrow[b2] = row;
+        kcb[b2] = kc;
+        vcb[b2] = vc;
+      } else {
+        kcb[b2] = (uint32_t)row * (2 * C) + kc;
+        vcb[b2] = (uint32_t)row * (2 * C) + vc;
+      }
+    }
+    auto slot_k = [&](int slot) { return smem + slot * 2 * L::TILE_B; };
+    auto slot_v = [&](int slot) { return smem + slot * 2 * L::TILE_B + L::TILE_B; };
+    // piece p of a sub-tile's DMA: block p / 2 of this wave, K (p even) or V
+    constexpr int NPIECE = 2 * BPW;
+    auto dma_piece = [&](int k0, int slot, int p) {
+      const int b2 = p >> 1;
+      const bool isv = p & 1;
+      const uint32_t lds = lds_addr_u((isv ? slot_v(slot) : slot_k(slot)) + (wv * BPW + b2) * 1024);
+      const uint16_t* base = isv ? vh : kh;
+      const uint32_t cb = isv ? vcb[b2] : kcb[b2];
+      if constexpr (KTAIL) {
+        // keys past the end load the last key; they are masked out of the softmax
+        const uint32_t r = (uint32_t)min(k0 + lrow[b2], a.Mk - 1) * (2 * C);
+        dma16(uniform_ptr(base), r + cb, lds);
+      } else {
+        dma16(uniform_ptr(base + (size_t)k0 * C), cb, lds);
+      }
+    };
+    auto dma_tile = [&](int k0, int slot) {
+#pragma unroll
+      for (int p2 = 0; p2 < NPIECE; ++p2) dma_piece(k0, slot, p2);
+    };
+    // is sub-tile t (entry en) computed by this wave: selected by its slot,
+    // not wholly above its rows (causal), not wholly past the last key
+    auto active = [&](uint32_t en, int t) -> bool {
+      const int k0 = key_start(en, t);
+      if (CAUSAL && k0 > qa0 + RPW - 1) return false;
+      if (KTAIL && k0 >= a.Mk) return false;
+      return mine_tile(en);
+    };
+    // S^T tiles (n): keys k0 + 32n + [8(r/4) + 4hh + r%4], query q0 + l32
+    auto s_mma = [&](int slot, f32x16 (&acc)[2]) {
+      const unsigned char* Kb = slot_k(slot);
+      acc[0] = acc[1] = f32x16{};
+      constexpr int KB = XATTN_KBATCH < KK ? XATTN_KBATCH : KK;
+#pragma unroll
+      for (int k0b = 0; k0b < KK; k0b += KB) {
+        bf16x8 ka[KB][2];
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            ka[u][n] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const u32x4*>(Kb + L::k_off(32 * n + l32, 2 * (k0b + u) + hh)));
+#pragma unroll
+        for (int u = 0; u < KB; ++u)
+#pragma unroll
+          for (int n = 0; n < 2; ++n) acc[n] = mfma32x32x16(ka[u][n], qf[0][k0b + u], acc[n]);
+      }
+    };
+    // masks (causal diagonal, key tail) and the row maximum, log2 units
+    auto mask_max = [&](int k0, f32x16 (&acc)[2]) -> float {
+      if ((CAUSAL && (k0 + L::KT - 1 > qa0)) || (KTAIL && k0 + L::KT > a.Mk)) {
+        const int qi = qa0 + l32;
+        const int kmax = !KTAIL ? qi : (CAUSAL ? min(qi, a.Mk - 1) : a.Mk - 1);  // last visible key
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * n + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (key > kmax) acc[n][r] = -INFINITY;
+          }
+      }
+      float m0 = fmaxf(acc[0][0], acc[1][0]), m1 = fmaxf(acc[0][1], acc[1][1]);
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) {
+        m0 = fmaxf(m0, fmaxf(acc[0][r], acc[1][r]));
+        m1 = fmaxf(m1, fmaxf(acc[0][r + 1], acc[1][r + 1]));
+      }
+      return halves_max(fmaxf(m0, m1)) * a.scale_log2;
+    };
+    bf16x8 pb[4];
+    // P = 2^(s*c - m) rounded to bf16, row sums in fp32
+    auto exp_tile = [&](f32x16 (&acc)[2], float m_use) {
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = fast_exp2(fmaf(acc[n][r], a.scale_log2, -m_use));
+          ls[r & 3] += pr;
+          pb[2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
+        }
+      l_run[0] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    // O^T[d][q] += V^T[d][key] P^T[key][q] over 16-key chunks tc
+    auto pv = [&](int slot) {
+      const unsigned char* Vb = slot_v(slot);
+      const int G16 = lane >> 4, s16 = lane & 15;
+#pragma unroll
+      for (int tc = 0; tc < 4; ++tc) {
+#pragma unroll
+        for (int d = 0; d < DN; ++d) {
+          const int vrow = 16 * tc + 4 * (G16 >> 1) + (s16 >> 2);
+          const int vbyte = 2 * (32 * d + 16 * (G16 & 1) + 4 * (s16 & 3));
+          const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow, vbyte)));
+          const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow + 8, vbyte)));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[0][d] = mfma32x32x16(vf, pb[tc], o[0][d]);
+        }
+      }
+    };
+    // lazy exact rescaling (as in the register-staged loop): the reference
+    // m_run is raised only when a tile's maximum exceeds it by more than 8
+    auto rescale_if_needed = [&](float m_tile) {
+      if (__builtin_amdgcn_ballot_w64(m_tile > m_run[0] + 8.f) != 0) {
+        const float m_new = fmaxf(m_run[0], m_tile);
+        const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[0] - m_new);
+        m_run[0] = m_new;
+        l_run[0] *= alpha;
+#pragma unroll
+        for (int d = 0; d < DN; ++d)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[0][d][r] *= alpha;
+      }
+    };
+
+    // masks (causal diagonal, key tail) needed on sub-tile t with first key k0
+    auto needs_mask = [&](int k0) -> bool {
+      return (CAUSAL && (k0 + L::KT - 1 > qa0)) || (KTAIL && k0 + L::KT > a.Mk);
+    };
+    // the row maximum of an unmasked sub-tile (log2 units)
+    auto row_max = [&](f32x16 (&acc)[2]) -> float {
+      float m0 = fmaxf(acc[0][0], acc[1][0]), m1 = fmaxf(acc[0][1], acc[1][1]);
+#pragma unroll
+      for (int r = 2; r < 16; r += 2) {
+        m0 = fmaxf(m0, fmaxf(acc[0][r], acc[1][r]));
+        m1 = fmaxf(m1, fmaxf(acc[0][r + 1], acc[1][r + 1]));
+      }
+      return halves_max(fmaxf(m0, m1)) * a.scale_log2;
+    };
+
+    // One pipelined sub-tile step for a wave that computes both tiles:
+    //  phase A, NSA = 2 KK groups: a K fragment read (4 ahead), one S(t+1)
+    //    MFMA, 32 / NSA exponentials of tile t (scaled logit, 2^x, row sum,
+    //    bf16 pairs);
+    //  phase B, NPV = 4 DN groups: two V^T fragment reads (4 MFMAs ahead), one
+    //    PV(t) MFMA, and (from the second quarter on) a share of the running
+    //    maximum of tile t+1.
+    // Fences keep the groups in this order; within a group the compiler
+    // schedules freely.
+    constexpr int NSA = 2 * KK;
+    constexpr int VPG = 32 / NSA;
+    constexpr int NPV = 4 * DN;
+    constexpr int MX0 = NPV / 4;  // first group that takes part of the maximum
+    static_assert(NSA >= 4 && NPV >= 4 && 32 % NSA == 0, "pipeline shape");
+    constexpr int DSTEP = NSA / NPIECE;  // S MFMAs per DMA piece
+    static_assert(DSTEP >= 1 && DSTEP * NPIECE == NSA, "the DMA pieces are issued within the S MFMAs");
+    float mx_run[2];
+    auto full_step = [&](int kslot, int vslot, f32x16 (&cur)[2], f32x16 (&acc)[2], float m_use, int dk0,
+                         int dslot) {
+      const unsigned char* Kb = slot_k(kslot);
+      const unsigned char* Vb = slot_v(vslot);
+      auto read_k = [&](int g) {  // S MFMA g = 2 kk + n
+        return __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const u32x4*>(Kb + L::k_off(32 * (g & 1) + l32, 2 * (g >> 1) + hh)));
+      };
+      const int G16 = lane >> 4, s16 = lane & 15;
+      auto read_v = [&](int g) {  // PV MFMA g = DN tc + d
+        const int tc = g / DN, d = g % DN;
+        const int vrow = 16 * tc + 4 * (G16 >> 1) + (s16 >> 2);
+        const int vbyte = 2 * (32 * d + 16 * (G16 & 1) + 4 * (s16 & 3));
+        const i16x4 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow, vbyte)));
+        const i16x4 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(Vb + L::v_off(vrow + 8, vbyte)));
+        return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      };
+      acc[0] = acc[1] = f32x16{};
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};
+      bf16x8 kf[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) kf[g] = read_k(g);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < NSA; ++g) {
+        const bf16x8 f = kf[g & 3];
+        if (g + 4 < NSA) kf[g & 3] = read_k(g + 4);
+        acc[g & 1] = mfma32x32x16(f, qf[0][g >> 1], acc[g & 1]);
+        if (XATTN_DMA_SPREAD && g % DSTEP == (DSTEP > 1 ? 1 : 0)) dma_piece(dk0, dslot, g / DSTEP);
+#pragma unroll
+        for (int u = 0; u < VPG; ++u) {
+          const int v = VPG * g + u, n = v >> 4, r = v & 15;
+          const float pr = fast_exp2(fmaf(cur[n][r], a.scale_log2, -m_use));
+          ls[r & 3] += pr;
+          pb[2 * n + (r >> 3)][r & 7] = static_cast<__bf16>(pr);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_run[0] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      bf16x8 vf[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) vf[g] = read_v(g);
+      mx_run[0] = mx_run[1] = -INFINITY;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < NPV; ++g) {
+        const bf16x8 f = vf[g & 3];
+        if (g + 4 < NPV) vf[g & 3] = read_v(g + 4);
+        o[0][g % DN] = mfma32x32x16(f, pb[g / DN], o[0][g % DN]);
+        if (g >= MX0) {
+          // values [32 (g - MX0), 32 (g + 1 - MX0)) / (NPV - MX0) of tile t+1's S^T
+          const int v0 = (32 * (g - MX0)) / (NPV - MX0), v1 = (32 * (g + 1 - MX0)) / (NPV - MX0);
+#pragma unroll
+          for (int v = v0; v < v1; ++v) mx_run[v & 1] = fmaxf(mx_run[v & 1], acc[v >> 4][v & 15]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // Prologue: tiles 0 and 1 in flight. Iteration t = -1 then computes only
+    // S(0) (and refills with tile 2), so every iteration has one shape.
+    // Every iteration issues one sub-tile's DMA (past the end: the last
+    // sub-tile again, never read), so the count of loads in flight is the same
+    // at every wait; the loop drains them before the item ends.
+    __syncthreads();  // block list visible
+    const int t_last = n_sub - 1;
+    uint32_t e1 = entry(0), e2 = entry(1);  // entries of tiles t+1, t+2 (clamped to the last)
     if (n_sub > 0) {
-      load_tile(key_start(e0, 0), r0);
-      store_tile(0, r0);
+      dma_tile(key_start(e1, 0), 0);
+      dma_tile(key_start(e2, min(1, t_last)), 1);
     }
-    __syncthreads();
-    for (int t = 0; t < n_sub; ++t) {
-      const bool more = t + 1 < n_sub;
-      const uint32_t e2 = entry(t + 2);
-      if (more) load_tile(key_start(e1, t + 1), r0);
-      compute(key_start(e0, t), mine_tile(e0), t & 1);
-      if (more) store_tile((t + 1) & 1, r0);
-      __syncthreads();
-      e0 = e1;
-      e1 = e2;
-    }
-  } else {
-    // two sub-tiles in flight: tile t+2 is fetched while tile t is computed and
-    // tile t+1 (fetched one iteration earlier) waits in registers
-    Stage ra, rb;
-    uint32_t e0 = entry(0), e1 = entry(1), e2 = entry(2);  // entries of tiles t .. t+2
-    if (n_sub > 0) load_tile(key_start(e0, 0), ra);
-    if (n_sub > 1) load_tile(key_start(e1, 1), rb);
-    if (n_sub > 0) store_tile(0, ra);
-    __syncthreads();
-    auto iter = [&](int t, Stage& ld, const Stage& st) {
+    f32x16 sa[2], sb[2];
+    bool act = false;        // tile t computed by this wave
+    float mt = -INFINITY;    // its maximum
+    // iteration t: tile t's S^T in cur, tile t+1's into nxt
+    auto iter = [&](int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+      vm_wait<DPT>();                       // tile t+1 landed (t+2 may be in flight)
+      __syncthreads();                      // ... for every wave; all are past iteration t-1
       const uint32_t e3 = entry(t + 3);
-      if (t + 2 < n_sub) load_tile(key_start(e2, t + 2), ld);
-      compute(key_start(e0, t), mine_tile(e0), t & 1);
-      if (t + 1 < n_sub) store_tile((t + 1) & 1, st);
-      __syncthreads();
-      e0 = e1;
+      const int k3 = key_start(e3, min(t + 3, t_last));
+      const int slot3 = (t + 3) & 3;
+      const int k1 = key_start(e1, t + 1);
+      const bool act1 = t + 1 < n_sub && active(e1, t + 1);
+      float mt1 = -INFINITY;
+      if (act) rescale_if_needed(mt);
+      const float m_use = (m_run[0] == -INFINITY) ? 0.f : m_run[0];
+      if (act && act1 && !needs_mask(k1)) {
+        // the common case, written in issue order with scheduling fences:
+        // S(t+1) with the exponentials of t, then PV(t) with the maximum of
+        // t+1; K/V fragments are read four MFMAs ahead
+        if (!XATTN_DMA_SPREAD) dma_tile(k3, slot3);
+        full_step((t + 1) & 3, t & 3, cur, nxt, m_use, k3, slot3);
+        mt1 = halves_max(fmaxf(mx_run[0], mx_run[1])) * a.scale_log2;
+      } else {
+        dma_tile(k3, slot3);
+        if (act1) s_mma((t + 1) & 3, nxt);
+        if (act) {
+          exp_tile(cur, m_use);
+          pv(t & 3);
+        }
+        if (act1) mt1 = mask_max(k1, nxt);
+      }
+      act = act1;
+      mt = mt1;
       e1 = e2;
       e2 = e3;
     };
-    for (int t = 0; t < n_sub; t += 2) {
-      iter(t, ra, rb);
-      if (t + 1 < n_sub) iter(t + 1, rb, ra);
+    if (n_sub > 0) {
+      for (int t = -1; t < n_sub; t += 2) {
+        iter(t, sb, sa);
+        if (t + 1 < n_sub) iter(t + 1, sa, sb);
+      }
+      vm_wait<0>();  // the trailing loads, so no DMA reaches the ring after the item
+    }
+  } else {
+    __syncthreads();  // block list visible
+    if constexpr (DEPTH == 1) {
+      Stage r0;
+      uint32_t e0 = entry(0), e1 = entry(1);  // entries of tiles t, t+1
+      if (n_sub > 0) {
+        load_tile(key_start(e0, 0), r0);
+        store_tile(0, r0);
+      }
+      __syncthreads();
+      for (int t = 0; t < n_sub; ++t) {
+        const bool more = t + 1 < n_sub;
+        const uint32_t e2 = entry(t + 2);
+        if (more) load_tile(key_start(e1, t + 1), r0);
+        compute(key_start(e0, t), mine_tile(e0), t & 1);
+        if (more) store_tile((t + 1) & 1, r0);
+        __syncthreads();
+        e0 = e1;
+        e1 = e2;
+      }
+    } else {
+      // two sub-tiles in flight: tile t+2 is fetched while tile t is computed and
+      // tile t+1 (fetched one iteration earlier) waits in registers
+      Stage ra, rb;
+      uint32_t e0 = entry(0), e1 = entry(1), e2 = entry(2);  // entries of tiles t .. t+2
+      if (n_sub > 0) load_tile(key_start(e0, 0), ra);
+      if (n_sub > 1) load_tile(key_start(e1, 1), rb);
+      if (n_sub > 0) store_tile(0, ra);
+      __syncthreads();
+      auto iter = [&](int t, Stage& ld, const Stage& st) {
+        const uint32_t e3 = entry(t + 3);
+        if (t + 2 < n_sub) load_tile(key_start(e2, t + 2), ld);
+        compute(key_start(e0, t), mine_tile(e0), t & 1);
+        if (t + 1 < n_sub) store_tile((t + 1) & 1, st);
+        __syncthreads();
+        e0 = e1;
+        e1 = e2;
+        e2 = e3;
+      };
+      for (int t = 0; t < n_sub; t += 2) {
+        iter(t, ra, rb);
+        if (t + 1 < n_sub) iter(t + 1, rb, ra);
+      }
     }
   }
 
@@ -543,7 +911,10 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
                  ((uint32_t)f32_to_bf16(o[y][d][4 * g4 + 1] * inv) << 16);
           w[1] = (uint32_t)f32_to_bf16(o[y][d][4 * g4 + 2] * inv) |
                  ((uint32_t)f32_to_bf16(o[y][d][4 * g4 + 3] * inv) << 16);
-          *reinterpret_cast<u32x2*>(orow + dc) = w;
+          if (XATTN_NT_QO)
+            __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(orow + dc));
+          else
+            *reinterpret_cast<u32x2*>(orow + dc) = w;
         }
       if (a.lse && hh == 0) a.lse[bh * a.Mq + qi] = (m_run[y] + log2f(l_tot)) * kLn2;
     }
@@ -584,7 +955,8 @@ void attn_fwd_bf16_kernel(AttnArgs a) {
   using L = AttnLds<C>;
   constexpr int SLOTS = AttnMode<MODE>::SLOTS;
   constexpr int NT = 64 * (BLK / RPW) * SLOTS;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[L::bytes(SLOTS)];
+  constexpr bool PIPE = XATTN_ATTN_PIPE != 0 && SLOTS == 2 && RPW == 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[PIPE ? L::bytes_pipe(SLOTS) : L::bytes(SLOTS)];
   __shared__ int scan_s[SLOTS > 1 ? NT / 64 : 1];
   const AttnItems its(a, MODE);
   if constexpr (!SPARSE) {

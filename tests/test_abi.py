@@ -272,3 +272,22 @@ def test_noalloc_rejects_oversized_problems_on_the_host(xa):
     assert b"scratch" in L.xattn_last_error()
     assert L.xattn_prefill_noalloc(ctypes.byref(_p(xa, C=96)), FAKE, FAKE, FAKE, arr, 0.01, 0.1, FAKE, None,
                                    FAKE, FAKE, FAKE, None, None) == 5
+
+
+def test_peaks_library_exports_its_header():
+    # the peak-rate microbenchmarks live in a library of their own
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_xattn_amd", "libxattn_peaks.so"))
+    text = open(os.path.join(ROOT, "include", "xattn_peaks.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)
+    names = sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)))
+    assert names == ["xattn_peak_copy", "xattn_peak_mfma", "xattn_peak_mfma_waves_per_block"]
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.xattn_peak_mfma_waves_per_block() == 8
+    # bad arguments are refused on the host (hipErrorInvalidValue), nothing launched
+    lib.xattn_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    assert lib.xattn_peak_copy(None, None, 16, None) != 0
+    assert lib.xattn_peak_copy(FAKE, FAKE, 15, None) != 0
+    lib.xattn_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.xattn_peak_mfma(0, 10, FAKE, None, None) != 0
