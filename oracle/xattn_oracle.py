@@ -42,6 +42,10 @@ Readings taken where the pages are silent:
     the threshold cut;
   * sparse attention is exact softmax attention renormalised over the
     selected keys only;
+  * DuSA1 multi-stride scoring (pattern "dusa1"): each of the S phases of the
+    (S, M // S, C) reshape is softmaxed on its own and a block's score is the
+    phases' summed mass over its S * r rows, divided by S * r; it needs
+    lengths that are multiples of S;
   * ragged lengths ([DuSA] rebuttal, "Response to Q1": padding makes the
     sequence length divisible by the block size): the missing tokens of a
     partial stride group are zero vectors; strided key rows and keys past the
@@ -60,6 +64,8 @@ __all__ = [
     "reversed_key_rows",
     "strided_logits",
     "block_score_row",
+    "dusa1_phase_rows",
+    "dusa1_block_score_row",
     "block_scores",
     "minimal_set",
     "select_row",
@@ -165,9 +171,63 @@ def strided_logits(qh, kh, stride: int, score_scale: float, causal: bool,
 # keys for each strided query row.
 # ---------------------------------------------------------------------------
 
+def dusa1_phase_rows(x: np.ndarray, stride: int) -> np.ndarray:
+    """(S, M // S, C): x (M, C) reshaped to (M // S, S, C), then its first two
+    axes swapped, so phase s holds rows s, s + S, s + 2S, ... ([DuSA] Response
+    to Q2, DuSA1)."""
+    x = _f64(x)
+    m, c = x.shape
+    if m % stride:
+        raise ValueError("DuSA1 scoring needs a length that is a multiple of the stride")
+    return x.reshape(m // stride, stride, c).transpose(1, 0, 2)
+
+
+def dusa1_block_score_row(qh, kh, big_i: int, block: int, stride: int,
+                          score_scale: float, causal: bool) -> np.ndarray:
+    """DuSA1 multi-stride block scores for query block ``big_i`` (length NBk).
+
+    [DuSA] Response to Q2: Q and K are reshaped to (M // S, S, C) and
+    transposed to (S, M // S, C); an attention with its softmax on the final
+    two dimensions is computed for each of the S phases (they may be folded
+    into the head axis without changing the result). Reading taken: every
+    phase row is softmaxed over its own phase's strided keys (j <= i at the
+    strided level when causal), and block (I, J) scores the probability mass of
+    its S * r_I phase rows falling in key block J, summed over the phases and
+    divided by S * r_I, so each row of block scores sums to 1.
+    """
+    if block % stride:
+        raise ValueError("block must be a multiple of the stride")
+    mq, mk = qh.shape[0], kh.shape[0]
+    if (mk - mq) % block:
+        raise ValueError("Mk - Mq must be a multiple of the block size")
+    qp = dusa1_phase_rows(qh, stride)        # (S, Rq, C)
+    kp = dusa1_phase_rows(kh, stride)        # (S, Rk, C)
+    r = block // stride
+    rq, rk = qp.shape[1], kp.shape[1]
+    nbk = _cdiv(mk, block)
+    off = (mk - mq) // stride                # strided position of query row 0
+    rows = range(big_i * r, min((big_i + 1) * r, rq))
+    total = np.zeros(nbk)
+    for s in range(stride):
+        logits = score_scale * (qp[s, rows.start:rows.stop] @ kp[s].T)   # (r_I, Rk)
+        if causal:
+            i = np.arange(rows.start, rows.stop)[:, None] + off
+            j = np.arange(rk)[None, :]
+            logits[j > i] = -np.inf
+        mx = logits.max(axis=1, keepdims=True)
+        p = np.exp(logits - mx)
+        p /= p.sum(axis=1, keepdims=True)                                 # softmax over the phase's keys
+        p = np.concatenate([p, np.zeros((p.shape[0], nbk * r - rk))], axis=1)
+        total += p.reshape(p.shape[0], nbk, r).sum(axis=2).sum(axis=0)
+    return total / (stride * len(rows))
+
+
 def block_score_row(qh, kh, big_i: int, block: int, stride: int,
                     score_scale: float, causal: bool, pattern: str = "antidiagonal") -> np.ndarray:
-    """Block scores S^[I, :] (length NBk) for query block ``big_i`` of one head."""
+    """Block scores S^[I, :] (length NBk) for query block ``big_i`` of one head.
+    ``pattern`` is "antidiagonal" (the method), "diagonal" or "dusa1"."""
+    if pattern == "dusa1":
+        return dusa1_block_score_row(qh, kh, big_i, block, stride, score_scale, causal)
     if block % stride:
         raise ValueError("block must be a multiple of the stride")
     mq, mk = qh.shape[0], kh.shape[0]

@@ -580,3 +580,71 @@ def test_global_selection_chunk_exhaustive():
             want[cands[t]] = True
         want[np.arange(nbq), np.arange(nbq) + qoff] = True
         np.testing.assert_array_equal(got, want)
+
+
+# ------------------------------------------------------- DuSA1 multi-stride scoring
+
+@pytest.mark.parametrize("stride,r", [(2, 2), (2, 4), (4, 2), (4, 4)])
+@pytest.mark.parametrize("causal", [True, False])
+def test_dusa1_block_scores_bruteforce(stride, r, causal):
+    # From the token-level logits with loops: phase s keeps tokens s, s+S, ...;
+    # each phase row is softmaxed over the phase's keys (j <= i when causal),
+    # and the probabilities of the S * r phase rows of a query block are summed
+    # per key block and divided by S * r.
+    rng = _rng(300 + 10 * stride + r)
+    block = stride * r
+    nb, c = 3, 4
+    m = nb * block
+    q = rng.standard_normal((m, c))
+    k = rng.standard_normal((m, c))
+    scale = 0.45
+    big_r = m // stride
+    expect = np.zeros((nb, nb))
+    for s in range(stride):
+        for i in range(big_r):
+            keys = range(i + 1) if causal else range(big_r)
+            vals = [scale * float(q[i * stride + s] @ k[j * stride + s]) for j in keys]
+            top = max(vals)
+            z = sum(math.exp(v - top) for v in vals)
+            for j, v in zip(keys, vals):
+                expect[i // r, j // r] += math.exp(v - top) / z / (stride * r)
+    got = oracle.block_scores(q[None, None], k[None, None], block, stride, scale, causal, pattern="dusa1")[0, 0]
+    np.testing.assert_allclose(got, expect, rtol=1e-12, atol=1e-15)
+    # not the diagonal XAttention pattern, which sums the phases' logits before
+    # one softmax per strided row
+    diag = oracle.block_scores(q[None, None], k[None, None], block, stride, scale, causal, pattern="diagonal")[0, 0]
+    assert np.abs(got - diag).max() > 1e-3
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_dusa1_stride_one_is_the_block_attention_mass(causal):
+    # one phase: the textbook per-block attention mass averaged over the block's rows
+    rng = _rng(17)
+    m, c, block = 48, 5, 8
+    q = rng.standard_normal((m, c))
+    k = rng.standard_normal((m, c))
+    logits = 0.6 * (q @ k.T)
+    if causal:
+        logits = np.where(np.tril(np.ones((m, m), dtype=bool)), logits, -np.inf)
+    p = scipy.special.softmax(logits, axis=1)
+    nb = m // block
+    expect = p.reshape(nb, block, nb, block).sum(axis=(1, 3)) / block
+    got = oracle.block_scores(q[None, None], k[None, None], block, 1, 0.6, causal, pattern="dusa1")[0, 0]
+    np.testing.assert_allclose(got, expect, rtol=1e-12, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_dusa1_invariants_and_chunk(causal):
+    rng = _rng(23)
+    q = rng.standard_normal((1, 2, 256, 8))
+    k = rng.standard_normal((1, 1, 256, 8))
+    sc = oracle.block_scores(q, k, 32, 4, 0.5, causal, pattern="dusa1")
+    assert (sc >= 0).all()
+    np.testing.assert_allclose(sc.sum(-1), 1.0, rtol=1e-12)
+    if causal:
+        assert (sc[..., np.triu(np.ones((8, 8), dtype=bool), 1)] == 0).all()
+    # the last 96 queries against all 256 keys score like the last 3 rows of the full run
+    part = oracle.block_scores(q[:, :, 160:], k, 32, 4, 0.5, causal, pattern="dusa1")
+    np.testing.assert_allclose(part, sc[:, :, 5:], rtol=1e-12, atol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.block_scores(q[:, :, :250], k[:, :, :250], 32, 4, 0.5, causal, pattern="dusa1")
