@@ -360,8 +360,8 @@ def cpu_baseline(wl, torch, res, budget_s):
 
 def run_variants(xa, torch, head, steps):
     """The headline layer through xattn_prefill with each method variant:
-    global and GQA-union selection, the diagonal scoring pattern, a chunked
-    prefill step and a ragged length."""
+    global and GQA-union selection, the diagonal and DuSA1 scoring patterns, a
+    chunked prefill step and a ragged length."""
     w = head["workload"]
     q, k, v, tau = head["_tensors"][:4]
     sscale, smscale = 1.0 / (w.stride * math.sqrt(w.C)), 1.0 / math.sqrt(w.C)
@@ -369,11 +369,14 @@ def run_variants(xa, torch, head, steps):
     res = {}
     for label, kw in (("select_global", dict(selection="global")),
                       ("select_gqa_union", dict(selection="gqa_union")),
-                      ("pattern_diagonal", dict(pattern=xa.DIAGONAL))):
+                      ("pattern_diagonal", dict(pattern=xa.DIAGONAL)),
+                      ("pattern_dusa1", dict(pattern=xa.DUSA1))):
         bufs = xa.PrefillBuffers(q, k, w.block, w.stride, w.causal, want_mask=False, **kw)
+        # a DuSA1 phase logit is one dot product: the attention scale
+        ss = smscale if kw.get("pattern") == xa.DUSA1 else sscale
 
         def step():
-            xa.xattn_prefill(q, k, v, tau, w.block, w.stride, sscale, smscale, w.causal, buffers=bufs, **kw)
+            xa.xattn_prefill(q, k, v, tau, w.block, w.stride, ss, smscale, w.causal, buffers=bufs, **kw)
 
         step()
         torch.cuda.synchronize()

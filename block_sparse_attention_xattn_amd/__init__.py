@@ -42,6 +42,7 @@ EXPORTS = (
 
 ANTIDIAGONAL = 0
 DIAGONAL = 1
+DUSA1 = 2
 
 SELECT_ROW = 0
 SELECT_GLOBAL = 1

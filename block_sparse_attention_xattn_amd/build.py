@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libxattn.so")
 PEAKS_LIB = os.path.join(HERE, "libxattn_peaks.so")
 PEAKS_SOURCES = ["peaks.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["api.hip", "score.hip", "select.hip", "attn.hip"]
+SOURCES = ["api.hip", "score.hip", "select.hip", "attn.hip", "dusa1.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms stay disabled on this target

@@ -34,8 +34,8 @@ xattn_status check_problem(const xattn_problem* p, bool need_stride = true) {
       (need_stride && p->stride < 1))
     return fail(XATTN_ERR_SHAPE, "B, Hq, Hkv, M, C, block and stride must be positive");
   if (p->causal != 0 && p->causal != 1) return fail(XATTN_ERR_ARG, "causal must be 0 or 1");
-  if (p->pattern != XATTN_ANTIDIAGONAL && p->pattern != XATTN_DIAGONAL)
-    return fail(XATTN_ERR_ARG, "pattern %d is neither antidiagonal nor diagonal", p->pattern);
+  if (p->pattern != XATTN_ANTIDIAGONAL && p->pattern != XATTN_DIAGONAL && p->pattern != XATTN_DUSA1)
+    return fail(XATTN_ERR_ARG, "pattern %d is not an xattn_pattern", p->pattern);
   if (p->selection != XATTN_SELECT_ROW && p->selection != XATTN_SELECT_GLOBAL &&
       p->selection != XATTN_SELECT_GQA_UNION)
     return fail(XATTN_ERR_ARG, "selection %d is not an xattn_selection", p->selection);
@@ -55,6 +55,12 @@ xattn_status check_problem(const xattn_problem* p, bool need_stride = true) {
   const int nbk = (mk + p->block - 1) / p->block;
   if (nbk > XATTN_MAX_BLOCKS)
     return fail(XATTN_ERR_UNSUPPORTED, "%d key blocks exceed %d", nbk, XATTN_MAX_BLOCKS);
+  if (need_stride && p->pattern == XATTN_DUSA1) {
+    if (p->dtype != XATTN_BF16) return fail(XATTN_ERR_UNSUPPORTED, "DuSA1 scoring runs on bf16 inputs only");
+    if (p->M % p->stride || mk % p->stride)
+      return fail(XATTN_ERR_SHAPE, "DuSA1 scoring needs M=%d and Mk=%d to be multiples of the stride %d", p->M, mk,
+                  p->stride);
+  }
   if (p->dtype == XATTN_F32 && mk > XATTN_F32_MAX_TOKENS)
     return fail(XATTN_ERR_UNSUPPORTED, "float32 problems take at most %d key tokens (Mk=%d); use bf16",
                 XATTN_F32_MAX_TOKENS, mk);
@@ -105,9 +111,19 @@ xattn_status do_partials(const xattn_problem* p, const void* q, const void* k, f
   return hip_status(e, "score partials launch");
 }
 
+// DuSA1: log-sum-exps into the workspace, block scores written directly
+xattn_status do_score_dusa1(const xattn_problem* p, const void* q, const void* k, float score_scale,
+                            float* block_scores, void* ws, hipStream_t st) {
+  return hip_status(xattn::launch_score_dusa1(shape_of(p), static_cast<const uint16_t*>(q),
+                                              static_cast<const uint16_t*>(k), score_scale, static_cast<float*>(ws),
+                                              block_scores, st),
+                    "DuSA1 score launch");
+}
+
 // Partials, then the normalised block scores (the separate scoring stage).
 xattn_status do_score(const xattn_problem* p, const void* q, const void* k, float score_scale,
                       float* block_scores, void* ws, hipStream_t st) {
+  if (p->pattern == XATTN_DUSA1) return do_score_dusa1(p, q, k, score_scale, block_scores, ws, st);
   const xattn_status r = do_partials(p, q, k, score_scale, ws, st);
   if (r != XATTN_OK) return r;
   return hip_status(xattn::launch_score_finalize(shape_of(p), static_cast<const float*>(ws), block_scores, st),
@@ -218,6 +234,8 @@ const char* xattn_last_error(void) { return g_err; }
 size_t xattn_score_workspace_bytes(const xattn_problem* p) {
   if (check_problem(p) != XATTN_OK) return 0;
   const xattn::Shape s = shape_of(p);
+  if (p->pattern == XATTN_DUSA1)  // per (phase, strided row) log-sum-exps, then room for block scores
+    return align256(xattn::dusa1_lse_bytes(s)) + (size_t)p->B * p->Hq * (size_t)s.NBq() * s.NBk() * sizeof(float);
   return (size_t)p->B * p->Hq * (size_t)s.NBq() * s.NBk() * s.r() * sizeof(float);
 }
 
@@ -306,6 +324,15 @@ xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
   const PrefillLayout lay = prefill_layout(p);
   char* wsb = static_cast<char*>(ws);
   const xattn::Shape sh = shape_of(p);
+  if (p->pattern == XATTN_DUSA1) {
+    // block scores first (into the workspace when the caller does not want them),
+    // then the selection on them
+    float* sc = block_scores ? block_scores
+                             : reinterpret_cast<float*>(wsb + align256(xattn::dusa1_lse_bytes(sh)));
+    if ((s = do_score_dusa1(p, q, k, score_scale, sc, ws, st)) != XATTN_OK) return s;
+    if ((s = do_select(p, sc, t, mask, kv_idx, kv_cnt, wsb + lay.select_off, st)) != XATTN_OK) return s;
+    return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, wsb + lay.queue_off, st);
+  }
   if ((s = do_partials(p, q, k, score_scale, ws, st)) != XATTN_OK) return s;
   if (p->selection == XATTN_SELECT_GLOBAL) {
     // the head's whole block matrix is needed first

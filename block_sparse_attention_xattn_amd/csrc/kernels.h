@@ -14,7 +14,7 @@ namespace xattn {
 // the last stride group and the last block may be partial.
 struct Shape {
   int B, Hq, Hkv, M, C, block, stride, causal;
-  int diagonal;  // 1: scoring pairs q[iS+s] with k[jS+s] instead of k[jS+S-1-s]
+  int diagonal;  // scoring pattern: 0 antidiagonal, 1 diagonal (q[iS+s] with k[jS+s]), 2 DuSA1
   int selection; // SEL_ROW, SEL_GLOBAL or SEL_GQA_UNION
   int Mk;        // key length
   int NBq() const { return (M + block - 1) / block; }
@@ -33,6 +33,13 @@ hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const u
                                       float score_scale, float* ws, hipStream_t st);
 hipError_t launch_score_partials_f32(const Shape& s, const float* q, const float* k,
                                      float score_scale, float* ws, hipStream_t st);
+// DuSA1 multi-stride scoring (pattern 2, bf16, lengths multiples of the
+// stride): per (phase, strided row) log2-sum-exps into lse_ws (B*Hq*M floats,
+// dusa1_lse_bytes), then the block scores written directly.
+size_t dusa1_lse_bytes(const Shape& s);
+hipError_t launch_score_dusa1(const Shape& s, const uint16_t* q, const uint16_t* k, float score_scale,
+                              float* lse_ws, float* block_scores, hipStream_t st);
+
 // Stage 2: block scores from the partials (row-normalised, divided by r).
 hipError_t launch_score_finalize(const Shape& s, const float* ws, float* block_scores,
                                  hipStream_t st);

@@ -113,11 +113,19 @@ typedef struct {
   int32_t Mk;     /* key length; 0 means M. Mk - M is a multiple of block */
 } xattn_problem;
 
-/* Which line of each stride x stride tile the scoring sums:
- *  ANTIDIAGONAL (the method, [XA-abs]): query row i*S+s with key row j*S+S-1-s;
+/* How the strided scoring forms its logits:
+ *  ANTIDIAGONAL (the method, [XA-abs]): query row i*S+s with key row j*S+S-1-s,
+ *  summed over s, one softmax per strided row;
  *  DIAGONAL (the older variant compared in [DuSA] Response to Q2 and in the
- *  [XA-sum] ablation table): query row i*S+s with key row j*S+s. */
-typedef enum { XATTN_ANTIDIAGONAL = 0, XATTN_DIAGONAL = 1 } xattn_pattern;
+ *  [XA-sum] ablation table): query row i*S+s with key row j*S+s, summed over s;
+ *  DUSA1 ([DuSA] Response to Q2, DuSA1: Q and K reshaped to (S, M/S, C)
+ *  phases, a softmax per phase): each phase row q[i*S+s] is softmaxed over its
+ *  phase's keys k[j*S+s] on its own (logit score_scale * q.k, j <= i + off/S
+ *  when causal), and block (I, J) scores the phases' summed mass over its
+ *  S * r_I rows divided by S * r_I. DUSA1 takes bf16 inputs whose lengths M and
+ *  Mk are multiples of S (else XATTN_ERR_UNSUPPORTED / XATTN_ERR_SHAPE); its
+ *  natural score_scale is the attention scale 1/sqrt(C). */
+typedef enum { XATTN_ANTIDIAGONAL = 0, XATTN_DIAGONAL = 1, XATTN_DUSA1 = 2 } xattn_pattern;
 
 /* How xattn_select (and xattn_prefill) choose blocks:
  *  ROW (the method, [XA-sum] Approach): a minimal set per query-block row;
@@ -149,7 +157,9 @@ size_t xattn_workspace_bytes(const xattn_problem* p);
 
 /* Device workspace bytes xattn_score needs for problem p;
  * 0 if p is invalid. The workspace holds per-(strided row, key block) partial
- * log-sum-exp values: B*Hq*NBq*NBk*r float32. */
+ * log-sum-exp values: B*Hq*NBq*NBk*r float32 (DUSA1: per (phase, strided row)
+ * log-sum-exps, B*Hq*M float32 rounded up to 256 bytes, then room for
+ * B*Hq*NBq*NBk float32 block scores). */
 size_t xattn_score_workspace_bytes(const xattn_problem* p);
 
 /*

@@ -58,7 +58,9 @@ FAKE = 0x1000  # never dereferenced: validation fails first
     (dict(Hkv=3), 2), (dict(Mk=1000), 2), (dict(Mk=1100), 2), (dict(stride=3), 2), (dict(C=96), 5),
     (dict(block=32, stride=4), 5), (dict(stride=128), 5), (dict(stride=1), 5),
     (dict(dtype=7), 3), (dict(causal=2), 4), (dict(Hq=512, Hkv=1), 5), (dict(B=0), 2),
-    (dict(M=4096 * 128 * 2), 5), (dict(pattern=2), 4), (dict(pattern=-1), 4),
+    (dict(M=4096 * 128 * 2), 5), (dict(pattern=3), 4), (dict(pattern=-1), 4),
+    # DuSA1 scoring: bf16 only, lengths multiples of the stride
+    (dict(pattern=2, dtype=1), 5), (dict(pattern=2, M=1004), 2), (dict(pattern=2, M=1024, Mk=1540), 2),
     (dict(selection=3), 4), (dict(selection=-1), 4), (dict(Mk=4096 * 128 + 128), 5),
     # empty problems are errors, not silent no-ops
     (dict(M=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(C=0), 2), (dict(block=0), 2),
@@ -291,3 +293,12 @@ def test_peaks_library_exports_its_header():
     assert lib.xattn_peak_copy(FAKE, FAKE, 15, None) != 0
     lib.xattn_peak_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     assert lib.xattn_peak_mfma(0, 10, FAKE, None, None) != 0
+
+
+def test_dusa1_workspace(xa):
+    # per (phase, strided row) log-sum-exps (B*Hq*M floats, 256-byte aligned),
+    # then room for the block scores; the attention workspace follows in prefill
+    p = _p(xa, pattern=2)
+    lse = 1 * 4 * 1024 * 4
+    assert xa.workspace_bytes(p) == (lse + 255) // 256 * 256 + 1 * 4 * 8 * 8 * 4
+    assert xa.total_workspace_bytes(p) == (xa.workspace_bytes(p) + 255) // 256 * 256 + 1024
