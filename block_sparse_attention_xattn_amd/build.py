@@ -28,9 +28,15 @@ FLAGS = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# the debug build: the same sources with the kernels' bounds checks counted
+# (-DXATTN_DEBUG=1, include/xattn_debug.h), a library of its own
+DEBUG_LIB = os.path.join(HERE, "libxattn_debug.so")
+DEBUG_BUILD = os.path.join(BUILD, "debug")
+
+
+def _compile(src: str, verbose: bool, debug: bool = False) -> str:
+    obj = os.path.join(DEBUG_BUILD if debug else BUILD, src.replace(".hip", ".o"))
+    cmd = [HIPCC, *FLAGS, *(["-DXATTN_DEBUG=1"] if debug else []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         cmd += ["-Rpass-analysis=kernel-resource-usage"]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,14 +59,44 @@ def _link(objs, lib):
 
 
 def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = SOURCES + PEAKS_SOURCES
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
-    _link([objs[s] for s in SOURCES], LIB)
-    _link([objs[s] for s in PEAKS_SOURCES], PEAKS_LIB)
+    os.makedirs(DEBUG_BUILD, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES + PEAKS_SOURCES] + [(s, True) for s in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = dict(zip(jobs, ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs)))
+    _link([objs[(s, False)] for s in SOURCES], LIB)
+    _link([objs[(s, False)] for s in PEAKS_SOURCES], PEAKS_LIB)
+    _link([objs[(s, True)] for s in SOURCES], DEBUG_LIB)
     return LIB
+
+
+def build_asan_check() -> str:
+    """The host-ASan check of the C ABI's validation layer: api.hip's host code
+    and tests/native/abi_check.cpp built with AddressSanitizer (host code only;
+    the device code of every object is unchanged), linked with the library's
+    other objects into an executable that needs no GPU. Returns its path."""
+    out_dir = os.path.join(BUILD, "asan")
+    os.makedirs(out_dir, exist_ok=True)
+    objs = [os.path.join(BUILD, s.replace(".hip", ".o")) for s in SOURCES if s != "api.hip"]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    asan = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+    api_o = os.path.join(out_dir, "api.o")
+    chk_o = os.path.join(out_dir, "abi_check.o")
+    exe = os.path.join(out_dir, "xattn_abi_check")
+    steps = [
+        [HIPCC, *FLAGS, *asan, "-c", os.path.join(CSRC, "api.hip"), "-o", api_o],
+        [HIPCC, "--offload-arch=gfx950", "-O1", "-std=c++17", *asan, "-x", "c++", "-c",
+         os.path.join(ROOT, "tests", "native", "abi_check.cpp"), "-o", chk_o],
+        [HIPCC, "--offload-arch=gfx950", *asan, chk_o, api_o, *objs, "-o", exe],
+    ]
+    for cmd in steps:
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("ASan check build failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+    return exe
 
 
 if __name__ == "__main__":
     print(build(verbose="--verbose" in sys.argv))
+    if "--asan-check" in sys.argv:
+        print(build_asan_check())

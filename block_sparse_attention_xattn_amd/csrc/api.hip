@@ -356,6 +356,21 @@ xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
   return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, wsb + lay.queue_off, st);
 }
 
+#if XATTN_DEBUG
+// Debug builds only: the kernels' failed bounds checks per category (see
+// include/xattn_debug.h), summed over the sources; reset clears them.
+xattn_status xattn_debug_violations(uint32_t* out, int32_t n, int32_t reset) {
+  if (!out || n < (int32_t)xattn::DBG_CATEGORIES) return fail(XATTN_ERR_ARG, "need %d counters", (int)xattn::DBG_CATEGORIES);
+  unsigned int c[xattn::DBG_CATEGORIES] = {};
+  hipError_t e;
+  if ((e = xattn::debug_counts_score(c, reset)) != hipSuccess || (e = xattn::debug_counts_select(c, reset)) != hipSuccess ||
+      (e = xattn::debug_counts_attn(c, reset)) != hipSuccess || (e = xattn::debug_counts_dusa1(c, reset)) != hipSuccess)
+    return hip_status(e, "reading the debug counters");
+  for (int i = 0; i < (int)xattn::DBG_CATEGORIES; ++i) out[i] = c[i];
+  return XATTN_OK;
+}
+#endif
+
 xattn_status xattn_prefill_noalloc(const xattn_problem* p, const void* q, const void* k, const void* v,
                                    const float* tau, float score_scale, float sm_scale, float* block_scores,
                                    uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, void* out, float* lse,

@@ -95,6 +95,8 @@
 
 namespace xattn {
 
+XATTN_DEBUG_COUNTERS
+
 // Queries are the last Mq of Mk tokens: query block I is key block I + qoff.
 struct AttnArgs {
   const uint16_t* q;
@@ -272,6 +274,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   auto slot_I = [&](int s2) { return MODE == MODE_ROWS ? 2 * P + s2 : P; };
   const int h = slot_h(hs);                    // this wave's head
   const int I = slot_I(hs);                    // this wave's query block
+  XATTN_DCHECK(b < a.B && g < a.Hkv && h < a.Hq && P < NP && I <= a.NBq, DBG_ATTN_ITEM);
   const bool live = I < a.NBq;                 // the odd row count leaves a half-empty pair
 
   const size_t bh = (size_t)b * a.Hq + h;
@@ -399,6 +402,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
       if (e >= ebase + 64) {  // uniform: refresh the window
         ebase = e & ~63;
         const int el = min(ebase + lane, cnt > 0 ? cnt - 1 : 0);
+        XATTN_DCHECK(el < L::IDX_MAX, DBG_ATTN_LDS);
         ewin = SLOTS > 1 ? (uint32_t)idx_s[el] | ((uint32_t)memb_s[el] << 16) : (uint32_t)idx_s[el];
       }
       return (uint32_t)__builtin_amdgcn_readlane((int)ewin, e - ebase);
@@ -425,6 +429,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
       // keys past the end (a partial last block) load the last key; they are
       // masked out of the softmax
       const size_t kr = KTAIL ? (size_t)min(k0 + row, a.Mk - 1) : (size_t)(k0 + row);
+      XATTN_DCHECK(k0 >= 0 && kr < (size_t)a.Mk, DBG_ATTN_KV_ROW);
       r.k[p] = *reinterpret_cast<const u32x4*>(kh + kr * C + col);
       r.v[p] = *reinterpret_cast<const u32x4*>(vh + kr * C + col);
     }
@@ -588,6 +593,8 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
     // piece p of a sub-tile's DMA: block p / 2 of this wave, K (p even) or V
     constexpr int NPIECE = 2 * BPW;
     auto dma_piece = [&](int k0, int slot, int p) {
+      XATTN_DCHECK(KTAIL || (k0 >= 0 && k0 + L::KT <= a.Mk), DBG_ATTN_KV_ROW);
+      XATTN_DCHECK(slot >= 0 && slot < L::RING, DBG_ATTN_LDS);
       const int b2 = p >> 1;
       const bool isv = p & 1;
       const uint32_t lds = lds_addr_u((isv ? slot_v(slot) : slot_k(slot)) + (wv * BPW + b2) * 1024);
@@ -1164,6 +1171,25 @@ hipError_t launch_attn_f32(const Shape& s, const float* q, const float* k, const
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
+}
+
+
+hipError_t debug_counts_attn(unsigned int* out, bool reset) {
+#if XATTN_DEBUG
+  unsigned int h[DBG_CATEGORIES];
+  hipError_t e = hipMemcpyFromSymbol(h, HIP_SYMBOL(debug_counts), sizeof(h));
+  if (e != hipSuccess) return e;
+  for (int c = 0; c < DBG_CATEGORIES; ++c) out[c] += h[c];
+  if (reset) {
+    const unsigned int z[DBG_CATEGORIES] = {};
+    e = hipMemcpyToSymbol(HIP_SYMBOL(debug_counts), z, sizeof(z));
+  }
+  return e;
+#else
+  (void)out;
+  (void)reset;
+  return hipSuccess;
+#endif
 }
 
 }  // namespace xattn

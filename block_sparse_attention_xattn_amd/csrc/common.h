@@ -5,6 +5,28 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Debug builds (-DXATTN_DEBUG=1, libxattn_debug.so): bounds checks at the
+// kernels' indexing sites. A failed check adds one to a per-source device
+// counter of its category (no trap: the access that follows is the release
+// code's, already bounded); the host reads the counters through
+// xattn_debug_violations(). Release builds compile the checks away.
+#ifndef XATTN_DEBUG
+#define XATTN_DEBUG 0
+#endif
+// (the categories are xattn::DebugCheck, in kernels.h)
+#if XATTN_DEBUG
+#define XATTN_DEBUG_COUNTERS static __device__ unsigned int debug_counts[DBG_CATEGORIES];
+#define XATTN_DCHECK(cond, cat)                                      \
+  do {                                                               \
+    if (!(cond)) atomicAdd(&debug_counts[(cat)], 1u);                \
+  } while (0)
+#else
+#define XATTN_DEBUG_COUNTERS
+#define XATTN_DCHECK(cond, cat) \
+  do {                          \
+  } while (0)
+#endif
+
 namespace xattn {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -28,6 +28,8 @@
 
 namespace xattn {
 
+XATTN_DEBUG_COUNTERS
+
 struct Dusa1Args {
   const uint16_t* q;
   const uint16_t* k;
@@ -119,6 +121,7 @@ __global__ __launch_bounds__(256) void dusa1_lse_kernel(Dusa1Args a) {
   }
   const float lt = halves_sum(l);
   const int i = i0 + l32;
+  XATTN_DCHECK(bh < (size_t)a.B * a.Hq && s < a.S, DBG_DUSA1_INDEX);
   if (hh == 0 && i < a.Rq) a.lse[(bh * a.S + s) * (size_t)a.Rq + i] = m + log2f(lt);
 }
 
@@ -187,6 +190,7 @@ __global__ __launch_bounds__(256) void dusa1_block_kernel(Dusa1Args a) {
     const int I = qt * QB + ib, J = kt * KB + jb;
     if (I >= a.NBq || J >= a.NBk) continue;
     const int rows = min(RB, a.Rq - I * RB);
+    XATTN_DCHECK(rows >= 1 && bh < (size_t)a.B * a.Hq, DBG_DUSA1_INDEX);
     float sum = 0.f;
     for (int t = 0; t < rows; ++t) sum += red[ib * RB + t][jb];
     a.scores[(bh * a.NBq + I) * (size_t)a.NBk + J] = sum / (float)(a.S * rows);
@@ -230,6 +234,25 @@ hipError_t launch_score_dusa1(const Shape& s, const uint16_t* q, const uint16_t*
   if (s.C == 128) return launch_dusa1_c<128>(s, a, st);
   if (s.C == 64) return launch_dusa1_c<64>(s, a, st);
   return hipErrorInvalidValue;
+}
+
+
+hipError_t debug_counts_dusa1(unsigned int* out, bool reset) {
+#if XATTN_DEBUG
+  unsigned int h[DBG_CATEGORIES];
+  hipError_t e = hipMemcpyFromSymbol(h, HIP_SYMBOL(debug_counts), sizeof(h));
+  if (e != hipSuccess) return e;
+  for (int c = 0; c < DBG_CATEGORIES; ++c) out[c] += h[c];
+  if (reset) {
+    const unsigned int z[DBG_CATEGORIES] = {};
+    e = hipMemcpyToSymbol(HIP_SYMBOL(debug_counts), z, sizeof(z));
+  }
+  return e;
+#else
+  (void)out;
+  (void)reset;
+  return hipSuccess;
+#endif
 }
 
 }  // namespace xattn

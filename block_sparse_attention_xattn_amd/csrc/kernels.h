@@ -82,4 +82,22 @@ hipError_t launch_attn_f32(const Shape& s, const float* q, const float* k, const
                            const int32_t* kv_idx, const int32_t* kv_cnt, float sm_scale,
                            float* out, float* lse, hipStream_t st);
 
+// Categories of the debug build's bounds checks (XATTN_DCHECK in common.h).
+enum DebugCheck {
+  DBG_SCORE_STORE = 0,   // score partial written outside its head's [NBq][NBk][r] slab
+  DBG_SELECT_ROW = 1,    // selection row or candidate count outside its state
+  DBG_ATTN_KV_ROW = 2,   // K/V sub-tile rows outside [0, Mk)
+  DBG_ATTN_LDS = 3,      // LDS ring slot or list entry outside its region
+  DBG_ATTN_ITEM = 4,     // work item decoded outside (B, Hq, NBq)
+  DBG_DUSA1_INDEX = 5,   // DuSA1 log-sum-exp or block-score index out of range
+  DBG_CATEGORIES = 8
+};
+
+// Debug builds: adds each source's check counters into out[8] (and clears
+// them when reset); release builds leave out untouched.
+hipError_t debug_counts_score(unsigned int* out, bool reset);
+hipError_t debug_counts_select(unsigned int* out, bool reset);
+hipError_t debug_counts_attn(unsigned int* out, bool reset);
+hipError_t debug_counts_dusa1(unsigned int* out, bool reset);
+
 }  // namespace xattn

@@ -39,6 +39,8 @@
 
 namespace xattn {
 
+XATTN_DEBUG_COUNTERS
+
 struct ScoreArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -200,7 +202,10 @@ __device__ __forceinline__ void score_epilogue(const ScoreArgs& a, const f32x16 
           const float Lv = (m == -INFINITY) ? -INFINITY : m + log2f(s);
           const int j = jb + 8 * (r0 >> 2) + 4 * hh + (r0 & 3);
           const int J = j / RB;
-          if (i < a.Rq && j < a.Rk) wsh[((size_t)(i / RB) * a.NBk + J) * RB + i % RB] = Lv;
+          if (i < a.Rq && j < a.Rk) {
+            XATTN_DCHECK(i / RB < a.NBq && J < a.NBk, DBG_SCORE_STORE);
+            wsh[((size_t)(i / RB) * a.NBk + J) * RB + i % RB] = Lv;
+          }
         }
       }
     }
@@ -255,7 +260,10 @@ __device__ __forceinline__ void score_epilogue(const ScoreArgs& a, const f32x16 
           sum += fast_exp2(fmaf(lo[k], a.scale2, -mu)) + fast_exp2(fmaf(hi[k], a.scale2, -mu));
         // sum >= 1 (the max term), so the hardware log2 needs no denormal care
         const float Lv = (ms == -INFINITY) ? -INFINITY : ms + __builtin_amdgcn_logf(sum);
-        if (i < a.Rq && jr < a.Rk) wsh[((size_t)(i / RB) * a.NBk + jr / RB) * RB + i % RB] = Lv;
+        if (i < a.Rq && jr < a.Rk) {
+          XATTN_DCHECK(i / RB < a.NBq && jr / RB < a.NBk, DBG_SCORE_STORE);
+          wsh[((size_t)(i / RB) * a.NBk + jr / RB) * RB + i % RB] = Lv;
+        }
       }
     }
   }
@@ -668,6 +676,25 @@ hipError_t launch_score_finalize(const Shape& s, const float* ws, float* block_s
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+
+hipError_t debug_counts_score(unsigned int* out, bool reset) {
+#if XATTN_DEBUG
+  unsigned int h[DBG_CATEGORIES];
+  hipError_t e = hipMemcpyFromSymbol(h, HIP_SYMBOL(debug_counts), sizeof(h));
+  if (e != hipSuccess) return e;
+  for (int c = 0; c < DBG_CATEGORIES; ++c) out[c] += h[c];
+  if (reset) {
+    const unsigned int z[DBG_CATEGORIES] = {};
+    e = hipMemcpyToSymbol(HIP_SYMBOL(debug_counts), z, sizeof(z));
+  }
+  return e;
+#else
+  (void)out;
+  (void)reset;
+  return hipSuccess;
+#endif
 }
 
 }  // namespace xattn

@@ -30,6 +30,8 @@
 
 namespace xattn {
 
+XATTN_DEBUG_COUNTERS
+
 // Rows are (b, h, I) with I < NBq; row I's candidates are key blocks
 // J <= I + qoff (causal) or all J < NBk, and its diagonal block is I + qoff.
 struct SelectArgs {
@@ -304,6 +306,7 @@ __global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   int npad = 1;
   while (npad < n) npad <<= 1;
   const float* srow = a.scores + row * NB;
+  XATTN_DCHECK(n <= CAP && NB <= CAP, DBG_SELECT_ROW);
 #if XATTN_SELECT_SORT
   for (int p = tid; p < npad; p += 256) sh.keys[p] = p < n ? sel_key(srow[p], p) : 0;
   for (int p = tid; p < NB; p += 256) sh.flags[p] = 0;
@@ -348,6 +351,7 @@ __global__ __launch_bounds__(256) void score_select_kernel(FusedArgs a) {
   while (npad < n) npad <<= 1;
   const float* L = a.ws + (bh * (size_t)a.NBq + I) * (size_t)NB * RB;
   float* orow = a.scores ? a.scores + row * NB : nullptr;  // block scores are an optional output
+  XATTN_DCHECK(n <= CAP && NB <= CAP && rows >= 1 && rows <= RB, DBG_SELECT_ROW);
   for (int p = tid; p < NB; p += 256) sh.flags[p] = 0;
 #if XATTN_SELECT_SORT
   for (int p = n + tid; p < npad; p += 256) sh.keys[p] = 0;
@@ -740,6 +744,25 @@ hipError_t launch_select_global(const Shape& s, const float* block_scores, const
   hipLaunchKernelGGL(gsel_ties_kernel, dim3((unsigned)heads), dim3(256), 0, st, a);
   hipLaunchKernelGGL(gsel_compact_kernel, dim3((unsigned)(heads * NBq)), dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+
+hipError_t debug_counts_select(unsigned int* out, bool reset) {
+#if XATTN_DEBUG
+  unsigned int h[DBG_CATEGORIES];
+  hipError_t e = hipMemcpyFromSymbol(h, HIP_SYMBOL(debug_counts), sizeof(h));
+  if (e != hipSuccess) return e;
+  for (int c = 0; c < DBG_CATEGORIES; ++c) out[c] += h[c];
+  if (reset) {
+    const unsigned int z[DBG_CATEGORIES] = {};
+    e = hipMemcpyToSymbol(HIP_SYMBOL(debug_counts), z, sizeof(z));
+  }
+  return e;
+#else
+  (void)out;
+  (void)reset;
+  return hipSuccess;
+#endif
 }
 
 }  // namespace xattn

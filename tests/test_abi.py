@@ -302,3 +302,41 @@ def test_dusa1_workspace(xa):
     lse = 1 * 4 * 1024 * 4
     assert xa.workspace_bytes(p) == (lse + 255) // 256 * 256 + 1 * 4 * 8 * 8 * 4
     assert xa.total_workspace_bytes(p) == (xa.workspace_bytes(p) + 255) // 256 * 256 + 1024
+
+
+def test_validation_layer_under_address_sanitizer():
+    # api.hip's host code and a driver of every refused path, built with
+    # AddressSanitizer on the host side (device code unchanged); no GPU needed
+    import importlib.util
+    import shutil
+    import subprocess
+    if not shutil.which(os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")):
+        pytest.skip("hipcc not available")
+    spec = importlib.util.spec_from_file_location(
+        "_xattn_build", os.path.join(ROOT, "block_sparse_attention_xattn_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    exe = mod.build_asan_check()
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:halt_on_error=1:abort_on_error=0")
+    res = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert "all validation paths refused as expected" in res.stdout
+    assert "AddressSanitizer" not in res.stderr
+
+
+def test_debug_library_exports_its_header():
+    # the debug build exports one more entry point, declared in xattn_debug.h;
+    # the release library does not
+    lib = ctypes.CDLL(os.path.join(ROOT, "block_sparse_attention_xattn_amd", "libxattn_debug.so"))
+    text = open(os.path.join(ROOT, "include", "xattn_debug.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)
+    names = sorted(set(re.findall(r"\b(\w+)\s*\([^;{]*\)\s*;", text)))
+    assert names == ["xattn_debug_violations"]
+    assert hasattr(lib, "xattn_debug_violations")
+    for n in _declared():
+        assert hasattr(lib, n), n
+    import block_sparse_attention_xattn_amd as xa
+    assert not hasattr(xa._lib, "xattn_debug_violations")
+    lib.xattn_debug_violations.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32]
+    assert lib.xattn_debug_violations(None, 8, 0) == 4
