@@ -360,14 +360,18 @@ def cpu_baseline(wl, torch, res, budget_s):
 
 def run_variants(xa, torch, head, steps):
     """The headline layer through xattn_prefill with each method variant:
-    global and GQA-union selection, the diagonal and DuSA1 scoring patterns, a
-    chunked prefill step and a ragged length."""
+    per-row selection on the same buffers (no mask output, the reference for
+    the others), selection inside the scoring launch, global and GQA-union
+    selection, the diagonal and DuSA1 scoring patterns, a chunked prefill step
+    and a ragged length."""
     w = head["workload"]
     q, k, v, tau = head["_tensors"][:4]
     sscale, smscale = 1.0 / (w.stride * math.sqrt(w.C)), 1.0 / math.sqrt(w.C)
     cand = w.B * w.Hq * (w.nb * (w.nb + 1) // 2 if w.causal else w.nb * w.nb)
     res = {}
-    for label, kw in (("select_global", dict(selection="global")),
+    for label, kw in (("select_row", {}),
+                      ("select_in_score", dict(select_in_score=True)),
+                      ("select_global", dict(selection="global")),
                       ("select_gqa_union", dict(selection="gqa_union")),
                       ("pattern_diagonal", dict(pattern=xa.DIAGONAL)),
                       ("pattern_dusa1", dict(pattern=xa.DUSA1))):

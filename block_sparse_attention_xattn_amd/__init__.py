@@ -29,7 +29,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 XATTN_BF16 = 0
 XATTN_F32 = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 MAX_HEADS = 256
 
 EXPORTS = (
@@ -47,13 +47,17 @@ DUSA1 = 2
 SELECT_ROW = 0
 SELECT_GLOBAL = 1
 SELECT_GQA_UNION = 2
+
+# xattn_flags
+SELECT_IN_SCORE = 1
+
 _SELECTIONS = {"row": SELECT_ROW, "global": SELECT_GLOBAL, "gqa_union": SELECT_GQA_UNION}
 
 
 class Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("B", "Hq", "Hkv", "M", "C", "block", "stride", "causal", "dtype", "pattern", "selection",
-                 "Mk")]
+                 "Mk", "flags")]
 
 
 _P = ctypes.POINTER(Problem)
@@ -109,17 +113,19 @@ def _selection(sel) -> int:
 
 
 def problem(B, Hq, Hkv, M, C, block, stride, causal, dtype, pattern=ANTIDIAGONAL,
-            selection=SELECT_ROW, Mk=0) -> Problem:
+            selection=SELECT_ROW, Mk=0, flags=0) -> Problem:
     """C struct for the given sizes; dtype is torch.bfloat16/torch.float32 or 0/1;
     selection is an xattn_selection value or "row" / "global" / "gqa_union";
-    Mk is the key length (0: M; the queries are the last M of Mk tokens)."""
+    Mk is the key length (0: M; the queries are the last M of Mk tokens);
+    flags OR-s xattn_flags (SELECT_IN_SCORE)."""
     if isinstance(dtype, torch.dtype):
         dtype = {torch.bfloat16: XATTN_BF16, torch.float32: XATTN_F32}.get(dtype, 99)
     return Problem(B, Hq, Hkv, M, C, block, stride, int(bool(causal)), dtype, pattern,
-                   _selection(selection), Mk)
+                   _selection(selection), Mk, flags)
 
 
-def _problem_of(q, k, block, stride, causal, pattern=ANTIDIAGONAL, selection=SELECT_ROW, v=None) -> Problem:
+def _problem_of(q, k, block, stride, causal, pattern=ANTIDIAGONAL, selection=SELECT_ROW, v=None,
+                flags=0) -> Problem:
     """Sizes from q (B, Hq, M, C), k (B, Hkv, Mk, C) and, if given, v (k's shape)."""
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q and k must be 4-D (B, H, M, C)")
@@ -129,7 +135,7 @@ def _problem_of(q, k, block, stride, causal, pattern=ANTIDIAGONAL, selection=SEL
     if v is not None and v.shape != k.shape:
         raise ValueError(f"v {tuple(v.shape)} must have k's shape {tuple(k.shape)}")
     return problem(B, Hq, k.shape[1], M, C, block, stride, causal, q.dtype, pattern, selection,
-                   Mk=k.shape[2])
+                   Mk=k.shape[2], flags=flags)
 
 
 def _expect(t, name, shape, dtype, device):
@@ -288,16 +294,20 @@ class PrefillBuffers:
 
     ``key`` records what the buffers were sized for; xattn_prefill refuses
     inputs or arguments that differ from it. want_scores=False leaves the block
-    scores unwritten (not allowed with global selection)."""
+    scores unwritten (not allowed with global selection). select_in_score asks
+    for normalisation and selection inside the scoring launch
+    (XATTN_SELECT_IN_SCORE)."""
 
     def __init__(self, q, k, block, stride, causal=True, want_mask=True, want_lse=False,
-                 pattern=ANTIDIAGONAL, selection=SELECT_ROW, want_scores=True, want_ws=True):
-        p = _problem_of(q, k, block, stride, causal, pattern, selection)
+                 pattern=ANTIDIAGONAL, selection=SELECT_ROW, want_scores=True, want_ws=True,
+                 select_in_score=False):
+        p = _problem_of(q, k, block, stride, causal, pattern, selection,
+                        flags=SELECT_IN_SCORE if select_in_score else 0)
         B, Hq, M, C = q.shape
         nbq, nbk = _cdiv(M, block), _cdiv(k.shape[2], block)
         dev = q.device
         self.problem = p
-        self.key = _prefill_key(q, k, block, stride, causal, pattern, selection)
+        self.key = _prefill_key(q, k, block, stride, causal, pattern, selection, select_in_score)
         self.block_scores = (torch.empty((B, Hq, nbq, nbk), dtype=torch.float32, device=dev)
                              if want_scores else None)
         self.mask = torch.empty((B, Hq, nbq, nbk), dtype=torch.uint8, device=dev) if want_mask else None
@@ -309,22 +319,24 @@ class PrefillBuffers:
         self.lse = torch.empty((B, Hq, M), dtype=torch.float32, device=dev) if want_lse else None
 
 
-def _prefill_key(q, k, block, stride, causal, pattern, selection):
+def _prefill_key(q, k, block, stride, causal, pattern, selection, select_in_score=False):
     return (tuple(q.shape), tuple(k.shape), q.dtype, str(q.device), int(block), int(stride),
-            bool(causal), int(pattern), _selection(selection))
+            bool(causal), int(pattern), _selection(selection), bool(select_in_score))
 
 
 def xattn_prefill(q, k, v, tau, block, stride, score_scale, sm_scale, causal=True, buffers=None,
-                  pattern=ANTIDIAGONAL, selection=SELECT_ROW, want_scores=True):
+                  pattern=ANTIDIAGONAL, selection=SELECT_ROW, want_scores=True, select_in_score=False):
     """All three stages in one call. Returns the PrefillBuffers holding the results
-    (block_scores is None when want_scores is False)."""
+    (block_scores is None when want_scores is False). select_in_score: normalise
+    and select inside the scoring launch (same results, one launch fewer; slower
+    on MI355X, see XATTN_SELECT_IN_SCORE)."""
     _same(q, k, v)
     _problem_of(q, k, block, stride, causal, pattern, selection, v=v)
-    if buffers is not None and buffers.key != _prefill_key(q, k, block, stride, causal, pattern, selection):
-        raise ValueError("buffers were made for other inputs or arguments: "
-                         f"{buffers.key} != {_prefill_key(q, k, block, stride, causal, pattern, selection)}")
+    key = _prefill_key(q, k, block, stride, causal, pattern, selection, select_in_score)
+    if buffers is not None and buffers.key != key:
+        raise ValueError(f"buffers were made for other inputs or arguments: {buffers.key} != {key}")
     bufs = buffers or PrefillBuffers(q, k, block, stride, causal, pattern=pattern, selection=selection,
-                                     want_scores=want_scores)
+                                     want_scores=want_scores, select_in_score=select_in_score)
     tau_h = _tau_host(tau, q.shape[1])
     b = bufs
     _check(_lib.xattn_prefill(ctypes.byref(b.problem), _ptr(q), _ptr(k), _ptr(v), tau_h.data_ptr(),
@@ -338,17 +350,18 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def xattn_prefill_noalloc(q, k, v, tau, block, stride, score_scale, sm_scale, causal=True, buffers=None,
-                          pattern=ANTIDIAGONAL, selection=SELECT_ROW, want_scores=True):
+                          pattern=ANTIDIAGONAL, selection=SELECT_ROW, want_scores=True, select_in_score=False):
     """xattn_prefill on the library's own per-GPU scratch (no workspace), for
     callers that cannot allocate device memory. Pass ``buffers`` (a
     PrefillBuffers, e.g. made with want_ws=False) to allocate nothing here
     either. Calls that overlap on one GPU share the scratch and race."""
     _same(q, k, v)
     _problem_of(q, k, block, stride, causal, pattern, selection, v=v)
-    if buffers is not None and buffers.key != _prefill_key(q, k, block, stride, causal, pattern, selection):
+    if buffers is not None and buffers.key != _prefill_key(q, k, block, stride, causal, pattern, selection,
+                                                          select_in_score):
         raise ValueError("buffers were made for other inputs or arguments")
     bufs = buffers or PrefillBuffers(q, k, block, stride, causal, pattern=pattern, selection=selection,
-                                     want_scores=want_scores, want_ws=False)
+                                     want_scores=want_scores, want_ws=False, select_in_score=select_in_score)
     tau_h = _tau_host(tau, q.shape[1])
     b = bufs
     _check(_lib.xattn_prefill_noalloc(ctypes.byref(b.problem), _ptr(q), _ptr(k), _ptr(v), tau_h.data_ptr(),

@@ -39,6 +39,8 @@ xattn_status check_problem(const xattn_problem* p, bool need_stride = true) {
   if (p->selection != XATTN_SELECT_ROW && p->selection != XATTN_SELECT_GLOBAL &&
       p->selection != XATTN_SELECT_GQA_UNION)
     return fail(XATTN_ERR_ARG, "selection %d is not an xattn_selection", p->selection);
+  if (p->flags & ~(int32_t)XATTN_SELECT_IN_SCORE)
+    return fail(XATTN_ERR_ARG, "flags 0x%x hold bits that are not xattn_flags", (unsigned)p->flags);
   const int mk = p->Mk ? p->Mk : p->M;
   if (mk < p->M) return fail(XATTN_ERR_SHAPE, "Mk=%d is shorter than M=%d", p->Mk, p->M);
   if (p->Hq % p->Hkv) return fail(XATTN_ERR_SHAPE, "Hq=%d is not a multiple of Hkv=%d", p->Hq, p->Hkv);
@@ -132,13 +134,14 @@ xattn_status do_score(const xattn_problem* p, const void* q, const void* k, floa
 
 xattn_status do_attn(const xattn_problem* p, const void* q, const void* k, const void* v,
                      const int32_t* kv_idx, const int32_t* kv_cnt, float sm_scale, void* out,
-                     float* lse, void* queue, hipStream_t st) {
+                     float* lse, void* queue, hipStream_t st, bool queue_zeroed = false) {
   const xattn::Shape s = shape_of(p);
   hipError_t e;
   if (p->dtype == XATTN_BF16)
     e = xattn::launch_attn_bf16(s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                 static_cast<const uint16_t*>(v), kv_idx, kv_cnt, sm_scale,
-                                static_cast<uint16_t*>(out), lse, static_cast<uint32_t*>(queue), st);
+                                static_cast<uint16_t*>(out), lse, static_cast<uint32_t*>(queue), st,
+                                queue_zeroed);
   else
     e = xattn::launch_attn_f32(s, static_cast<const float*>(q), static_cast<const float*>(k),
                                static_cast<const float*>(v), kv_idx, kv_cnt, sm_scale,
@@ -166,17 +169,28 @@ xattn_status do_select(const xattn_problem* p, const float* block_scores, const 
   return r;
 }
 
-// xattn_prefill's workspace: score partials | select scratch | attention queues,
-// each part starting on a 256-byte boundary.
+// xattn_prefill normalises and selects inside the scoring launch when asked
+// to and the scoring runs on the DMA kernel
+bool select_in_score(const xattn_problem* p) {
+  return (p->flags & XATTN_SELECT_IN_SCORE) && p->dtype == XATTN_BF16 && xattn::tile_select_ok(shape_of(p));
+}
+
+// xattn_prefill's workspace: score partials | select scratch | arrival
+// counters (when selection runs in the scoring launch) | attention queues,
+// each part starting on a 256-byte boundary; the last two are zeroed by one
+// launch.
 struct PrefillLayout {
-  size_t select_off, queue_off, total;
+  size_t select_off, arrive_off, queue_off, total;
 };
 PrefillLayout prefill_layout(const xattn_problem* p) {
+  const xattn::Shape s = shape_of(p);
   const size_t score = xattn_score_workspace_bytes(p);
-  const size_t sel = xattn::select_workspace_bytes(shape_of(p), p->selection);
+  const size_t sel = xattn::select_workspace_bytes(s, p->selection);
   PrefillLayout l;
   l.select_off = align256(score);
-  l.queue_off = align256(l.select_off + sel);
+  l.arrive_off = align256(l.select_off + sel);
+  const bool one_launch = select_in_score(p);
+  l.queue_off = align256(l.arrive_off + (one_launch ? xattn::arrive_words(s) * sizeof(uint32_t) : 0));
   l.total = l.queue_off + xattn_attn_workspace_bytes(p);
   return l;
 }
@@ -332,6 +346,25 @@ xattn_status xattn_prefill(const xattn_problem* p, const void* q, const void* k,
     if ((s = do_score_dusa1(p, q, k, score_scale, sc, ws, st)) != XATTN_OK) return s;
     if ((s = do_select(p, sc, t, mask, kv_idx, kv_cnt, wsb + lay.select_off, st)) != XATTN_OK) return s;
     return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, wsb + lay.queue_off, st);
+  }
+  if (select_in_score(p)) {
+    // one launch zeroes the arrival counters and the attention queues; the
+    // scoring launch then normalises and selects each query tile's rows as
+    // soon as the tile's last partials are stored
+    uint32_t* arrive = reinterpret_cast<uint32_t*>(wsb + lay.arrive_off);
+    const size_t words = (lay.queue_off - lay.arrive_off) / sizeof(uint32_t) + xattn::kQueueWords;
+    if ((s = hip_status(xattn::launch_clear_words(arrive, words, st), "workspace clear launch")) != XATTN_OK)
+      return s;
+    xattn::TileSelect ts{arrive, block_scores, mask, kv_idx, kv_cnt, sh.qoff(), t};
+    if ((s = hip_status(xattn::launch_score_tile_select(sh, static_cast<const uint16_t*>(q),
+                                                        static_cast<const uint16_t*>(k), score_scale,
+                                                        static_cast<float*>(ws), ts, st),
+                        "score+select launch")) != XATTN_OK)
+      return s;
+    if (p->selection == XATTN_SELECT_GQA_UNION &&
+        (s = hip_status(xattn::launch_gqa_union(sh, mask, kv_idx, kv_cnt, st), "GQA union launch")) != XATTN_OK)
+      return s;
+    return do_attn(p, q, k, v, kv_idx, kv_cnt, sm_scale, out, lse, wsb + lay.queue_off, st, true);
   }
   if ((s = do_partials(p, q, k, score_scale, ws, st)) != XATTN_OK) return s;
   if (p->selection == XATTN_SELECT_GLOBAL) {

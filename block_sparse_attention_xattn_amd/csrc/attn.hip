@@ -1069,7 +1069,7 @@ static int resident_workgroups(Kern kern, int threads) {
 }
 
 template <int C, int BLK, int MODE, bool KTAIL, int RPW>
-static hipError_t launch_bf16_cbmt(const Shape& s, const AttnArgs& a, hipStream_t st) {
+static hipError_t launch_bf16_cbmt(const Shape& s, const AttnArgs& a, hipStream_t st, bool queue_zeroed) {
   const int G = s.Hq / s.Hkv;
   const int NP = MODE == MODE_ROWS ? (s.NBq() + 1) / 2 : s.NBq();
   const int GW = MODE == MODE_SIBLINGS ? G / 2 : G;
@@ -1088,9 +1088,11 @@ static hipError_t launch_bf16_cbmt(const Shape& s, const AttnArgs& a, hipStream_
                        : attn_fwd_bf16_kernel<C, BLK, false, true, MODE, KTAIL, RPW>;
   const int slots = resident_workgroups(kern, threads);
   if (slots <= 0) return hipErrorInvalidDeviceFunction;
-  hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(kQueueWords), 0, st, a.queue);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!queue_zeroed) {
+    hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(kQueueWords), 0, st, a.queue);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((unsigned)(n_items < (size_t)slots ? n_items : (size_t)slots));
   hipLaunchKernelGGL(kern, grid, dim3(threads), 0, st, a);
   return hipGetLastError();
@@ -1106,17 +1108,17 @@ static hipError_t launch_bf16_cbmt(const Shape& s, const AttnArgs& a, hipStream_
 #endif
 
 template <int C, int BLK, int MODE, int RPW>
-static hipError_t launch_bf16_cbmr(const Shape& s, const AttnArgs& a, hipStream_t st) {
-  return s.Mk % BLK ? launch_bf16_cbmt<C, BLK, MODE, true, RPW>(s, a, st)
-                    : launch_bf16_cbmt<C, BLK, MODE, false, RPW>(s, a, st);
+static hipError_t launch_bf16_cbmr(const Shape& s, const AttnArgs& a, hipStream_t st, bool qz) {
+  return s.Mk % BLK ? launch_bf16_cbmt<C, BLK, MODE, true, RPW>(s, a, st, qz)
+                    : launch_bf16_cbmt<C, BLK, MODE, false, RPW>(s, a, st, qz);
 }
 
 template <int C, int BLK, int MODE>
-static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t st) {
+static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t st, bool qz) {
   constexpr int SR = BLK >= XATTN_SPARSE_RPW ? XATTN_SPARSE_RPW : 32;
   constexpr int DR = BLK >= XATTN_DENSE_RPW ? XATTN_DENSE_RPW : 32;
-  return a.kv_idx != nullptr ? launch_bf16_cbmr<C, BLK, MODE, SR>(s, a, st)
-                             : launch_bf16_cbmr<C, BLK, MODE, DR>(s, a, st);
+  return a.kv_idx != nullptr ? launch_bf16_cbmr<C, BLK, MODE, SR>(s, a, st, qz)
+                             : launch_bf16_cbmr<C, BLK, MODE, DR>(s, a, st, qz);
 }
 
 // 128-row blocks: dense attention pairs GQA siblings (identical block lists)
@@ -1128,32 +1130,32 @@ static hipError_t launch_bf16_cbm(const Shape& s, const AttnArgs& a, hipStream_t
 // very different numbers of blocks, so a sibling pair would leave one half
 // idle. 64-row blocks use one (head, row) per workgroup.
 template <int C, int BLK>
-static hipError_t launch_bf16_cb(const Shape& s, const AttnArgs& a, hipStream_t st) {
+static hipError_t launch_bf16_cb(const Shape& s, const AttnArgs& a, hipStream_t st, bool qz) {
   if (BLK == 128) {
     const bool pairs = (s.Hq / s.Hkv) % 2 == 0;
-    if (a.kv_idx == nullptr && pairs) return launch_bf16_cbm<C, BLK, MODE_SIBLINGS>(s, a, st);
+    if (a.kv_idx == nullptr && pairs) return launch_bf16_cbm<C, BLK, MODE_SIBLINGS>(s, a, st, qz);
     // GQA-union lists are shared by the siblings: one tile load serves both
     if (a.kv_idx != nullptr && pairs && s.selection == SEL_GQA_UNION)
-      return launch_bf16_cbm<C, BLK, MODE_SIBLINGS>(s, a, st);
+      return launch_bf16_cbm<C, BLK, MODE_SIBLINGS>(s, a, st, qz);
     if (a.kv_idx != nullptr &&
         s.NBq() >= (s.causal ? XATTN_SPARSE_PAIR_ROWS_MIN_NB : XATTN_SPARSE_PAIR_ROWS_MIN_NB_NC))
-      return launch_bf16_cbm<C, BLK, MODE_ROWS>(s, a, st);
-    if (a.kv_idx == nullptr && XATTN_DENSE_PAIR_ROWS) return launch_bf16_cbm<C, BLK, MODE_ROWS>(s, a, st);
+      return launch_bf16_cbm<C, BLK, MODE_ROWS>(s, a, st, qz);
+    if (a.kv_idx == nullptr && XATTN_DENSE_PAIR_ROWS) return launch_bf16_cbm<C, BLK, MODE_ROWS>(s, a, st, qz);
   }
-  return launch_bf16_cbm<C, BLK, MODE_SINGLE>(s, a, st);
+  return launch_bf16_cbm<C, BLK, MODE_SINGLE>(s, a, st, qz);
 }
 
 hipError_t launch_attn_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, const int32_t* kv_idx, const int32_t* kv_cnt,
                             float sm_scale, uint16_t* out, float* lse, uint32_t* queue,
-                            hipStream_t st) {
+                            hipStream_t st, bool queue_zeroed) {
   AttnArgs a{q,   k,    v,        kv_idx,  kv_cnt,  out,    lse,    queue,
              s.B, s.Hq, s.Hkv,    s.M,     s.Mk,    s.NBq(), s.NBk(), s.qoff(),
              sm_scale * kLog2e};
-  if (s.C == 128 && s.block == 128) return launch_bf16_cb<128, 128>(s, a, st);
-  if (s.C == 128 && s.block == 64) return launch_bf16_cb<128, 64>(s, a, st);
-  if (s.C == 64 && s.block == 128) return launch_bf16_cb<64, 128>(s, a, st);
-  if (s.C == 64 && s.block == 64) return launch_bf16_cb<64, 64>(s, a, st);
+  if (s.C == 128 && s.block == 128) return launch_bf16_cb<128, 128>(s, a, st, queue_zeroed);
+  if (s.C == 128 && s.block == 64) return launch_bf16_cb<128, 64>(s, a, st, queue_zeroed);
+  if (s.C == 64 && s.block == 128) return launch_bf16_cb<64, 128>(s, a, st, queue_zeroed);
+  if (s.C == 64 && s.block == 64) return launch_bf16_cb<64, 64>(s, a, st, queue_zeroed);
   return hipErrorInvalidValue;
 }
 

@@ -69,15 +69,38 @@ hipError_t launch_gqa_union(const Shape& s, uint8_t* mask, int32_t* kv_idx, int3
 hipError_t launch_score_select(const Shape& s, const float* ws, float* block_scores, const TauArray& tau,
                                uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt, hipStream_t st);
 
+// Stages 1-3 in the scoring launch (xattn_prefill, per-row or GQA-union
+// selection, bf16 with complete stride groups): the workgroup that stores the
+// last partials of a (b, h, query tile) normalises and selects that tile's
+// query-block rows. `arrive` holds arrive_words(s) counters that must be zero
+// when the launch starts; block scores and the mask are optional outputs. The
+// results equal launch_score_partials_bf16 followed by launch_score_select.
+struct TileSelect {
+  uint32_t* arrive;
+  float* scores;
+  uint8_t* mask;
+  int32_t* kv_idx;
+  int32_t* kv_cnt;
+  int qoff;  // key block of query block 0
+  TauArray tau;
+};
+bool tile_select_ok(const Shape& s);
+size_t arrive_words(const Shape& s);
+hipError_t launch_score_tile_select(const Shape& s, const uint16_t* q, const uint16_t* k, float score_scale,
+                                    float* ws, const TileSelect& sel, hipStream_t st);
+// Zeroes n words of device memory (a kernel, so the call can be captured).
+hipError_t launch_clear_words(uint32_t* words, size_t n, hipStream_t st);
+
 // Stage 4: attention over listed key blocks (kv_idx == nullptr: every candidate).
 // The sparse bf16 kernel schedules its rows through per-XCD item queues held
 // in `queue` (kQueueWords words of device memory, cleared by the launcher on
-// the stream first); dense launches ignore it.
+// the stream first unless queue_zeroed says an earlier launch on the stream
+// already did); dense launches ignore it.
 constexpr int kQueueWords = 256;
 hipError_t launch_attn_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
                             const uint16_t* v, const int32_t* kv_idx, const int32_t* kv_cnt,
                             float sm_scale, uint16_t* out, float* lse, uint32_t* queue,
-                            hipStream_t st);
+                            hipStream_t st, bool queue_zeroed = false);
 hipError_t launch_attn_f32(const Shape& s, const float* q, const float* k, const float* v,
                            const int32_t* kv_idx, const int32_t* kv_cnt, float sm_scale,
                            float* out, float* lse, hipStream_t st);

@@ -36,6 +36,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "score_row.h"
+#include "select_row.h"
 
 namespace xattn {
 
@@ -419,6 +420,70 @@ __device__ __forceinline__ int sd_off(int row, int chunk) { return row * SD_ROW 
 // Waits until at most N of this wave's loads (DMA included) are outstanding,
 // then the workgroup barrier; the empty asm statements keep LDS accesses from
 // being moved across it.
+// ------------------------------------------------------------------ selection in the scoring launch
+//
+// xattn_prefill with per-row or GQA-union selection runs normalisation and
+// selection inside the scoring launch. Each (b, h, query tile) has an arrival
+// counter, zero before the launch. A workgroup that has stored its tile's
+// partials adds one to the counter with an agent-scope acquire-release atomic
+// (its barrier first orders every wave's stores before that release); the
+// workgroup that brings the counter to the query tile's number of key tiles
+// then sees every partial of the tile's query-block rows and normalises and
+// selects those rows at once, two at a time, one per 256-thread half, with the
+// row code of the fused normalise+select kernel, so block scores, masks and
+// lists are bit-identical to the staged path's. The halves pass the same
+// number of barriers per row (the row code's count depends only on the head's
+// tau), and with an odd number of rows the second half repeats the last row,
+// writing the same values. The row state of each half lives in one stage of
+// the now idle operand ring.
+#if !XATTN_SELECT_SORT
+template <int RB, bool CAUSAL>
+__device__ __forceinline__ void tile_select(const ScoreArgs& a, const TileSelect& sel, size_t bh, int i0,
+                                            uint16_t* ring0, uint16_t* ring1, int ring_bytes) {
+  using SL = SelectLdsT<SEL_MAX>;
+  __shared__ uint32_t last;
+  const int tid = threadIdx.x;
+  const int tq = i0 / SC_TILE;
+  __syncthreads();  // every wave's partials are stored; the ring is no longer read
+  if (tid == 0) {
+    const uint32_t need = CAUSAL ? (uint32_t)min(a.Tk, tq + a.c0 + 1) : (uint32_t)a.Tk;
+    const uint32_t old = __hip_atomic_fetch_add(sel.arrive + bh * a.Tq + tq, 1u, __ATOMIC_ACQ_REL,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    XATTN_DCHECK(old < need, DBG_SCORE_STORE);
+    last = old + 1 == need;
+  }
+  __syncthreads();
+  if (!last) return;
+  const int half = tid >> 8, t = tid & 255;
+  char* base = reinterpret_cast<char*>(half ? ring1 : ring0);
+  SL& sh = *reinterpret_cast<SL*>(base);
+  ScoreRowLds& shs = *reinterpret_cast<ScoreRowLds*>(base + sizeof(SL));
+  XATTN_DCHECK(sizeof(SL) + sizeof(ScoreRowLds) <= (size_t)ring_bytes, DBG_SELECT_ROW);
+  (void)ring_bytes;
+  const int NB = a.NBk;
+  const int I0 = i0 / RB, I1 = min(a.NBq, I0 + SC_TILE / RB);
+  const float tau = sel.tau.v[bh % a.Hq];
+  for (int I = I0 + half; I - half < I1; I += 2) {
+    const int Ir = min(I, I1 - 1);
+    const int Ia = Ir + sel.qoff;
+    const int n = CAUSAL ? Ia + 1 : NB;
+    const int rows = min(RB, a.Rq - Ir * RB);
+    const size_t row = bh * a.NBq + Ir;
+    const float* L = a.ws + row * (size_t)NB * RB;
+    float* orow = sel.scores ? sel.scores + row * NB : nullptr;
+    XATTN_DCHECK(n <= SEL_MAX && NB <= SEL_MAX && rows >= 1 && rows <= RB, DBG_SELECT_ROW);
+    __syncthreads();  // the previous row's state is no longer read
+    for (int p = t; p < NB; p += 256) sh.flags[p] = 0;
+    block_score_row<RB>(L, n, NB, rows, shs, t, [&](int J, float sc) {
+      if (orow) orow[J] = sc;
+      if (J < n) sh.sc[J] = sc;
+    });
+    __syncthreads();
+    select_radix(sh, t, n, NB, Ia, tau, row, sel.mask, sel.kv_idx, sel.kv_cnt);
+  }
+}
+#endif
+
 template <int N>
 __device__ __forceinline__ void vm_wait_barrier() {
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(N));
@@ -427,8 +492,8 @@ __device__ __forceinline__ void vm_wait_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int C, int RB, bool CAUSAL>
-__global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_kernel(ScoreArgs a) {
+template <int C, int RB, bool CAUSAL, bool SELECT>
+__global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_kernel(ScoreArgs a, TileSelect sel) {
   using W = ScDma;
   static_assert(RB == 2 || RB == 4 || RB == 8 || RB == 16 || RB == 32, "r");
   __shared__ __attribute__((aligned(1024))) uint16_t st0[SD_STAGE];
@@ -528,6 +593,14 @@ __global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_ker
   vm_wait_barrier<0>();
   mma(st3);
   score_epilogue<RB, CAUSAL, W>(a, acc, tl.bh, tl.i0, tl.j0, wk, wq, l32, hh);
+#if !XATTN_SELECT_SORT
+  if constexpr (SELECT) {
+    static_assert(sizeof(SelectLdsT<SEL_MAX>) + sizeof(ScoreRowLds) <= sizeof(st0), "row state must fit a stage");
+    tile_select<RB, CAUSAL>(a, sel, tl.bh, tl.i0, st0, st1, (int)sizeof(st0));
+  }
+#else
+  (void)sel;
+#endif
 }
 
 // fp32 inputs: one thread per (strided row i, key block J), plain FMA.
@@ -591,7 +664,7 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
   const int rows = min(RB, a.Rq - I * RB);
   const float* L = a.ws + (bh * (size_t)a.NBq + I) * (size_t)a.NBk * RB;  // [J][t] of row I
   float* orow = a.out + row * a.NBk;
-  block_score_row<RB>(L, n_cand, a.NBk, rows, sh, [&](int J, float sc) { orow[J] = sc; });
+  block_score_row<RB>(L, n_cand, a.NBk, rows, sh, threadIdx.x, [&](int J, float sc) { orow[J] = sc; });
 }
 
 // ------------------------------------------------------------------ launchers
@@ -600,16 +673,35 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
 #define XATTN_SCORE_DMA 1
 #endif
 
+// The DMA kernel needs complete stride groups and a chunk count that is a
+// multiple of the ring's four stages.
+static bool dma_ok(const Shape& s) {
+  return XATTN_SCORE_DMA && s.M % s.stride == 0 && s.Mk % s.stride == 0 && (s.stride * s.C / SD_KC) % 4 == 0;
+}
+
 template <int C, int RB, bool TAIL>
-static hipError_t launch_partials_crt(const Shape& s, const ScoreArgs& a, hipStream_t st) {
+static hipError_t launch_partials_crt(const Shape& s, const ScoreArgs& a, const TileSelect* sel, hipStream_t st) {
   const unsigned grid = (unsigned)((size_t)s.B * s.Hq * a.pairs);
-  if (XATTN_SCORE_DMA && !TAIL && (s.stride * C / SD_KC) % 4 == 0) {
+  if (!TAIL && dma_ok(s)) {
+    static const TileSelect none{};
+    if (sel) {
+#if XATTN_SELECT_SORT
+      return hipErrorInvalidValue;
+#else
+      if (s.causal)
+        hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, true, true>), dim3(grid), dim3(ScDma::NT), 0, st, a, *sel);
+      else
+        hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, false, true>), dim3(grid), dim3(ScDma::NT), 0, st, a, *sel);
+      return hipGetLastError();
+#endif
+    }
     if (s.causal)
-      hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, true>), dim3(grid), dim3(ScDma::NT), 0, st, a);
+      hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, true, false>), dim3(grid), dim3(ScDma::NT), 0, st, a, none);
     else
-      hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, false>), dim3(grid), dim3(ScDma::NT), 0, st, a);
+      hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, false, false>), dim3(grid), dim3(ScDma::NT), 0, st, a, none);
     return hipGetLastError();
   }
+  if (sel) return hipErrorInvalidValue;
   if (s.causal)
     hipLaunchKernelGGL((score_partials_bf16_kernel<C, RB, true, TAIL>), dim3(grid), dim3(ScReg::NT), 0, st, a);
   else
@@ -618,24 +710,24 @@ static hipError_t launch_partials_crt(const Shape& s, const ScoreArgs& a, hipStr
 }
 
 template <int C, int RB>
-static hipError_t launch_partials_cr(const Shape& s, const ScoreArgs& a, hipStream_t st) {
-  return a.tail ? launch_partials_crt<C, RB, true>(s, a, st) : launch_partials_crt<C, RB, false>(s, a, st);
+static hipError_t launch_partials_cr(const Shape& s, const ScoreArgs& a, const TileSelect* sel, hipStream_t st) {
+  return a.tail ? launch_partials_crt<C, RB, true>(s, a, sel, st) : launch_partials_crt<C, RB, false>(s, a, sel, st);
 }
 
 template <int C>
-static hipError_t launch_partials_c(const Shape& s, const ScoreArgs& a, hipStream_t st) {
+static hipError_t launch_partials_c(const Shape& s, const ScoreArgs& a, const TileSelect* sel, hipStream_t st) {
   switch (s.r()) {
-    case 2: return launch_partials_cr<C, 2>(s, a, st);
-    case 4: return launch_partials_cr<C, 4>(s, a, st);
-    case 8: return launch_partials_cr<C, 8>(s, a, st);
-    case 16: return launch_partials_cr<C, 16>(s, a, st);
-    case 32: return launch_partials_cr<C, 32>(s, a, st);
+    case 2: return launch_partials_cr<C, 2>(s, a, sel, st);
+    case 4: return launch_partials_cr<C, 4>(s, a, sel, st);
+    case 8: return launch_partials_cr<C, 8>(s, a, sel, st);
+    case 16: return launch_partials_cr<C, 16>(s, a, sel, st);
+    case 32: return launch_partials_cr<C, 32>(s, a, sel, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
-                                      float score_scale, float* ws, hipStream_t st) {
+static hipError_t launch_partials(const Shape& s, const uint16_t* q, const uint16_t* k, float score_scale,
+                                  float* ws, const TileSelect* sel, hipStream_t st) {
   const int Rq = s.Rq(), Rk = s.Rk();
   const int Tq = (Rq + SC_TILE - 1) / SC_TILE, Tk = (Rk + SC_TILE - 1) / SC_TILE;
   const int qoff_s = (s.Mk - s.M) / s.stride;
@@ -648,9 +740,30 @@ hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const u
   const int tail = (s.M % s.stride) != 0 || (s.Mk % s.stride) != 0;
   ScoreArgs a{q, k, ws, s.B, s.Hq, s.Hkv, s.M, s.Mk, s.stride, Rq, Rk, s.NBq(), s.NBk(), qoff_s,
               s.diagonal, Tq, Tk, c0, pairs, tail, score_scale * kLog2e};
-  if (s.C == 128) return launch_partials_c<128>(s, a, st);
-  if (s.C == 64) return launch_partials_c<64>(s, a, st);
+  if (s.C == 128) return launch_partials_c<128>(s, a, sel, st);
+  if (s.C == 64) return launch_partials_c<64>(s, a, sel, st);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_score_partials_bf16(const Shape& s, const uint16_t* q, const uint16_t* k,
+                                      float score_scale, float* ws, hipStream_t st) {
+  return launch_partials(s, q, k, score_scale, ws, nullptr, st);
+}
+
+bool tile_select_ok(const Shape& s) {
+  const int r = s.r();
+  return !XATTN_SELECT_SORT && dma_ok(s) && (s.C == 64 || s.C == 128) && s.diagonal != 2 &&
+         s.selection != SEL_GLOBAL && (r == 2 || r == 4 || r == 8 || r == 16 || r == 32) && s.NBk() <= SEL_MAX;
+}
+
+size_t arrive_words(const Shape& s) {
+  return (size_t)s.B * s.Hq * (size_t)((s.Rq() + SC_TILE - 1) / SC_TILE);
+}
+
+hipError_t launch_score_tile_select(const Shape& s, const uint16_t* q, const uint16_t* k, float score_scale,
+                                    float* ws, const TileSelect& sel, hipStream_t st) {
+  if (!tile_select_ok(s) || !sel.arrive || !sel.kv_idx || !sel.kv_cnt) return hipErrorInvalidValue;
+  return launch_partials(s, q, k, score_scale, ws, &sel, st);
 }
 
 hipError_t launch_score_partials_f32(const Shape& s, const float* q, const float* k,

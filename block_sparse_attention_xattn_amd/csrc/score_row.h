@@ -7,8 +7,10 @@
 // candidates are J < n_cand.
 // lse_t = log2 sum_J 2^L[J][t]; score[J] = (1/rows) sum_{t<rows} 2^(L[J][t] - lse_t).
 // emit(J, score) is called once for every J in [0, NB) (0 for non-candidates),
-// from some thread of the workgroup. Needs 256 threads and the given LDS
-// scratch; callers synchronise before reading what emit wrote.
+// from some thread of the group. Runs on a group of 256 threads, `tid` being
+// the thread's index in it (a 512-thread workgroup may run two rows at once);
+// needs the given LDS scratch and passes two workgroup barriers in either
+// form; callers synchronise before reading what emit wrote.
 #pragma once
 
 #include "common.h"
@@ -26,8 +28,8 @@ struct ScoreRowLds {
 // across the wave and the four waves.
 template <int RB, class Emit>
 __device__ __forceinline__ void block_score_row_long(const float* L, int n_cand, int NB, int rows,
-                                                ScoreRowLds& sh, Emit&& emit) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+                                                ScoreRowLds& sh, int tid, Emit&& emit) {
+  const int lane = tid & 63, wave = tid >> 6;
   // pass 1: per strided row t, log2-sum-exp over candidate blocks
   float m[RB], s[RB];
 #pragma unroll
@@ -103,10 +105,10 @@ __device__ __forceinline__ void block_score_row_long(const float* L, int n_cand,
 // 2^(x - max), and the block sums over t run over RB adjacent lanes.
 template <int RB, class Emit>
 __device__ __forceinline__ void block_score_row_short(const float* L, int n_cand, int NB, int rows,
-                                                      ScoreRowLds& sh, Emit&& emit) {
+                                                      ScoreRowLds& sh, int tid, Emit&& emit) {
   static_assert(RB >= 2 && RB <= 32 && (RB & (RB - 1)) == 0, "RB");
   constexpr int JL = 256 / RB;  // key-block lanes
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = tid >> 6;
   const int t = tid % RB, jl = tid / RB;
   const bool live = t < rows;  // rows past the end were never written
   // pass 1: lse_t = log2 sum_J 2^L[J][t], as a max then a sum of 2^(x - max)
@@ -148,11 +150,11 @@ constexpr int kScoreRowShortMax = 256;
 
 template <int RB, class Emit>
 __device__ __forceinline__ void block_score_row(const float* L, int n_cand, int NB, int rows,
-                                                ScoreRowLds& sh, Emit&& emit) {
+                                                ScoreRowLds& sh, int tid, Emit&& emit) {
   if (n_cand <= kScoreRowShortMax)
-    block_score_row_short<RB>(L, n_cand, NB, rows, sh, emit);
+    block_score_row_short<RB>(L, n_cand, NB, rows, sh, tid, emit);
   else
-    block_score_row_long<RB>(L, n_cand, NB, rows, sh, emit);
+    block_score_row_long<RB>(L, n_cand, NB, rows, sh, tid, emit);
 }
 
 }  // namespace xattn

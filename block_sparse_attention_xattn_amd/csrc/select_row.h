@@ -1,0 +1,226 @@
+// Minimal-set selection of one query-block row by a group of 256 threads,
+// shared by the selection kernels and the scoring kernel that selects each
+// query tile's rows as soon as the tile's last partials are written.
+//
+// Definition (XAttention AI summary, "Approach": keep the minimal set of
+// blocks whose softmax-normalised mass exceeds the per-head threshold;
+// FlexPrefill rebuttal, "R Q3": the minimal |S| under a cumulative-mass
+// constraint is the descending-order prefix that first meets it):
+//   candidates J <= I (causal) or all J; order by score descending, ties by J
+//   ascending; prefix masses c_k in float64, T = c_n; keep the first
+//   k* = min{k >= 0 : c_k >= tau * T} (tau >= 1 keeps all); then add J = I.
+//
+// Implementation: a radix select of the cut, no sort. The kept set is the
+// prefix of the (score desc, J asc) order that first reaches tau * T, so it is
+// every candidate scoring above the cut score v* plus the first t* (by J) of
+// those scoring exactly v*, where v* is the largest score whose tail mass
+// F(v*) = mass(score >= v*) reaches tau * T. Block scores are non-negative, so
+// their IEEE bits order like the values: four passes over 8-bit digits of the
+// bits (most significant first) histogram the candidate mass per digit within
+// the digits chosen so far, and pick the digit where the mass counted from the
+// top first reaches tau * T. Masses are 64-bit fixed-point integers (score *
+// 2^50), so the sums are exact and independent of the order of the atomic
+// adds; they differ from float64 prefix sums by at most about 1e-12 of the row
+// total, so a decision can differ only for a block whose cumulative mass lies
+// that close to tau * T. Then t* = ceil((tau*T - mass above v*) / v*), the ties
+// ranked by a scan over J, flags, and an ascending compaction.
+// Build option XATTN_SELECT_SORT=1 (selection kernels only): a bitonic sort of
+// (score bits << 32 | ~J) keys with float64 prefix sums instead.
+//
+// Thread index: `tid` in [0, 256) is the thread's index within its group, so a
+// 512-thread workgroup can run two rows at once, one per half. The number of
+// workgroup barriers a row takes depends only on whether tau >= 1 (a per-head
+// value), never on the data, so two halves selecting rows of one head pass
+// their barriers in step.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace xattn {
+
+constexpr int SEL_MAX = 4096;
+
+#ifndef XATTN_SELECT_SORT
+#define XATTN_SELECT_SORT 0
+#endif
+
+__device__ __forceinline__ double wave_incl_scan(double x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan_i(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Per-row selection state for rows of up to CAP candidate blocks. Layers of
+// at most 2048 key blocks use the small form: about 13 KiB instead of 24, so
+// registers (7 workgroups of 256 threads per CU) rather than LDS (6) cap the
+// rows in flight, and the latency-bound selection runs more of them at once.
+template <int CAP>
+struct SelectLdsT {
+#if XATTN_SELECT_SORT
+  uint64_t keys[CAP];
+#else
+  float sc[CAP];                  // candidate scores by J
+  unsigned long long hist[256];   // fixed-point mass per digit
+  unsigned int hcnt[256];         // candidates per digit (last pass)
+  unsigned long long wsum64[4];
+  unsigned int cut[2];            // digits chosen so far; tie count
+  unsigned long long cut_above;   // mass above the digits chosen so far
+#endif
+  uint8_t flags[CAP];
+  double wsum[4];
+  int wcnt[4];
+};
+using SelectLds = SelectLdsT<SEL_MAX>;
+// the small form, where the sort option (which needs power-of-two padding up
+// to SEL_MAX keys) is off
+constexpr int SEL_SMALL = XATTN_SELECT_SORT ? SEL_MAX : 2048;
+
+// Writes one row from its keep flags (flags[0, NB), visible to every thread of
+// the group): the mask row (if requested), the kept J in ascending order, and
+// the count. wcnt is 4 ints of LDS scratch. Two barriers.
+__device__ inline void compact_row(int tid, const uint8_t* flags, int NB, size_t row, uint8_t* mask,
+                                   int32_t* kv_idx, int32_t* kv_cnt, int* wcnt) {
+  const int lane = tid & 63, wave = tid >> 6;
+  if (mask) {
+    uint8_t* mrow = mask + row * NB;
+    for (int p = tid; p < NB; p += 256) mrow[p] = flags[p];
+  }
+  // ascending compaction: per-thread contiguous runs of J
+  const int per = (NB + 255) / 256;
+  const int p0 = tid * per, p1 = min(p0 + per, NB);
+  int mine = 0;
+  for (int p = p0; p < p1; ++p) mine += flags[p];
+  const int incl = wave_incl_scan_i(mine, lane);
+  __syncthreads();  // wcnt may still be read by the caller's last step
+  if (lane == 63) wcnt[wave] = incl;
+  __syncthreads();
+  int pos = incl - mine;
+  for (int w = 0; w < wave; ++w) pos += wcnt[w];
+  int32_t* irow = kv_idx + row * NB;
+  for (int p = p0; p < p1; ++p)
+    if (flags[p]) irow[pos++] = p;
+  if (tid == 0) kv_cnt[row] = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+}
+
+#if !XATTN_SELECT_SORT
+__device__ __forceinline__ unsigned long long sel_fx(float s) {
+  return __double2ull_rz((double)s * 0x1p50);  // scores are in [0, 1]
+}
+
+// Inclusive scan of a 64-bit value over the group's 256 threads; every thread
+// also gets the total. Two barriers; wsum may be reused afterwards.
+__device__ __forceinline__ unsigned long long block_scan_u64(int tid, unsigned long long x,
+                                                             unsigned long long* wsum,
+                                                             unsigned long long& total) {
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) x += wsum[w];
+  total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+  __syncthreads();
+  return x;
+}
+
+// With sc[0, n) filled, flags[0, NB) zeroed and a barrier passed: find the
+// cut, set the kept flags, add the diagonal, write the row. Barriers: 3 when
+// tau >= 1, else 24, whatever the scores.
+template <class SL>
+__device__ void select_radix(SL& sh, int tid, int n, int NB, int I, float tau, size_t row, uint8_t* mask,
+                             int32_t* kv_idx, int32_t* kv_cnt) {
+  const int lane = tid & 63, wave = tid >> 6;
+  uint8_t* flags = sh.flags;
+  if (tau >= 1.f) {
+    for (int p = tid; p < n; p += 256) flags[p] = 1;
+  } else {
+    unsigned long long thr = 0;  // ceil(tau * T) in fixed point
+    unsigned int prefix = 0;
+    unsigned long long above = 0;
+    bool none = false;  // tau * T <= 0: no candidate is kept (the passes still run, idle)
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      sh.hist[tid] = 0ull;
+      sh.hcnt[tid] = 0u;
+      __syncthreads();
+      if (!none) {
+        for (int p = tid; p < n; p += 256) {
+          const float v = sh.sc[p];
+          const unsigned int u = __float_as_uint(v);
+          if (pass == 0 || (u >> (shift + 8)) == prefix) {
+            const int d = (u >> shift) & 255;
+            atomicAdd(&sh.hist[d], sel_fx(v));
+            if (pass == 3) atomicAdd(&sh.hcnt[d], 1u);
+          }
+        }
+      }
+      __syncthreads();
+      // thread t holds digit 255 - t: the inclusive scan is the mass of the
+      // digits from the top down to this one
+      const int d = 255 - tid;
+      const unsigned long long h = sh.hist[d];
+      unsigned long long total;
+      const unsigned long long incl = block_scan_u64(tid, h, sh.wsum64, total);
+      if (pass == 0) {
+        // total = T; tau * T <= 0 keeps no candidate
+        thr = (unsigned long long)ceil((double)tau * (double)total);
+        none = tau <= 0.f || total == 0ull || thr == 0ull;
+      }
+      if (!none && above + incl >= thr && above + incl - h < thr) {
+        sh.cut[0] = (prefix << 8) | (unsigned int)d;
+        sh.cut_above = above + incl - h;
+        if (pass == 3) sh.cut[1] = sh.hcnt[d];
+      }
+      __syncthreads();
+      prefix = sh.cut[0];
+      above = sh.cut_above;
+    }
+    // v* = prefix; keep the first t* ties by J
+    const int per = (n + 255) / 256;
+    const int p0 = min(tid * per, n), p1 = min(p0 + per, n);
+    int mine = 0;
+    if (!none)
+      for (int p = p0; p < p1; ++p) mine += __float_as_uint(sh.sc[p]) == prefix;
+    const int incl_t = wave_incl_scan_i(mine, lane);
+    if (lane == 63) sh.wcnt[wave] = incl_t;
+    __syncthreads();
+    if (!none) {
+      const unsigned long long fv = sel_fx(__uint_as_float(prefix));
+      const unsigned int ties = sh.cut[1];
+      const unsigned long long need = thr - above;  // > 0
+      unsigned int tstar = fv ? (unsigned int)((need + fv - 1) / fv) : ties;
+      tstar = tstar > ties ? ties : tstar;
+      int rank = incl_t - mine;
+      for (int w = 0; w < wave; ++w) rank += sh.wcnt[w];
+      // only ever set flags (they start zeroed): the diagonal's flag, set by
+      // thread 0 without a barrier, must not be cleared by the thread that
+      // owns it as an unkept tie
+      for (int p = p0; p < p1; ++p) {
+        const unsigned int u = __float_as_uint(sh.sc[p]);
+        if (u > prefix || (u == prefix && (unsigned int)(rank++) < tstar)) flags[p] = 1;
+      }
+    }
+  }
+  if (tid == 0) flags[I] = 1;  // diagonal block
+  __syncthreads();
+  compact_row(tid, flags, NB, row, mask, kv_idx, kv_cnt, sh.wcnt);
+}
+#endif
+
+}  // namespace xattn

@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define XATTN_ABI_VERSION 4
+#define XATTN_ABI_VERSION 5
 #define XATTN_MAX_HEADS 256
 #define XATTN_MAX_BLOCKS 4096
 /* XATTN_F32 problems run scalar fp32 kernels (reference precision for small
@@ -111,7 +111,22 @@ typedef struct {
   int32_t pattern; /* xattn_pattern of the strided scoring (0 = antidiagonal) */
   int32_t selection; /* xattn_selection of the block selection (0 = per row) */
   int32_t Mk;     /* key length; 0 means M. Mk - M is a multiple of block */
+  int32_t flags;  /* xattn_flags, OR-ed; 0 = the defaults */
 } xattn_problem;
+
+/* Options of xattn_problem.flags (unknown bits return XATTN_ERR_ARG):
+ *  SELECT_IN_SCORE: xattn_prefill normalises and selects inside the scoring
+ *  launch ([XA-sum] Approach runs the three steps back to back; here the
+ *  workgroup that stores a query tile's last partials selects that tile's
+ *  rows at once), one launch fewer per call, with block scores, masks, lists
+ *  and output bit-identical to the default. It applies where the scoring
+ *  streams whole stride groups (bf16, M and Mk multiples of S, S*C a multiple
+ *  of 128, antidiagonal or diagonal pattern, per-row or GQA-union selection)
+ *  and is ignored elsewhere. On MI355X it is slower than the default separate
+ *  selection launch: the scoring kernel holds a whole compute unit, which then
+ *  idles its matrix cores through the latency-bound selection, while the
+ *  separate launch overlaps seven selections per compute unit. */
+typedef enum { XATTN_SELECT_IN_SCORE = 1 } xattn_flags;
 
 /* How the strided scoring forms its logits:
  *  ANTIDIAGONAL (the method, [XA-abs]): query row i*S+s with key row j*S+S-1-s,
@@ -258,8 +273,9 @@ xattn_status dense_fwd(const xattn_problem* p, const void* q, const void* k,
                        void* stream);
 
 /* Device workspace bytes xattn_prefill needs: the score partials, the
- * selection scratch and the attention queues, each part starting on a
- * 256-byte boundary; 0 if p is invalid. */
+ * selection scratch, the per-(b, h, query tile) arrival counters when
+ * XATTN_SELECT_IN_SCORE applies, and the attention queues, each part starting
+ * on a 256-byte boundary; 0 if p is invalid. */
 size_t xattn_prefill_workspace_bytes(const xattn_problem* p);
 
 /*

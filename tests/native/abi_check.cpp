@@ -28,6 +28,7 @@ static xattn_problem base() {
   std::memset(&p, 0, sizeof(p));
   p.B = 1; p.Hq = 4; p.Hkv = 2; p.M = 1024; p.C = 128; p.block = 128; p.stride = 8;
   p.causal = 1; p.dtype = XATTN_BF16; p.pattern = XATTN_ANTIDIAGONAL; p.selection = XATTN_SELECT_ROW; p.Mk = 0;
+  p.flags = 0;
   return p;
 }
 
@@ -58,6 +59,8 @@ int main() {
       {"causal flag", [](xattn_problem& p) { p.causal = 2; }, XATTN_ERR_ARG},
       {"pattern", [](xattn_problem& p) { p.pattern = 3; }, XATTN_ERR_ARG},
       {"selection", [](xattn_problem& p) { p.selection = -1; }, XATTN_ERR_ARG},
+      {"unknown flag bit", [](xattn_problem& p) { p.flags = 2; }, XATTN_ERR_ARG},
+      {"negative flags", [](xattn_problem& p) { p.flags = -1; }, XATTN_ERR_ARG},
       {"too many heads", [](xattn_problem& p) { p.Hq = 512; p.Hkv = 1; }, XATTN_ERR_UNSUPPORTED},
       {"too many key blocks", [](xattn_problem& p) { p.M = 4096 * 128 + 128; }, XATTN_ERR_UNSUPPORTED},
       {"int32 extremes", [](xattn_problem& p) { p.B = 2147483647; p.Hq = 256; p.Hkv = 1; p.M = 2147483647 / 2048 * 128; }, XATTN_ERR_UNSUPPORTED},

@@ -37,7 +37,7 @@ def test_every_declared_symbol_is_exported(xa):
 
 
 def test_version_and_strings(xa):
-    assert xa._lib.xattn_abi_version() == 4
+    assert xa._lib.xattn_abi_version() == 5
     for s in range(8):
         assert xa._lib.xattn_status_string(s)
     assert xa._lib.xattn_status_string(99) == b"unknown status"
@@ -45,10 +45,10 @@ def test_version_and_strings(xa):
 
 def _p(xa, **kw):
     base = dict(B=1, Hq=4, Hkv=2, M=1024, C=128, block=128, stride=8, causal=1, dtype=0, pattern=0,
-                selection=0, Mk=0)
+                selection=0, Mk=0, flags=0)
     base.update(kw)
     return xa.Problem(*[base[k] for k in ("B", "Hq", "Hkv", "M", "C", "block", "stride", "causal", "dtype",
-                                          "pattern", "selection", "Mk")])
+                                          "pattern", "selection", "Mk", "flags")])
 
 
 FAKE = 0x1000  # never dereferenced: validation fails first
@@ -62,6 +62,8 @@ FAKE = 0x1000  # never dereferenced: validation fails first
     # DuSA1 scoring: bf16 only, lengths multiples of the stride
     (dict(pattern=2, dtype=1), 5), (dict(pattern=2, M=1004), 2), (dict(pattern=2, M=1024, Mk=1540), 2),
     (dict(selection=3), 4), (dict(selection=-1), 4), (dict(Mk=4096 * 128 + 128), 5),
+    # only xattn_flags bits
+    (dict(flags=2), 4), (dict(flags=-1), 4),
     # empty problems are errors, not silent no-ops
     (dict(M=0), 2), (dict(Hq=0), 2), (dict(Hkv=0), 2), (dict(C=0), 2), (dict(block=0), 2),
     (dict(stride=0), 2), (dict(M=-5), 2),
@@ -96,6 +98,14 @@ def test_workspace_bytes(xa):
     odd = _p(xa, B=1, Hq=1, Hkv=1, M=192, block=64, stride=32, C=64)   # 3 * 6 * 4 = 72 bytes
     assert xa.workspace_bytes(odd) == 72
     assert xa.prefill_workspace_bytes(odd) == 256 + 1024
+    # selection inside the scoring launch adds one arrival counter per
+    # (b, h, 256-row query tile) before the queues, where it applies
+    assert xa.prefill_workspace_bytes(_p(xa, flags=1)) == 1 * 4 * 8 * 128 * 4 + 256 + 1024
+    assert xa.prefill_workspace_bytes(_p(xa, flags=1, M=1004)) == xa.prefill_workspace_bytes(_p(xa, M=1004))
+    assert xa.prefill_workspace_bytes(_p(xa, flags=1, dtype=1)) == xa.prefill_workspace_bytes(_p(xa, dtype=1))
+    assert xa.prefill_workspace_bytes(_p(xa, flags=1, selection=1)) == xa.prefill_workspace_bytes(g := _p(xa, selection=1))
+    assert xa.prefill_workspace_bytes(_p(xa, flags=1, B=2, Hq=8, M=8192)) == \
+        xa.prefill_workspace_bytes(_p(xa, B=2, Hq=8, M=8192)) + 256
     assert xa.prefill_workspace_bytes(_p(xa, stride=0)) == 0
     # selection scratch: none per row or for the GQA union; per head a 64-byte
     # state, a 4096-bucket histogram (8 + 4 bytes each) and NB words for global

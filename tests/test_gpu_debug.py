@@ -1,7 +1,7 @@
 """The debug build (libxattn_debug.so, -DXATTN_DEBUG=1): the kernels' bounds
 checks at every indexing site stay at zero failures over layers that reach each
-kernel and mode (per-row, global and GQA-union selection; antidiagonal and
-DuSA1 scoring; single, sibling and row-pair attention; ragged and chunked
+kernel and mode (per-row, global and GQA-union selection, selection inside the
+scoring launch; antidiagonal and DuSA1 scoring; single, sibling and row-pair attention; ragged and chunked
 lengths; dense attention), and the debug build's outputs equal the release
 build's bitwise (the checks only count, they change no value)."""
 import ctypes
@@ -54,6 +54,7 @@ CASES = [
     ("llama8k-global", dict(M=4096, Hq=4, Hkv=2), dict(selection="global")),
     ("llama8k-gqa-union", dict(M=4096, Hq=4, Hkv=2), dict(selection="gqa_union")),
     ("llama32k-dusa1", dict(M=4096, Hq=4, Hkv=1), dict(pattern=2)),
+    ("llama32k-select-in-score", dict(M=4096, Hq=8, Hkv=2), dict(select_in_score=True)),
     ("ragged-3000", dict(M=3000, Hq=4, Hkv=2), {}),
 ]
 
