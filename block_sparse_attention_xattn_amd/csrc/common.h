@@ -114,6 +114,38 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return __builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11)) & 7u;
 }
 
+// LDS byte address of a pointer into a __shared__ array, made wave-uniform.
+__device__ __forceinline__ uint32_t lds_addr_u(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+
+// A 64-bit pointer that is the same in every lane, in scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// DMA of 16 bytes per lane from global memory (wave-uniform base plus a
+// per-lane byte offset) straight into LDS: the 64 lanes fill the 1 KiB at
+// lds_base in lane order. Written as asm so the compiler, which would treat
+// every LDS read after such a load as dependent on it, adds no waits of its
+// own: the loop that issues these waits for them explicitly (vm_wait) before
+// the barrier that publishes the data. It has no register results.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base), "s"(lds_base) : "memory", "m0");
+}
+
+// Waits until at most N vector-memory loads of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
 // s_waitcnt immediate that waits on the vector-memory counter only: at most n
 // loads (including LDS DMA) of this wave outstanding.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }

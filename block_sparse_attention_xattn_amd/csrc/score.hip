@@ -32,6 +32,7 @@
 // K~' row j, element e is k[j*S + S-1 - e/C][e%C] — the stride group read in
 // reverse, so the reversal costs only address arithmetic.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -573,25 +574,113 @@ __global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_ker
     __builtin_amdgcn_sched_barrier(0);  // keep the refill ahead of this chunk's work
     mma(cur);
   };
-  issue(0, st0);
-  issue(1, st1);
-  issue(2, st2);
-  // n_chunks is a multiple of 4, at least 4 (checked by the launcher); the
-  // last group refills only its first step's stage, and its waits count down
-  // as fewer chunks remain in flight
-  for (int c = 0; c < n_chunks - 4; c += 4) {
-    step(c, st0, st3);
-    step(c + 1, st1, st0);
-    step(c + 2, st2, st1);
-    step(c + 3, st3, st2);
+  if constexpr (W::MINW == 1) {
+    // One wave per SIMD (128 x 128 wave tiles): no second wave hides the
+    // fragment reads, so the loop is software-pipelined by hand. The fragments
+    // of k-step 1 of chunk c are read while the MFMAs of its k-step 0 run;
+    // then the barrier (chunk c+1 landed, every wave done with chunk c's
+    // stage), the reads of chunk c+1's k-step 0, and the MFMAs of k-step 1
+    // with the refill of chunk c's stage (chunk c+4) issued between them. The
+    // ring holds chunk c and three ahead.
+    bf16x8 fa0[W::MTK], fb0[W::MTQ], fa1[W::MTK], fb1[W::MTQ];
+    auto frags = [&](const uint16_t* stg, int ks, bf16x8 (&af)[W::MTK], bf16x8 (&bq)[W::MTQ]) {
+#pragma unroll
+      for (int x = 0; x < W::MTK; ++x)
+        af[x] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stg + sd_off(W::WK * wk + 32 * x + l32, 2 * ks + hh)));
+#pragma unroll
+      for (int y = 0; y < W::MTQ; ++y)
+        bq[y] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(stg + SC_TILE * SD_ROW +
+                                                                          sd_off(W::WQ * wq + 32 * y + l32, 2 * ks + hh)));
+    };
+    // DMA piece p of chunk c: p < SD_BPW a key block, else a query block
+    auto piece = [&](int c, uint16_t* stg, int p) {
+      const int srow = (SD_KC * c) / C, col0 = (SD_KC * c) % C;
+      const int u = p % SD_BPW, blk = wave + (W::NT / 64) * u;
+      if (p < SD_BPW)
+        __builtin_amdgcn_global_load_lds(kp[u] + ((ptrdiff_t)kdir * srow * C + col0),
+                                         (__attribute__((address_space(3))) void*)(stg + blk * 1024 / 2), 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(qp[u] + ((ptrdiff_t)srow * C + col0),
+                                         (__attribute__((address_space(3))) void*)(stg + SC_TILE * SD_ROW + blk * 1024 / 2),
+                                         16, 0, 0);
+    };
+    constexpr int NM = W::MTK * W::MTQ;            // MFMAs per k-step
+    constexpr int PER = NM / (2 * SD_BPW);         // MFMAs per DMA piece
+    static_assert(PER >= 1 && PER * 2 * SD_BPW == NM, "DMA pieces must spread over the k-step's MFMAs");
+    // WAITN: chunks that may still be in flight once chunk c+1 has landed;
+    // REFILL: chunk c+4 exists; NEXT: chunk c+1 exists
+    auto iter = [&](auto waitn, auto refill, auto next, int c, const uint16_t* cur, const uint16_t* nxt,
+                    uint16_t* cur_w) {
+      // the reads of k-step 1 go out after the first MFMAs of k-step 0: issued
+      // first, they would be waited for with k-step 0's (the LDS counter is
+      // waited to zero before the first use)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        acc[m / W::MTQ][m % W::MTQ] = mfma32x32x16(fa0[m / W::MTQ], fb0[m % W::MTQ], acc[m / W::MTQ][m % W::MTQ]);
+        if (m == W::MTQ - 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          frags(cur, 1, fa1, fb1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (decltype(next)::value) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of chunk c are done
+        vm_wait_barrier<decltype(waitn)::value * 2 * SD_BPW>();
+        frags(nxt, 0, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int m = 0; m < NM; ++m) {
+        acc[m / W::MTQ][m % W::MTQ] = mfma32x32x16(fa1[m / W::MTQ], fb1[m % W::MTQ], acc[m / W::MTQ][m % W::MTQ]);
+        if constexpr (decltype(refill)::value) {
+          if (m % PER == PER - 1) piece(c + 4, cur_w, m / PER);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using T = std::true_type;
+    using F = std::false_type;
+    issue(0, st0);
+    issue(1, st1);
+    issue(2, st2);
+    issue(3, st3);
+    vm_wait_barrier<3 * 2 * SD_BPW>();  // chunk 0 landed; 1, 2, 3 may be in flight
+    frags(st0, 0, fa0, fb0);
+    for (int c = 0; c < n_chunks - 4; c += 4) {
+      iter(I2{}, T{}, T{}, c, st0, st1, st0);
+      iter(I2{}, T{}, T{}, c + 1, st1, st2, st1);
+      iter(I2{}, T{}, T{}, c + 2, st2, st3, st2);
+      iter(I2{}, T{}, T{}, c + 3, st3, st0, st3);
+    }
+    iter(I2{}, F{}, T{}, n_chunks - 4, st0, st1, st0);
+    iter(I1{}, F{}, T{}, n_chunks - 3, st1, st2, st1);
+    iter(I0{}, F{}, T{}, n_chunks - 2, st2, st3, st2);
+    iter(I0{}, F{}, F{}, n_chunks - 1, st3, st3, st3);
+  } else {
+    issue(0, st0);
+    issue(1, st1);
+    issue(2, st2);
+    // n_chunks is a multiple of 4, at least 4 (checked by the launcher); the
+    // last group refills only its first step's stage, and its waits count down
+    // as fewer chunks remain in flight
+    for (int c = 0; c < n_chunks - 4; c += 4) {
+      step(c, st0, st3);
+      step(c + 1, st1, st0);
+      step(c + 2, st2, st1);
+      step(c + 3, st3, st2);
+    }
+    step(n_chunks - 4, st0, st3);
+    vm_wait_barrier<2 * 2 * SD_BPW>();  // chunks n-2, n-1 may be in flight
+    mma(st1);
+    vm_wait_barrier<1 * 2 * SD_BPW>();  // chunk n-1 may be in flight
+    mma(st2);
+    vm_wait_barrier<0>();
+    mma(st3);
   }
-  step(n_chunks - 4, st0, st3);
-  vm_wait_barrier<2 * 2 * SD_BPW>();  // chunks n-2, n-1 may be in flight
-  mma(st1);
-  vm_wait_barrier<1 * 2 * SD_BPW>();  // chunk n-1 may be in flight
-  mma(st2);
-  vm_wait_barrier<0>();
-  mma(st3);
   score_epilogue<RB, CAUSAL, W>(a, acc, tl.bh, tl.i0, tl.j0, wk, wq, l32, hh);
 #if !XATTN_SELECT_SORT
   if constexpr (SELECT) {
