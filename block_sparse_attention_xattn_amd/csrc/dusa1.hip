@@ -50,10 +50,15 @@ struct Dusa1Args {
   float sl2;            // score_scale * log2(e)
 };
 
-constexpr int D1_RPW = 64;             // strided query rows per wave (two 32-row MFMA tiles)
-constexpr int D1_NW = 8;               // waves per workgroup
+#ifndef XATTN_D1_RPW
+#define XATTN_D1_RPW 32
+#endif
+constexpr int D1_QR = 512;             // strided query rows per workgroup
+constexpr int D1_RPW = XATTN_D1_RPW;   // ... per wave: 64 (two 32-row MFMA tiles) or 32
+constexpr int D1_QTW = D1_RPW / 32;    // 32-row MFMA tiles per wave
+constexpr int D1_NW = D1_QR / D1_RPW;  // waves per workgroup
 constexpr int D1_NT = 64 * D1_NW;      // threads per workgroup
-constexpr int D1_QR = D1_RPW * D1_NW;  // strided query rows per workgroup
+static_assert(D1_RPW == 32 || D1_RPW == 64, "rows per wave");
 constexpr int D1_KT = 64;              // strided keys per K tile
 constexpr int D1_RING = 4;             // K tiles in the LDS ring
 
@@ -67,7 +72,7 @@ struct D1Lds {
   static constexpr int TILE_B = D1_KT * ROW_B;         // bytes per K tile
   static constexpr int ROWS_PER_256 = 256 / ROW_B;
   static constexpr int BLKS = TILE_B / 1024;           // 1 KiB DMA blocks per tile
-  static constexpr int BPW = BLKS / D1_NW;             // ... per wave
+  static constexpr int BPW = BLKS >= D1_NW ? BLKS / D1_NW : 1;  // ... per wave (waves past BLKS issue none)
   static constexpr int RPB = 1024 / ROW_B;             // key rows per DMA block
   static constexpr int LPR = ROW_B / 16;               // lanes per key row in a DMA block
   // byte offset of 16-byte chunk `chunk` of key row `row`
@@ -75,35 +80,60 @@ struct D1Lds {
     return row * ROW_B + 16 * (chunk ^ ((row / ROWS_PER_256) % (C / 8)));
   }
 };
-static_assert(D1Lds<128>::BPW == 2 && D1Lds<64>::BPW == 1, "DMA blocks per wave");
+static_assert(D1Lds<128>::BPW * D1_NW >= D1Lds<128>::BLKS && D1Lds<64>::BPW * D1_NW >= D1Lds<64>::BLKS,
+              "DMA blocks per wave");
 
 // DMA of K tile (phase s, strided keys j0 .. j0+63) into ring slot `slot`:
 // this wave's BPW blocks; lane L of block b fills key row b*RPB + L/LPR at slot
-// L%LPR, i.e. the row's chunk (L%LPR) ^ swizzle. Keys past Rk load key Rk - 1
-// (masked by the caller).
+// L%LPR, i.e. the row's chunk (L%LPR) ^ swizzle. The per-lane byte offsets
+// within a tile are fixed, so a whole tile costs a scalar base; only a tile
+// that runs past Rk clamps its keys (to key Rk - 1, masked by the caller).
 template <int C>
-__device__ __forceinline__ void d1_dma(const Dusa1Args& a, const void* kh_u, unsigned char* ring, int slot, int s,
-                                       int j0, int wave, int lane) {
+struct D1Dma {
   using L = D1Lds<C>;
+  uint32_t voff[L::BPW];  // key row * S * 2C + 16 * chunk
+  int row[L::BPW], chunk[L::BPW];
+  int wave, S;
+  __device__ D1Dma(int wave_, int lane, int S_) : wave(wave_), S(S_) {
 #pragma unroll
-  for (int u = 0; u < L::BPW; ++u) {
-    const int b = wave * L::BPW + u;
-    const int row = b * L::RPB + lane / L::LPR;
-    const int c = (lane % L::LPR) ^ ((row / L::ROWS_PER_256) % (C / 8));
-    const int j = min(j0 + row, a.Rk - 1);
-    const size_t byte = (((size_t)j * a.S + s) * C + 8 * c) * 2;
-    XATTN_DCHECK(slot >= 0 && slot < D1_RING && byte < ((size_t)1 << 32), DBG_DUSA1_INDEX);
-    dma16(kh_u, (uint32_t)byte, lds_addr_u(ring + slot * L::TILE_B + b * 1024));
+    for (int u = 0; u < L::BPW; ++u) {
+      const int b = wave * L::BPW + u;
+      row[u] = b * L::RPB + lane / L::LPR;
+      chunk[u] = (lane % L::LPR) ^ ((row[u] / L::ROWS_PER_256) % (C / 8));
+      voff[u] = (uint32_t)((row[u] * S * C + 8 * chunk[u]) * 2);
+    }
   }
-}
+  __device__ void issue(const Dusa1Args& a, const uint16_t* kh, unsigned char* ring, int slot, int s, int j0) const {
+    unsigned char* tile = ring + slot * L::TILE_B;
+    XATTN_DCHECK(slot >= 0 && slot < D1_RING, DBG_DUSA1_INDEX);
+    if (j0 + D1_KT <= a.Rk) {
+      const void* base = uniform_ptr(kh + ((size_t)j0 * S + s) * C);
+#pragma unroll
+      for (int u = 0; u < L::BPW; ++u) {
+        const int b = wave * L::BPW + u;
+        if (b < L::BLKS) dma16(base, voff[u], lds_addr_u(tile + b * 1024));  // wave-uniform
+      }
+    } else {
+      const void* base = uniform_ptr(kh);
+#pragma unroll
+      for (int u = 0; u < L::BPW; ++u) {
+        const int b = wave * L::BPW + u;
+        const int j = min(j0 + row[u], a.Rk - 1);
+        const size_t byte = (((size_t)j * S + s) * C + 8 * chunk[u]) * 2;
+        XATTN_DCHECK(byte < ((size_t)1 << 32), DBG_DUSA1_INDEX);
+        if (b < L::BLKS) dma16(base, (uint32_t)byte, lds_addr_u(tile + b * 1024));
+      }
+    }
+  }
+};
 
-// Q fragments (B operand) of this wave's 64 strided rows of phase s:
+// Q fragments (B operand) of this wave's strided rows of phase s:
 // row i0 + 32y + l32 -> token (i0 + 32y + l32) * S + s; rows past Rq read row Rq - 1.
 template <int C>
 __device__ __forceinline__ void d1_load_q(const Dusa1Args& a, const uint16_t* qh, int i0, int s, int l32, int hh,
-                                          bf16x8 (&qf)[2][C / 16]) {
+                                          bf16x8 (&qf)[D1_QTW][C / 16]) {
 #pragma unroll
-  for (int y = 0; y < 2; ++y) {
+  for (int y = 0; y < D1_QTW; ++y) {
     const int i = min(i0 + 32 * y + l32, a.Rq - 1);
     const uint16_t* row = qh + ((size_t)i * a.S + s) * C + 8 * hh;
 #pragma unroll
@@ -115,20 +145,20 @@ __device__ __forceinline__ void d1_load_q(const Dusa1Args& a, const uint16_t* qh
 // S^T of a K tile (in LDS) against the wave's rows: acc[n][y][r] = logit of
 // key 32n + 8(r/4) + 4hh + r%4 of the tile and query row i0 + 32y + l32.
 template <int C>
-__device__ __forceinline__ void d1_mma(const unsigned char* kt, const bf16x8 (&qf)[2][C / 16], f32x16 (&acc)[2][2],
+__device__ __forceinline__ void d1_mma(const unsigned char* kt, const bf16x8 (&qf)[D1_QTW][C / 16], f32x16 (&acc)[2][D1_QTW],
                                        int l32, int hh) {
   using L = D1Lds<C>;
 #pragma unroll
   for (int n = 0; n < 2; ++n)
 #pragma unroll
-    for (int y = 0; y < 2; ++y) acc[n][y] = f32x16{};
+    for (int y = 0; y < D1_QTW; ++y) acc[n][y] = f32x16{};
 #pragma unroll
   for (int kk = 0; kk < C / 16; ++kk)
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const bf16x8 kf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kt + L::off(32 * n + l32, 2 * kk + hh)));
 #pragma unroll
-      for (int y = 0; y < 2; ++y) acc[n][y] = mfma32x32x16(kf, qf[y][kk], acc[n][y]);
+      for (int y = 0; y < D1_QTW; ++y) acc[n][y] = mfma32x32x16(kf, qf[y][kk], acc[n][y]);
     }
 }
 
@@ -149,56 +179,59 @@ __global__ __launch_bounds__(D1_NT, 1) void dusa1_lse_kernel(Dusa1Args a) {
   const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
   const int g = h / (a.Hq / a.Hkv);
   const uint16_t* qh = a.q + bh * (size_t)a.Rq * a.S * C;
-  const void* kh_u = uniform_ptr(a.k + ((size_t)b * a.Hkv + g) * (size_t)a.Rk * a.S * C);
+  const uint16_t* kh = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.Rk * a.S * C;
+  const D1Dma<C> dma(wave, lane, a.S);
   const int q0 = qt * D1_QR, i0 = q0 + D1_RPW * wave;
   const int last_row = min(q0 + D1_QR, a.Rq) - 1;
   const int jend = CAUSAL ? min(a.Rk, last_row + a.offs + 1) : a.Rk;  // keys seen by some row of the tile
   const int n_t = (jend + D1_KT - 1) / D1_KT;                          // >= 1
-  bf16x8 qf[2][C / 16];
+  bf16x8 qf[D1_QTW][C / 16];
   d1_load_q<C>(a, qh, i0, s, l32, hh, qf);
   // the Q loads complete before any DMA is issued: a wait the compiler sees,
   // so it places none of its own in the loop (its count ignores the DMA,
   // and such a wait would drain the ring's lookahead every step)
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  float m[D1_QTW], l[D1_QTW];
 #pragma unroll
-  for (int u = 0; u < D1_RING - 1; ++u) d1_dma<C>(a, kh_u, ring, u, s, min(u, n_t - 1) * D1_KT, wave, lane);
+  for (int y = 0; y < D1_QTW; ++y) {
+    m[y] = -INFINITY;
+    l[y] = 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < D1_RING - 1; ++u) dma.issue(a, kh, ring, u, s, min(u, n_t - 1) * D1_KT);
   for (int t = 0; t < n_t; ++t) {
     vm_wait<2 * L::BPW>();  // tile t landed (t+1, t+2 may be in flight)
     __syncthreads();        // ... for every wave; all are done with tile t-1's slot
     // past the end: the last tile again, into a slot that is never read
-    d1_dma<C>(a, kh_u, ring, (t + 3) % D1_RING, s, min(t + 3, n_t - 1) * D1_KT, wave, lane);
+    dma.issue(a, kh, ring, (t + 3) % D1_RING, s, min(t + 3, n_t - 1) * D1_KT);
     const int j0 = t * D1_KT;
     if (i0 < a.Rq && (!CAUSAL || j0 <= i0 + D1_RPW - 1 + a.offs)) {
-      f32x16 acc[2][2];
+      f32x16 acc[2][D1_QTW];
       d1_mma<C>(ring + (t % D1_RING) * L::TILE_B, qf, acc, l32, hh);
       // the masked form only on tiles that cross the diagonal or the last key
       // (one branch per tile, not per element)
       auto update = [&](auto masked) {
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
+        for (int y = 0; y < D1_QTW; ++y) {
           const int qi = i0 + 32 * y + l32 + a.offs;  // this lane's row among the keys
-          float x[2][16];
-          float mt = -INFINITY;
+          float mt = -INFINITY;  // raw maximum: sl2 > 0, so the scaled maximum is mt * sl2
 #pragma unroll
           for (int n = 0; n < 2; ++n)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              float v = acc[n][y][r] * a.sl2;
               if constexpr (decltype(masked)::value) {
                 const int j = j0 + d1_key(n, r, hh);
-                v = (j >= a.Rk || (CAUSAL && j > qi)) ? -INFINITY : v;
+                acc[n][y][r] = (j >= a.Rk || (CAUSAL && j > qi)) ? -INFINITY : acc[n][y][r];
               }
-              x[n][r] = v;
-              mt = fmaxf(mt, v);
+              mt = fmaxf(mt, acc[n][y][r]);
             }
-          const float mn = fmaxf(m[y], mt);
+          const float mn = fmaxf(m[y], mt * a.sl2);
           const float mu = mn == -INFINITY ? 0.f : mn;  // no visible key yet: every term is 0
           float sum = 0.f;
 #pragma unroll
           for (int n = 0; n < 2; ++n)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sum += fast_exp2(x[n][r] - mu);
+            for (int r = 0; r < 16; ++r) sum += fast_exp2(fmaf(acc[n][y][r], a.sl2, -mu));
           l[y] = l[y] * fast_exp2(m[y] - mu) + sum;  // m = -inf before the first visible key: 2^-inf = 0
           m[y] = mn;
         }
@@ -211,7 +244,7 @@ __global__ __launch_bounds__(D1_NT, 1) void dusa1_lse_kernel(Dusa1Args a) {
   }
   vm_wait<0>();  // the trailing loads, so no DMA reaches the ring after the workgroup
 #pragma unroll
-  for (int y = 0; y < 2; ++y) {
+  for (int y = 0; y < D1_QTW; ++y) {
     // the two halves of the wave hold the same row over different keys
     const float mt = halves_max(m[y]);
     const float lt = halves_sum(m[y] == -INFINITY ? 0.f : l[y] * fast_exp2(m[y] - mt));
@@ -239,7 +272,8 @@ __global__ __launch_bounds__(D1_NT, 1) void dusa1_block_kernel(Dusa1Args a) {
   const int h = (int)(bh % a.Hq), b = (int)(bh / a.Hq);
   const int g = h / (a.Hq / a.Hkv);
   const uint16_t* qh = a.q + bh * (size_t)a.Rq * a.S * C;
-  const void* kh_u = uniform_ptr(a.k + ((size_t)b * a.Hkv + g) * (size_t)a.Rk * a.S * C);
+  const uint16_t* kh = a.k + ((size_t)b * a.Hkv + g) * (size_t)a.Rk * a.S * C;
+  const D1Dma<C> dmap(wave, lane, a.S);
   const int q0 = qt * D1_QR, k0 = kr * KR, i0 = q0 + D1_RPW * wave;
   for (int x = tid; x < QB * KBR; x += D1_NT) (&red[0][0])[x] = 0.f;
   const int last_row = min(q0 + D1_QR, a.Rq) - 1;
@@ -251,12 +285,12 @@ __global__ __launch_bounds__(D1_NT, 1) void dusa1_block_kernel(Dusa1Args a) {
   if (n_u > 0) {
     auto dma = [&](int u) {  // step u (clamped to the last)
       const int uu = min(u, n_u - 1), su = uu / n_t;
-      d1_dma<C>(a, kh_u, ring, u % D1_RING, su, k0 + (uu - su * n_t) * D1_KT, wave, lane);
+      dmap.issue(a, kh, ring, u % D1_RING, su, k0 + (uu - su * n_t) * D1_KT);
     };
 #pragma unroll
     for (int u = 0; u < D1_RING - 1; ++u) dma(u);
-    bf16x8 qf[2][C / 16];
-    float lse_r[2] = {0.f, 0.f};
+    bf16x8 qf[D1_QTW][C / 16];
+    float lse_r[D1_QTW] = {};
     for (int u = 0; u < n_u; ++u) {
       const int s = u / n_t, t = u - s * n_t;
       vm_wait<2 * L::BPW>();  // step u landed (u+1, u+2 may be in flight)
@@ -267,21 +301,21 @@ __global__ __launch_bounds__(D1_NT, 1) void dusa1_block_kernel(Dusa1Args a) {
         // compiler's lands behind a DMA in flight
         d1_load_q<C>(a, qh, i0, s, l32, hh, qf);
 #pragma unroll
-        for (int y = 0; y < 2; ++y)
+        for (int y = 0; y < D1_QTW; ++y)
           lse_r[y] = a.lse[(bh * a.S + s) * (size_t)a.Rq + min(i0 + 32 * y + l32, a.Rq - 1)];
         __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
       }
       dma(u + 3);  // past the end: the last step again, into a slot that is never read
       const int j0 = k0 + t * D1_KT;
       if (i0 < a.Rq && (!CAUSAL || j0 <= i0 + D1_RPW - 1 + a.offs)) {
-        f32x16 acc[2][2];
+        f32x16 acc[2][D1_QTW];
         d1_mma<C>(ring + (u % D1_RING) * L::TILE_B, qf, acc, l32, hh);
         // rows past Rq (a partial last query block) read row Rq - 1 and must add
         // nothing to their block's sum; the masked form only where a mask
         // applies (one branch per tile, not per element)
         auto sums = [&](auto masked) {
 #pragma unroll
-        for (int y = 0; y < 2; ++y) {
+        for (int y = 0; y < D1_QTW; ++y) {
           const int qi = i0 + 32 * y + l32 + a.offs;
           const bool row_ok = i0 + 32 * y + l32 < a.Rq;
           // per key block of the tile: this lane's mass. Element (n, r) holds key
