@@ -87,6 +87,15 @@
 #ifndef XATTN_DMA_SPREAD
 #define XATTN_DMA_SPREAD 1
 #endif
+// 1: in the pipelined step a wave raises its priority (s_setprio) over the
+// S(t+1) MFMAs with tile t's exponentials, so the arbiter favours the phase
+// that feeds both the matrix unit and the exponentials over the other wave's
+// PV phase. Measured 1.5% off the 128K and 256K steps (A/B on one box);
+// raising it over the PV phase instead was 0.5% slower, and two levels (S
+// phase above PV phase) the same as one.
+#ifndef XATTN_ATTN_PRIO
+#define XATTN_ATTN_PRIO 1
+#endif
 // 1: Q is loaded and O stored with the non-temporal hint (read once and
 // written once, so they need not displace K/V from the caches)
 #ifndef XATTN_NT_QO
@@ -730,6 +739,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
 #pragma unroll
       for (int g = 0; g < 4; ++g) kf[g] = read_k(g);
       __builtin_amdgcn_sched_barrier(0);
+      if (XATTN_ATTN_PRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int g = 0; g < NSA; ++g) {
         const bf16x8 f = kf[g & 3];
@@ -745,6 +755,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (XATTN_ATTN_PRIO) __builtin_amdgcn_s_setprio(0);
       l_run[0] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
       bf16x8 vf[4];
 #pragma unroll

@@ -177,3 +177,52 @@ def test_partial_stride_group_takes_the_staged_path(xa):
     assert torch.equal(got.block_scores, sc) and torch.equal(got.mask, mk)
     assert torch.equal(got.kv_cnt, cnt) and _equal_lists(got.kv_idx, idx, cnt)
     assert torch.equal(got.out, out)
+
+
+def test_tile_select_replays_from_a_hip_graph(xa):
+    # the arrival counters and the attention queues are zeroed by a kernel, so
+    # the one-launch form can be captured; every replay, with eager work and
+    # synchronisations in between, equals the eager call
+    w = wl.WORKLOADS["llama32k"].scaled(M=4096, Hq=8, Hkv=2)
+    x = wl.make_inputs(w, device=DEV)
+    sscale, smscale = wl.default_scales(w)
+    args = (x["q"], x["k"], x["v"], x["tau"], w.block, w.stride, sscale, smscale, w.causal)
+    ref = xa.xattn_prefill(*args, select_in_score=True)
+    bufs = xa.PrefillBuffers(x["q"], x["k"], w.block, w.stride, w.causal, select_in_score=True)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        xa.xattn_prefill(*args, buffers=bufs, select_in_score=True)  # warm-up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        xa.xattn_prefill(*args, buffers=bufs, select_in_score=True)
+    torch.cuda.synchronize()
+    valid = torch.arange(ref.kv_idx.shape[-1], device=DEV) < ref.kv_cnt[..., None]
+    for _ in range(3):
+        for t, fill in ((bufs.out, 0.0), (bufs.block_scores, -1.0), (bufs.mask, 7), (bufs.kv_cnt, -3)):
+            t.fill_(fill)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ref.block_scores, bufs.block_scores)
+        assert torch.equal(ref.mask, bufs.mask)
+        assert torch.equal(ref.kv_cnt, bufs.kv_cnt)
+        assert torch.equal(ref.kv_idx[valid], bufs.kv_idx[valid])
+        assert torch.equal(ref.out, bufs.out)
+
+
+def test_tile_select_without_a_workspace(xa):
+    # the entry point that allocates nothing, with the option: two calls on the
+    # shared scratch, the second smaller, each equal to the default path
+    for w in (wl.WORKLOADS["llama8k"].scaled(M=8192, Hq=8, Hkv=2), wl.WORKLOADS["llama32k"].scaled(M=2048, Hq=4, Hkv=1)):
+        print(f"[tile-select noalloc] M={w.M} Hq={w.Hq}", flush=True)
+        x = wl.make_inputs(w, device=DEV)
+        sscale, smscale = wl.default_scales(w)
+        args = (x["q"], x["k"], x["v"], x["tau"], w.block, w.stride, sscale, smscale, w.causal)
+        ref = xa.xattn_prefill(*args)
+        got = xa.xattn_prefill_noalloc(*args, select_in_score=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ref.block_scores, got.block_scores) and torch.equal(ref.mask, got.mask)
+        assert torch.equal(ref.kv_cnt, got.kv_cnt) and _equal_lists(ref.kv_idx, got.kv_idx, ref.kv_cnt)
+        assert torch.equal(ref.out, got.out)
