@@ -96,6 +96,11 @@
 #ifndef XATTN_ATTN_PRIO
 #define XATTN_ATTN_PRIO 1
 #endif
+// 1: the epilogue stages each wave's output rows in LDS and stores whole rows;
+// 0: each lane stores its pieces of 32 rows straight from the accumulators
+#ifndef XATTN_O_STAGE
+#define XATTN_O_STAGE 1
+#endif
 // 1: Q is loaded and O stored with the non-temporal hint (read once and
 // written once, so they need not displace K/V from the caches)
 #ifndef XATTN_NT_QO
@@ -879,6 +884,67 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
   }
 
   // ---- epilogue: O = O^T / l, lse = (m + log2 l) * ln 2
+#if XATTN_O_STAGE
+  // Each wave stages its rows of O (bf16) in LDS over the K/V tiles and then
+  // stores whole rows, 1 KiB of consecutive bytes per store instruction,
+  // instead of 16 bytes in each of 32 rows straight from the accumulators.
+  // On the short layers, where every row keeps two blocks and the kernel is
+  // bound by memory traffic, that took the output store from about a quarter
+  // of bsa_fwd's time to half that.
+  if constexpr (PIPE) __syncthreads();  // every wave past its last read of the ring
+  if (!live) return;
+  constexpr int ROWB = 2 * C;           // bytes per output row
+  constexpr int CH = ROWB / 16;         // 16-byte chunks per row
+  constexpr int PIECES = RPW * CH;      // 16-byte pieces of a wave's rows
+  static_assert((NT / 64) * RPW * ROWB <= TILES_B, "O staging fits over the K/V tiles");
+  static_assert(PIECES % 64 == 0, "whole store instructions");
+  unsigned char* stage = smem + wave * (RPW * ROWB);
+  // The staging addresses depend on the lane only. Redefined here (empty
+  // asm), they cannot be hoisted out of the item loop, where they would stay
+  // live across the key loop and push it into spills.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int l32s = ln & 31, hhs = ln >> 5;
+  // chunk c of staged row r sits at chunk c ^ (r % CH), so the 32 rows of one
+  // write instruction (256 bytes apart) spread over every bank
+#pragma unroll
+  for (int y = 0; y < QT; ++y) {
+    const float l_tot = halves_sum(l_run[y]);
+    const float inv = 1.f / l_tot;
+    const int r = 32 * y + l32s;
+#pragma unroll
+    for (int d = 0; d < DN; ++d)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        u32x2 w;
+        w[0] = (uint32_t)f32_to_bf16(o[y][d][4 * g4 + 0] * inv) |
+               ((uint32_t)f32_to_bf16(o[y][d][4 * g4 + 1] * inv) << 16);
+        w[1] = (uint32_t)f32_to_bf16(o[y][d][4 * g4 + 2] * inv) |
+               ((uint32_t)f32_to_bf16(o[y][d][4 * g4 + 3] * inv) << 16);
+        // dims 32 d + 8 g4 + 4 hh .. + 3: chunk 4 d + g4, its half hh
+        *reinterpret_cast<u32x2*>(stage + r * ROWB + 16 * ((4 * d + g4) ^ (r % CH)) + 8 * hhs) = w;
+      }
+    const int qi = q0 + r;
+    if (qi < a.Mq && a.lse && hhs == 0) a.lse[bh * a.Mq + qi] = (m_run[y] + log2f(l_tot)) * kLn2;
+  }
+  // the stage is private to the wave: its LDS operations complete in order
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int it = 0; it < PIECES / 64; ++it) {
+    const int pc = it * 64 + ln;
+    const int r = pc / CH, c = pc % CH;
+    const int qi = q0 + r;
+    const u32x4 val = *reinterpret_cast<const u32x4*>(stage + r * ROWB + 16 * (c ^ (r % CH)));
+    if (qi < a.Mq) {  // rows past the end of a partial last block are not written
+      u32x4* dst = reinterpret_cast<u32x4*>(a.out + (bh * a.Mq + qi) * C + 8 * c);
+      if (XATTN_NT_QO)
+        __builtin_nontemporal_store(val, dst);
+      else
+        *dst = val;
+    }
+  }
+#else
   if (!live) return;
 #pragma unroll
   for (int y = 0; y < QT; ++y) {
@@ -905,6 +971,7 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
       if (a.lse && hh == 0) a.lse[bh * a.Mq + qi] = (m_run[y] + log2f(l_tot)) * kLn2;
     }
   }
+#endif
 }
 
 // Claims the next item for a persistent workgroup. queue[32 x] counts the
