@@ -90,18 +90,8 @@ __device__ void select_from_keys(SelectLds& sh, int n, int npad, int NB, int I, 
 
 #endif
 
-// Occupancy asked of the compiler for the per-row selection kernels, in
-// 256-thread workgroups per CU (that many waves per SIMD). The rows are
-// latency-bound (about twenty barriers each), so more of them in flight help:
-// 8 (60 VGPRs, a few values in scratch) against the unhinted 5 (84 VGPRs)
-// measured 2% off the 8K and 32K steps, 1% off 128K and 0.6% off 256K, with
-// bitwise the same outputs; 6 (72 VGPRs) gave about half of that.
-#ifndef XATTN_SELECT_MINB
-#define XATTN_SELECT_MINB 8
-#endif
-
 template <int CAP>
-__global__ __launch_bounds__(256, XATTN_SELECT_MINB) void select_kernel(SelectArgs a) {
+__global__ __launch_bounds__(256) void select_kernel(SelectArgs a) {
   __shared__ SelectLdsT<CAP> sh;
   const int tid = threadIdx.x;
   const size_t row = blockIdx.x;  // (b*Hq + h)*NBq + I
@@ -142,7 +132,7 @@ struct FusedArgs {
 };
 
 template <int RB, int CAP>
-__global__ __launch_bounds__(256, XATTN_SELECT_MINB) void score_select_kernel(FusedArgs a) {
+__global__ __launch_bounds__(256) void score_select_kernel(FusedArgs a) {
   __shared__ SelectLdsT<CAP> sh;
   __shared__ ScoreRowLds shs;
   const int tid = threadIdx.x;

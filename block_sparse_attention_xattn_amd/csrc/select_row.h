@@ -141,9 +141,11 @@ __device__ __forceinline__ unsigned long long block_scan_u64(int tid, unsigned l
 
 // With sc[0, n) filled, flags[0, NB) zeroed and a barrier passed: find the
 // cut, set the kept flags, add the diagonal, write the row. Barriers: 3 when
-// tau >= 1, else 24, whatever the scores.
+// tau >= 1, else 24, whatever the scores. Inlined into each kernel, so each
+// gets its own register allocation (as a call it took one budget for all
+// callers and spilled to the stack under the selection kernels' occupancy).
 template <class SL>
-__device__ void select_radix(SL& sh, int tid, int n, int NB, int I, float tau, size_t row, uint8_t* mask,
+__device__ __forceinline__ void select_radix(SL& sh, int tid, int n, int NB, int I, float tau, size_t row, uint8_t* mask,
                              int32_t* kv_idx, int32_t* kv_cnt) {
   const int lane = tid & 63, wave = tid >> 6;
   uint8_t* flags = sh.flags;
