@@ -302,7 +302,12 @@ __device__ __forceinline__ void attn_item(const AttnArgs& a, const uint32_t item
       }
       __syncthreads();
       const int per = (NBk + NT - 1) / NT;
-      const int j0 = tid * per, j1 = min(j0 + per, NBk);
+      // redefined here (empty asm) so that values derived from the thread
+      // index alone are not hoisted out of the item loop and kept live
+      // across the key loop
+      int tidu = tid;
+      asm volatile("" : "+v"(tidu));
+      const int j0 = tidu * per, j1 = min(j0 + per, NBk);
       int mine = 0;
       for (int j = j0; j < j1; ++j) mine += flag[j] != 0;
       int incl = mine;
