@@ -1,6 +1,6 @@
 """Seeded random problems across the whole interface: ragged and chunked lengths,
 both head sizes and block sizes, every block/stride ratio, GQA group sizes
-1-4, batch 1-2, causal and not, the three scoring patterns, the three
+1-4 and 8, batch 1-2, causal and not, the three scoring patterns, the three
 selection modes, selection inside the scoring launch, bf16 and fp32.
 
 Each problem runs xattn_prefill and the staged calls (xattn_score, then
@@ -26,7 +26,7 @@ DEV = "cuda:0"
 N_CASES = 96
 
 
-def _case(seed):
+def _case(seed, group=None):
     rng = np.random.default_rng(1000 + seed)
     C = int(rng.choice([64, 128]))
     block = int(rng.choice([64, 128]))
@@ -34,6 +34,8 @@ def _case(seed):
     stride = block // r
     hkv = int(rng.choice([1, 2]))
     hq = hkv * int(rng.integers(1, 5))
+    if group is not None:
+        hq = hkv * group
     B = int(rng.choice([1, 1, 2]))
     causal = bool(rng.random() < 0.7)
     pattern = str(rng.choice(["antidiagonal", "antidiagonal", "antidiagonal", "diagonal", "dusa1"]))
@@ -51,7 +53,8 @@ def _case(seed):
                 dtype=dtype, selection=selection, M=M, Mk=Mk, tau=tau, seed=seed)
 
 
-CASES = [_case(i) for i in range(N_CASES)]
+# and eight with GQA groups of 8 (sibling pairs of four per KV head)
+CASES = [_case(i) for i in range(N_CASES)] + [_case(i, group=8) for i in range(N_CASES, N_CASES + 8)]
 
 
 def _ids(c):
