@@ -1109,16 +1109,6 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(AttnArgsF32 a) {
 
 // ------------------------------------------------------------------ launchers
 
-// Workgroups of one kernel instance that fit on the current device at once.
-template <class Kern>
-static int resident_workgroups(Kern kern, int threads) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess) return 0;
-  return cus * per_cu;
-}
-
 template <int C, int BLK, int MODE, bool KTAIL, int RPW>
 static hipError_t launch_bf16_cbmt(const Shape& s, const AttnArgs& a, hipStream_t st, bool queue_zeroed) {
   const int G = s.Hq / s.Hkv;

@@ -150,4 +150,15 @@ __device__ __forceinline__ void vm_wait() {
 // loads (including LDS DMA) of this wave outstanding.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
+// Workgroups of one kernel instance that fit on the current device at once
+// (0 if the runtime cannot tell).
+template <class Kern>
+static int resident_workgroups(Kern kern, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess) return 0;
+  return cus * per_cu;
+}
+
 }  // namespace xattn

@@ -146,9 +146,11 @@ __device__ __forceinline__ void tile_pair(int p, bool causal, int Tq, int Tk, in
 struct ScoreTile {
   size_t bh, bg;
   int i0, j0;  // first strided query row / strided key of the tile
-  __device__ ScoreTile(const ScoreArgs& a, bool causal) {
+  // w: the workgroup's index in launch order (blockIdx.x, or the k-th tile of a
+  // persistent workgroup: blockIdx.x + k gridDim.x)
+  __device__ ScoreTile(const ScoreArgs& a, bool causal, uint32_t w) {
     const uint32_t n_items = (uint32_t)a.B * a.Hq * a.pairs;
-    const uint32_t item = xcd_map(blockIdx.x, n_items, XATTN_SCORE_XCD_GROUP);
+    const uint32_t item = xcd_map(w, n_items, XATTN_SCORE_XCD_GROUP);
     const int G = a.Hq / a.Hkv;
     const int hq_in = item % G;
     uint32_t rest = item / G;
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(ScReg::NT, ScReg::MINW) void score_partials_bf16_ke
   const int l32 = lane & 31, hh = lane >> 5;
   const int wk = wave / W::WNQ, wq = wave % W::WNQ;
 
-  const ScoreTile tl(a, CAUSAL);
+  const ScoreTile tl(a, CAUSAL, blockIdx.x);
   const size_t bh = tl.bh;
   const uint16_t* qh = a.q + tl.bh * a.Mq * C;
   const uint16_t* kh = a.k + tl.bg * a.Mk * C;
@@ -505,7 +507,7 @@ __global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_ker
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
   const int wk = wave / W::WNQ, wq = wave % W::WNQ;
-  const ScoreTile tl(a, CAUSAL);
+  const ScoreTile tl(a, CAUSAL, blockIdx.x);
   const uint16_t* qh = a.q + tl.bh * a.Mq * C;
   const uint16_t* kh = a.k + tl.bg * a.Mk * C;
   const int S = a.S;
@@ -692,6 +694,147 @@ __global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_ker
 #endif
 }
 
+// Persistent form of the DMA kernel (two waves per SIMD, no selection in the
+// launch): one workgroup per CU takes the tiles w, w + grid, w + 2 grid, ...
+// of the launch order, the grid a multiple of 8, so every tile still runs on
+// the XCD that xcd_map gives it and the tiles in flight at any time are the
+// same window as with one workgroup per tile. Once every wave is past chunk
+// n-2 of a tile, the first three chunks of the next tile go into the three
+// free stages; the last chunk's MFMAs and the epilogue then cover their
+// latency, so neither a workgroup launch nor the first chunk's memory latency
+// sits between two tiles. The first wait of a tile is a full one: the
+// previous tile's partial stores are then in flight too, and loads and stores
+// need not complete in issue order, so a partial count would not prove that
+// chunk 0 has landed. Needs at least eight chunks (the launcher checks).
+template <int C, int RB, bool CAUSAL>
+__global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_persist_kernel(ScoreArgs a) {
+  using W = ScDma;
+  static_assert(W::MINW == 2, "persistent form of the two-waves-per-SIMD kernel");
+  static_assert(RB == 2 || RB == 4 || RB == 8 || RB == 16 || RB == 32, "r");
+  __shared__ __attribute__((aligned(1024))) uint16_t st0[SD_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st1[SD_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st2[SD_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint16_t st3[SD_STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int wk = wave / W::WNQ, wq = wave % W::WNQ;
+  const uint32_t n_items = (uint32_t)a.B * a.Hq * a.pairs;
+  const int S = a.S;
+  const int n_chunks = S * C / SD_KC;
+  const int kdir = a.diagonal ? 1 : -1;
+  const int piece = (lane & 3) ^ ((lane >> 4) & 3);
+
+  // this lane's DMA sources for a tile (as in score_partials_dma_kernel)
+  const uint16_t* kp[SD_BPW];
+  const uint16_t* qp[SD_BPW];
+  auto sources = [&](const ScoreTile& t) {
+    const uint16_t* qh = a.q + t.bh * a.Mq * C;
+    const uint16_t* kh = a.k + t.bg * a.Mk * C;
+#pragma unroll
+    for (int u = 0; u < SD_BPW; ++u) {
+      const int row = SD_BLK * (wave + (W::NT / 64) * u) + (lane >> 2);
+      const int j = min(t.j0 + row, a.Rk - 1), i = min(t.i0 + row, a.Rq - 1);
+      kp[u] = kh + ((size_t)j * S + (a.diagonal ? 0 : S - 1)) * C + 8 * piece;
+      qp[u] = qh + (size_t)i * S * C + 8 * piece;
+    }
+  };
+  auto issue = [&](int c, uint16_t* stg) {
+    const int srow = (SD_KC * c) / C, col0 = (SD_KC * c) % C;
+    const ptrdiff_t koff = (ptrdiff_t)kdir * srow * C + col0, qoff = (ptrdiff_t)srow * C + col0;
+#pragma unroll
+    for (int u = 0; u < SD_BPW; ++u) {
+      const int blk = wave + (W::NT / 64) * u;
+      __builtin_amdgcn_global_load_lds(kp[u] + koff, (__attribute__((address_space(3))) void*)(stg + blk * 1024 / 2),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(qp[u] + qoff,
+                                       (__attribute__((address_space(3))) void*)(stg + SC_TILE * SD_ROW + blk * 1024 / 2),
+                                       16, 0, 0);
+    }
+  };
+  f32x16 acc[W::MTK][W::MTQ];
+  auto mma = [&](const uint16_t* cur) {
+#pragma unroll
+    for (int ks = 0; ks < SD_KC / 16; ++ks) {
+      bf16x8 af[W::MTK], bfr[W::MTQ];
+#pragma unroll
+      for (int x = 0; x < W::MTK; ++x)
+        af[x] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + sd_off(W::WK * wk + 32 * x + l32, 2 * ks + hh)));
+#pragma unroll
+      for (int y = 0; y < W::MTQ; ++y)
+        bfr[y] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + SC_TILE * SD_ROW +
+                                                                           sd_off(W::WQ * wq + 32 * y + l32, 2 * ks + hh)));
+#pragma unroll
+      for (int x = 0; x < W::MTK; ++x)
+#pragma unroll
+        for (int y = 0; y < W::MTQ; ++y) acc[x][y] = mfma32x32x16(af[x], bfr[y], acc[x][y]);
+    }
+  };
+  auto step = [&](int c, const uint16_t* cur, uint16_t* nxt) {
+    vm_wait_barrier<2 * 2 * SD_BPW>();  // chunks c+1, c+2 may be in flight
+    issue(c + 3, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(cur);
+  };
+
+  uint32_t w = blockIdx.x;
+  ScoreTile tl(a, CAUSAL, w);
+  sources(tl);
+  issue(0, st0);
+  issue(1, st1);
+  issue(2, st2);
+  for (;;) {
+    // The next tile (after the last one, this tile again: its chunks are
+    // fetched once more and never read, an unconditional issue keeps the
+    // compiler's own waits out of the loop). Decoded here, while chunk 0 is in
+    // flight; the empty asm keeps the decode from sinking to the tail, where
+    // it would delay the next tile's first fetches and the last MFMAs.
+    const uint32_t wn = w + gridDim.x;
+    const bool more = wn < n_items;
+    ScoreTile tn(a, CAUSAL, more ? wn : w);
+    asm volatile("" : "+s"(tn.bh), "+s"(tn.bg), "+s"(tn.i0), "+s"(tn.j0));
+#pragma unroll
+    for (int x = 0; x < W::MTK; ++x)
+#pragma unroll
+      for (int y = 0; y < W::MTQ; ++y) acc[x][y] = f32x16{};
+    vm_wait_barrier<0>();  // chunks 0-2 and the previous tile's stores
+    issue(3, st3);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(st0);
+    step(1, st1, st0);
+    step(2, st2, st1);
+    step(3, st3, st2);
+    for (int c = 4; c < n_chunks - 4; c += 4) {
+      step(c, st0, st3);
+      step(c + 1, st1, st0);
+      step(c + 2, st2, st1);
+      step(c + 3, st3, st2);
+    }
+    step(n_chunks - 4, st0, st3);
+    vm_wait_barrier<2 * 2 * SD_BPW>();  // chunks n-2, n-1 may be in flight
+    mma(st1);
+    vm_wait_barrier<1 * 2 * SD_BPW>();  // chunk n-1 may be in flight
+    mma(st2);
+    // every wave is past chunks n-4 .. n-2, its own LDS reads of them included
+    // (lgkmcnt too: the scheduler may leave the fragment reads of chunk n-2 in
+    // flight across the barrier): stages 0-2 are free for the next tile
+    __builtin_amdgcn_s_waitcnt(0);
+    vm_wait_barrier<0>();
+    sources(tn);
+    issue(0, st0);
+    issue(1, st1);
+    issue(2, st2);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(st3);
+    score_epilogue<RB, CAUSAL, W>(a, acc, tl.bh, tl.i0, tl.j0, wk, wq, l32, hh);
+    if (!more) break;
+    w = wn;
+    tl = tn;
+  }
+  // the spare fetch lands before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
 // fp32 inputs: one thread per (strided row i, key block J), plain FMA.
 struct ScoreArgsF32 {
   const float* q;
@@ -761,6 +904,12 @@ __global__ __launch_bounds__(256) void score_finalize_kernel(FinalizeArgs a) {
 #ifndef XATTN_SCORE_DMA
 #define XATTN_SCORE_DMA 1
 #endif
+// 1: the DMA kernel without selection runs persistent workgroups that fetch
+// the next tile's first chunks during a tile's last MFMAs and epilogue
+// (score_partials_dma_persist_kernel); 0: one workgroup per tile
+#ifndef XATTN_SCORE_PERSIST
+#define XATTN_SCORE_PERSIST 1
+#endif
 
 // The DMA kernel needs complete stride groups and a chunk count that is a
 // multiple of the ring's four stages.
@@ -784,6 +933,21 @@ static hipError_t launch_partials_crt(const Shape& s, const ScoreArgs& a, const 
       return hipGetLastError();
 #endif
     }
+#if XATTN_SCORE_PERSIST
+    if (ScDma::MINW == 2 && s.stride * s.C / SD_KC >= 8) {
+      auto kern = s.causal ? score_partials_dma_persist_kernel<C, RB, true>
+                           : score_partials_dma_persist_kernel<C, RB, false>;
+      // whole XCD rounds of resident workgroups (the tile order relies on
+      // workgroup w running on XCD w % 8)
+      // (below two tiles per workgroup nothing is gained: 2% slower on the
+      // 8K layer's 320 tiles, 3-4% faster at 32K, 2% at 128K and 256K)
+      const unsigned slots = (unsigned)(resident_workgroups(kern, ScDma::NT) & ~7);
+      if (slots > 0 && grid >= 2 * slots) {
+        hipLaunchKernelGGL(kern, dim3(std::min(grid, slots)), dim3(ScDma::NT), 0, st, a);
+        return hipGetLastError();
+      }
+    }
+#endif
     if (s.causal)
       hipLaunchKernelGGL((score_partials_dma_kernel<C, RB, true, false>), dim3(grid), dim3(ScDma::NT), 0, st, a, none);
     else
