@@ -31,21 +31,32 @@ __device__ __forceinline__ void block_score_row_long(const float* L, int n_cand,
                                                 ScoreRowLds& sh, int tid, Emit&& emit) {
   const int lane = tid & 63, wave = tid >> 6;
   // pass 1: per strided row t, log2-sum-exp over candidate blocks
+  // U key blocks per thread are loaded together before any is used, so their
+  // latencies overlap; they are then taken in the order of J
+  constexpr int U = RB >= 32 ? 1 : 32 / RB;
   float m[RB], s[RB];
 #pragma unroll
   for (int t = 0; t < RB; ++t) { m[t] = -INFINITY; s[t] = 0.f; }
-  for (int J = tid; J < n_cand; J += 256) {
-    const float* p = L + (size_t)J * RB;
-    float xs[RB];
+  for (int J0 = tid; J0 < n_cand; J0 += 256 * U) {
+    float xs[U][RB];
 #pragma unroll
-    for (int t = 0; t < RB; ++t) xs[t] = p[t];  // unconditional, so the loads stay vectorised
+    for (int u = 0; u < U; ++u) {
+      const int J = min(J0 + 256 * u, n_cand - 1);  // in bounds; blocks past n_cand are skipped below
+      const float* p = L + (size_t)J * RB;
 #pragma unroll
-    for (int t = 0; t < RB; ++t) {
-      const float x = t < rows ? xs[t] : -INFINITY;  // rows past the end were never written
-      const float mn = fmaxf(m[t], x);
-      if (mn != -INFINITY) {
-        s[t] = s[t] * fast_exp2(m[t] - mn) + fast_exp2(x - mn);
-        m[t] = mn;
+      for (int t = 0; t < RB; ++t) xs[u][t] = p[t];  // unconditional, so the loads stay vectorised
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (J0 + 256 * u >= n_cand) break;
+#pragma unroll
+      for (int t = 0; t < RB; ++t) {
+        const float x = t < rows ? xs[u][t] : -INFINITY;  // rows past the end were never written
+        const float mn = fmaxf(m[t], x);
+        if (mn != -INFINITY) {
+          s[t] = s[t] * fast_exp2(m[t] - mn) + fast_exp2(x - mn);
+          m[t] = mn;
+        }
       }
     }
   }
@@ -78,21 +89,30 @@ __device__ __forceinline__ void block_score_row_long(const float* L, int n_cand,
   __syncthreads();
   // pass 2: block score = (1/rows) sum_t 2^(L[J][t] - lse_t)
   const float inv_r = 1.f / (float)rows;
-  for (int J = tid; J < NB; J += 256) {
-    float sc = 0.f;
-    if (J < n_cand) {
+  for (int J0 = tid; J0 < NB; J0 += 256 * U) {
+    float xs[U][RB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int J = min(J0 + 256 * u, n_cand - 1);
       const float* p = L + (size_t)J * RB;
-      float xs[RB];
 #pragma unroll
-      for (int t = 0; t < RB; ++t) xs[t] = p[t];
-#pragma unroll
-      for (int t = 0; t < RB; ++t) {
-        const float e = fast_exp2(xs[t] - sh.lse[t]);
-        sc += t < rows ? e : 0.f;
-      }
-      sc *= inv_r;
+      for (int t = 0; t < RB; ++t) xs[u][t] = p[t];
     }
-    emit(J, sc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int J = J0 + 256 * u;
+      if (J >= NB) break;
+      float sc = 0.f;
+      if (J < n_cand) {
+#pragma unroll
+        for (int t = 0; t < RB; ++t) {
+          const float e = fast_exp2(xs[u][t] - sh.lse[t]);
+          sc += t < rows ? e : 0.f;
+        }
+        sc *= inv_r;
+      }
+      emit(J, sc);
+    }
   }
 }
 
@@ -111,18 +131,30 @@ __device__ __forceinline__ void block_score_row_short(const float* L, int n_cand
   const int lane = tid & 63, wave = tid >> 6;
   const int t = tid % RB, jl = tid / RB;
   const bool live = t < rows;  // rows past the end were never written
+  // A lane's partials (at most RB of them: n_cand <= 256 = JL * RB) are all
+  // loaded up front, so their latencies overlap instead of adding up over
+  // three dependent passes; the arithmetic below keeps the order of J.
+  float xv[RB];
+#pragma unroll
+  for (int it = 0; it < RB; ++it) {
+    const int J = jl + it * JL;
+    xv[it] = (live && J < n_cand) ? L[(size_t)J * RB + t] : -INFINITY;
+  }
   // pass 1: lse_t = log2 sum_J 2^L[J][t], as a max then a sum of 2^(x - max)
   float m = -INFINITY;
-  if (live)
-    for (int J = jl; J < n_cand; J += JL) m = fmaxf(m, L[(size_t)J * RB + t]);
+#pragma unroll
+  for (int it = 0; it < RB; ++it) m = fmaxf(m, xv[it]);
 #pragma unroll
   for (int off = RB; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   if (lane < RB) sh.red_m[wave][lane] = m;
   __syncthreads();
   const float mt = fmaxf(fmaxf(sh.red_m[0][t], sh.red_m[1][t]), fmaxf(sh.red_m[2][t], sh.red_m[3][t]));
   float s = 0.f;
-  if (live && mt != -INFINITY)
-    for (int J = jl; J < n_cand; J += JL) s += fast_exp2(L[(size_t)J * RB + t] - mt);
+  if (live && mt != -INFINITY) {
+#pragma unroll
+    for (int it = 0; it < RB; ++it)
+      if (jl + it * JL < n_cand) s += fast_exp2(xv[it] - mt);
+  }
 #pragma unroll
   for (int off = RB; off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
   if (lane < RB) sh.red_s[wave][lane] = s;
@@ -133,14 +165,21 @@ __device__ __forceinline__ void block_score_row_short(const float* L, int n_cand
   // adjacent lanes of key block J (a uniform trip count keeps the shuffles
   // converged)
   const float inv_r = 1.f / (float)rows;
-  const int iters = (NB + JL - 1) / JL;
-  for (int it = 0; it < iters; ++it) {
+  const int iters = (NB + JL - 1) / JL;  // uniform, so the shuffles stay converged
+#pragma unroll
+  for (int it = 0; it < RB; ++it) {
+    if (it >= iters) break;
     const int J = jl + it * JL;
     float e = 0.f;
-    if (J < n_cand && live && lse != -INFINITY) e = fast_exp2(L[(size_t)J * RB + t] - lse);
+    if (J < n_cand && live && lse != -INFINITY) e = fast_exp2(xv[it] - lse);
 #pragma unroll
     for (int off = 1; off < RB; off <<= 1) e += __shfl_xor(e, off, 64);
     if (t == 0 && J < NB) emit(J, J < n_cand ? e * inv_r : 0.f);
+  }
+  // key blocks past the candidates (J >= JL * RB > n_cand) score 0
+  for (int it = RB; it < iters; ++it) {
+    const int J = jl + it * JL;
+    if (t == 0 && J < NB) emit(J, 0.f);
   }
 }
 

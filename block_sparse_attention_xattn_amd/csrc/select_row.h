@@ -139,16 +139,141 @@ __device__ __forceinline__ unsigned long long block_scan_u64(int tid, unsigned l
   return x;
 }
 
+// Layers of at most kSelWaveMax key blocks: one wave selects the row. The 256
+// candidate slots (4 per lane, slot e = 64 k + lane, empty slots key 0) are
+// sorted by (score bits << 32 | ~J) descending with an in-register bitonic
+// sort (over the first 64, 128 or 256 slots, as the row needs); the fixed-point masses in that order are scanned across the wave, and
+// a slot is kept while the mass before it is below ceil(tau * T). That is the
+// prefix rule itself, so the kept set is the one the radix select finds (same
+// masses, same threshold), with no workgroup barrier at all.
+constexpr int kSelWaveMax = 256;
+// 1: rows of such layers are selected by one wave; 0: by the radix select
+#ifndef XATTN_SELECT_WAVE
+#define XATTN_SELECT_WAVE 1
+#endif
+
+__device__ __forceinline__ unsigned long long wave_incl_scan_u64(unsigned long long x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Bitonic sort of the 64 NK slots held in kv[0, NK), descending.
+template <int NK>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&kv)[4], int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64 * NK; size <<= 1) {
+#pragma unroll
+    for (int j = size >> 1; j > 0; j >>= 1) {
+      if (j >= 64) {
+        // partner slots in this lane's registers: k and k | j/64
+        const int kj = j >> 6;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          if (k & kj) continue;
+          const int k2 = k | kj;
+          const bool big_first = ((64 * k + lane) & size) == 0;
+          const uint64_t a = kv[k], b = kv[k2];
+          const bool sw = big_first ? (a < b) : (a > b);
+          kv[k] = sw ? b : a;
+          kv[k2] = sw ? a : b;
+        }
+      } else {
+        // partner slot in lane ^ j; the lower slot of a pair keeps the larger
+        // key where its block of `size` slots runs descending
+        const bool lower = (lane & j) == 0;
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          const uint64_t o = __shfl_xor(kv[k], j, 64);
+          const bool big_first = ((64 * k + lane) & size) == 0;
+          const bool keep_max = lower == big_first;
+          kv[k] = keep_max ? (kv[k] > o ? kv[k] : o) : (kv[k] < o ? kv[k] : o);
+        }
+      }
+    }
+  }
+}
+
+// One wave (lane 0..63) selects a row of n <= NB <= kSelWaveMax candidates:
+// sc[0, n) filled, flags[0, NB) zeroed and visible to the wave. Writes flags,
+// the mask row, the kept list and the count; no barrier.
+template <class SL>
+__device__ __forceinline__ void select_wave_small(SL& sh, int lane, int n, int NB, int I, float tau, size_t row,
+                                                  uint8_t* mask, int32_t* kv_idx, int32_t* kv_cnt) {
+  uint8_t* flags = sh.flags;
+  if (tau >= 1.f) {
+    for (int p = lane; p < n; p += 64) flags[p] = 1;
+  } else {
+    uint64_t kv[4];
+    unsigned long long tot = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = 64 * k + lane;
+      const float v = p < n ? sh.sc[p] : 0.f;
+      kv[k] = p < n ? ((uint64_t)__float_as_uint(v) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)p) : 0ull;
+      tot += p < n ? sel_fx(v) : 0ull;
+    }
+    // T: an integer sum, so independent of the order
+    const unsigned long long total = __shfl(wave_incl_scan_u64(tot, lane), 63, 64);
+    const unsigned long long thr = (unsigned long long)ceil((double)tau * (double)total);
+    const bool none = tau <= 0.f || total == 0ull || thr == 0ull;
+    if (!none) {
+      // sort only the slots that can hold candidates (64, 128 or 256); the
+      // rest hold key 0 and already sit last
+      if (n <= 64)
+        wave_sort_desc<1>(kv, lane);
+      else if (n <= 128)
+        wave_sort_desc<2>(kv, lane);
+      else
+        wave_sort_desc<4>(kv, lane);
+      unsigned long long base = 0;  // mass of the slots before this register's 64
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float v = __uint_as_float((uint32_t)(kv[k] >> 32));
+        const unsigned long long fx = kv[k] ? sel_fx(v) : 0ull;
+        const unsigned long long incl = wave_incl_scan_u64(fx, lane);
+        if (kv[k] != 0ull && base + incl - fx < thr) flags[0xFFFFFFFFu - (uint32_t)(kv[k] & 0xFFFFFFFFu)] = 1;
+        base += __shfl(incl, 63, 64);
+      }
+    }
+  }
+  if (lane == 0) flags[I] = 1;  // diagonal block
+  __builtin_amdgcn_wave_barrier();
+  if (mask) {
+    uint8_t* mrow = mask + row * NB;
+    for (int p = lane; p < NB; p += 64) mrow[p] = flags[p];
+  }
+  const int per = (NB + 63) / 64;
+  const int p0 = min(lane * per, NB), p1 = min(p0 + per, NB);
+  int mine = 0;
+  for (int p = p0; p < p1; ++p) mine += flags[p];
+  const int incl = wave_incl_scan_i(mine, lane);
+  int pos = incl - mine;
+  int32_t* irow = kv_idx + row * NB;
+  for (int p = p0; p < p1; ++p)
+    if (flags[p]) irow[pos++] = p;
+  if (lane == 63) kv_cnt[row] = incl;
+}
+
 // With sc[0, n) filled, flags[0, NB) zeroed and a barrier passed: find the
-// cut, set the kept flags, add the diagonal, write the row. Barriers: 3 when
-// tau >= 1, else 24, whatever the scores. Inlined into each kernel, so each
-// gets its own register allocation (as a call it took one budget for all
-// callers and spilled to the stack under the selection kernels' occupancy).
+// cut, set the kept flags, add the diagonal, write the row. Barriers: none
+// when NB <= kSelWaveMax (wave 0 selects, select_wave_small); otherwise 3
+// when tau >= 1, else 24, whatever the scores. Callers synchronise before the
+// group reuses the row state. Inlined into each kernel, so each gets its own
+// register allocation (as a call it took one budget for all callers and
+// spilled to the stack under the selection kernels' occupancy).
 template <class SL>
 __device__ __forceinline__ void select_radix(SL& sh, int tid, int n, int NB, int I, float tau, size_t row, uint8_t* mask,
                              int32_t* kv_idx, int32_t* kv_cnt) {
   const int lane = tid & 63, wave = tid >> 6;
   uint8_t* flags = sh.flags;
+  if (XATTN_SELECT_WAVE && NB <= kSelWaveMax) {
+    if (wave == 0) select_wave_small(sh, lane, n, NB, I, tau, row, mask, kv_idx, kv_cnt);
+    return;
+  }
   if (tau >= 1.f) {
     for (int p = tid; p < n; p += 256) flags[p] = 1;
   } else {
