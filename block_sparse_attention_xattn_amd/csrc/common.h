@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 // Debug builds (-DXATTN_DEBUG=1, libxattn_debug.so): bounds checks at the
 // kernels' indexing sites. A failed check adds one to a per-source device
 // counter of its category (no trap: the access that follows is the release
@@ -151,14 +153,33 @@ __device__ __forceinline__ void vm_wait() {
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // Workgroups of one kernel instance that fit on the current device at once
-// (0 if the runtime cannot tell).
+// (0 if the runtime cannot tell). The answer is kept per (kernel, block size,
+// device) after the first call, so launches do not ask the runtime again.
 template <class Kern>
 static int resident_workgroups(Kern kern, int threads) {
+  struct Entry {
+    const void* kern;
+    int threads, dev, n;
+  };
+  static std::mutex mu;
+  static Entry known[64];  // a fixed table: no allocation; when full, nothing more is kept
+  static int used = 0;
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const void* k = reinterpret_cast<const void*>(kern);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (known[i].kern == k && known[i].threads == threads && known[i].dev == dev) return known[i].n;
+  }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, 0) != hipSuccess) return 0;
-  return cus * per_cu;
+  const int n = cus * per_cu;
+  if (n > 0) {
+    std::lock_guard<std::mutex> lock(mu);
+    if (used < 64) known[used++] = Entry{k, threads, dev, n};
+  }
+  return n;
 }
 
 }  // namespace xattn
