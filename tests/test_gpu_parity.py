@@ -175,11 +175,15 @@ def test_short_and_long_score_rows(xa, case):
             assert all(int(j) in ok for j in diff), (h, big_i, diff[:5])
 
 
+# Layers of at most 256 key blocks are selected by one wave per row (sorting
+# 64, 128 or 256 slots); larger ones by the radix passes: block counts on
+# every side of those sizes.
+@pytest.mark.parametrize("nb", [40, 130, 300])
 @pytest.mark.parametrize("tau", [0.0, 0.5, 0.9, 0.95, 1.0])
 @pytest.mark.parametrize("causal", [True, False])
-def test_select_matches_oracle_on_same_scores(xa, tau, causal):
-    B, Hq, nb = 1, 3, 40
-    rng = np.random.default_rng(int(tau * 100) + causal)
+def test_select_matches_oracle_on_same_scores(xa, tau, causal, nb):
+    B, Hq = 1, 3
+    rng = np.random.default_rng(int(tau * 100) + causal + nb)
     raw = rng.gamma(0.3, size=(B, Hq, nb, nb))
     raw[..., :, 3] *= 0.0       # exact zeros
     raw[..., :, 5] = raw[..., :, 6]  # exact ties
@@ -213,11 +217,11 @@ def _cut_case_rows(nb):
     return rows
 
 
+@pytest.mark.parametrize("nb", [64, 100, 200, 300])
 @pytest.mark.parametrize("causal", [False, True])
-def test_select_exact_cuts(xa, causal):
+def test_select_exact_cuts(xa, causal, nb):
     # per-head tau: 0.5 and 0.625 land exactly on cumulative masses of these rows
     # (c_k = tau * T), 0.51 and 0.85 between them, 0.99 near the total
-    nb = 64
     taus = [0.5, 0.51, 0.625, 0.85, 0.99, 0.0, 1.0]
     cases = _cut_case_rows(nb)
     raw = np.zeros((1, len(taus), nb, nb))
@@ -233,7 +237,10 @@ def test_select_exact_cuts(xa, causal):
     scores = torch.from_numpy(raw.astype(np.float32))
     mask, idx, cnt = xa.xattn_select(scores.to(DEV), taus, 128, 8, causal, Hkv=1)
     torch.cuda.synchronize()
-    ref = oracle.select(raw, taus, causal)
+    # the C ABI takes tau as float32, so the oracle is given that same value:
+    # with 1/nb scores a cut can land exactly on a cumulative mass (0.85 * 100
+    # blocks), where float32 and float64 tau fall on either side of it
+    ref = oracle.select(raw, np.float32(taus).astype(np.float64), causal)
     m = mask.cpu().numpy()
     bad = np.argwhere(m.astype(bool) != ref.astype(bool))
     assert bad.size == 0, bad[:8]
