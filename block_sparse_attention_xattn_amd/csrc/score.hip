@@ -69,6 +69,16 @@ constexpr int SC_TILE = XATTN_SCORE_TILE;   // strided keys x strided queries pe
 // (64 x 64 about 2% and 128 x 128 about 6% behind 64 x 128 at 256K); the
 // register-staged kernel with 64 x 64 (64 x 128 about 3% slower: its staging
 // registers leave two waves per SIMD too little room).
+// 1: the two-waves-per-SIMD DMA kernel (one workgroup per tile) also runs the
+// hand-pipelined chunk loop (fragment reads of the next k-step ahead of the
+// MFMAs, across the barrier); 0: the plain loop. Measured with one workgroup
+// per tile: 2.4% faster at 256K, 1.2% at 128K, neutral at 32K; the same loop
+// in the persistent kernel was 3-8% slower than its plain loop (registers
+// spilled around the chunk loop, reloaded every tile), and the persistent
+// plain loop is the faster of all, so this stays off.
+#ifndef XATTN_SCORE_KPIPE
+#define XATTN_SCORE_KPIPE 0
+#endif
 #ifndef XATTN_SCORE_DMA_WK
 #define XATTN_SCORE_DMA_WK 128
 #endif
@@ -576,7 +586,7 @@ __global__ __launch_bounds__(ScDma::NT, ScDma::MINW) void score_partials_dma_ker
     __builtin_amdgcn_sched_barrier(0);  // keep the refill ahead of this chunk's work
     mma(cur);
   };
-  if constexpr (W::MINW == 1) {
+  if constexpr (W::MINW == 1 || XATTN_SCORE_KPIPE) {
     // One wave per SIMD (128 x 128 wave tiles): no second wave hides the
     // fragment reads, so the loop is software-pipelined by hand. The fragments
     // of k-step 1 of chunk c are read while the MFMAs of its k-step 0 run;
