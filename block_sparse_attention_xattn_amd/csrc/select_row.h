@@ -142,9 +142,10 @@ __device__ __forceinline__ unsigned long long block_scan_u64(int tid, unsigned l
 // Layers of at most kSelWaveMax key blocks: one wave selects the row. The 256
 // candidate slots (4 per lane, slot e = 64 k + lane, empty slots key 0) are
 // sorted by (score bits << 32 | ~J) descending with an in-register bitonic
-// sort (over the first 64, 128 or 256 slots, as the row needs); the fixed-point masses in that order are scanned across the wave, and
-// a slot is kept while the mass before it is below ceil(tau * T). That is the
-// prefix rule itself, so the kept set is the one the radix select finds (same
+// sort (over the first 64, 128 or 256 slots, as the row needs); the
+// fixed-point masses in that order are scanned across the wave, and a slot is
+// kept while the mass before it is below ceil(tau * T). That is the prefix
+// rule itself, so the kept set is the one the radix select finds (same
 // masses, same threshold), with no workgroup barrier at all.
 constexpr int kSelWaveMax = 256;
 // 1: rows of such layers are selected by one wave; 0: by the radix select
