@@ -28,11 +28,12 @@ CASES = [
     (1, 16, 16, 4096, 4096, 128, 64, 2, True, "antidiagonal"),    # 576 tiles, 8 chunks, r = 32
     (1, 32, 8, 8192, 32768, 128, 128, 8, True, "antidiagonal"),   # chunked: 1856 tiles
     (1, 16, 4, 16384, 16384, 128, 128, 8, True, "diagonal"),      # 576 tiles
+    (2, 8, 2, 8192, 8192, 64, 64, 4, True, "antidiagonal"),       # two batch entries: 576 tiles
 ]
 
 
 def _ids(c):
-    return f"h{c[1]}-{c[3]}of{c[4]}-C{c[5]}-b{c[6]}-s{c[7]}-{'c' if c[8] else 'n'}-{c[9]}"
+    return f"B{c[0]}-h{c[1]}-{c[3]}of{c[4]}-C{c[5]}-b{c[6]}-s{c[7]}-{'c' if c[8] else 'n'}-{c[9]}"
 
 
 @pytest.fixture(scope="module")
@@ -43,18 +44,18 @@ def xa():
     return x
 
 
-def _tiles(Hq, Mq, Mk, stride, causal, tile=256):
+def _tiles(B, Hq, Mq, Mk, stride, causal, tile=256):
     rq, rk = Mq // stride, Mk // stride
     tq, tk = -(-rq // tile), -(-rk // tile)
     c0 = -(-((Mk - Mq) // stride) // tile)
     pairs = sum(min(tk, t + c0 + 1) for t in range(tq)) if causal else tq * tk
-    return Hq * pairs
+    return B * Hq * pairs
 
 
 @pytest.mark.parametrize("case", CASES, ids=_ids)
 def test_persistent_scoring_sampled_rows(xa, case):
     B, Hq, Hkv, Mq, Mk, C, block, stride, causal, pattern = case
-    assert _tiles(Hq, Mq, Mk, stride, causal) >= 512 and stride * C // 32 >= 8
+    assert _tiles(B, Hq, Mq, Mk, stride, causal) >= 512 and stride * C // 32 >= 8
     print(f"[persistent] {_ids(case)}", flush=True)
     g = torch.Generator().manual_seed(Mq + Mk + C + stride)
     k = torch.randn((B, Hkv, Mk, C), generator=g)
@@ -69,13 +70,14 @@ def test_persistent_scoring_sampled_rows(xa, case):
     nbq = Mq // block
     np.testing.assert_allclose(got_all.sum(axis=-1), 1.0, rtol=1e-4)
     rng = np.random.default_rng(7)
-    rows = {(0, 0), (Hq - 1, nbq - 1)}
-    rows |= {(int(h), int(i)) for h, i in zip(rng.integers(0, Hq, 10), rng.integers(0, nbq, 10))}
+    rows = {(0, 0, 0), (B - 1, Hq - 1, nbq - 1)}
+    rows |= {(int(b), int(h), int(i)) for b, h, i in
+             zip(rng.integers(0, B, 10), rng.integers(0, Hq, 10), rng.integers(0, nbq, 10))}
     G = Hq // Hkv
-    for h, big_i in sorted(rows):
-        ref = oracle.block_score_row(f64(q[0, h]), f64(k[0, h // G]), big_i, block, stride, ss, causal,
+    for b, h, big_i in sorted(rows):
+        ref = oracle.block_score_row(f64(q[b, h]), f64(k[b, h // G]), big_i, block, stride, ss, causal,
                                      pattern=pattern)
-        got = got_all[0, h, big_i]
+        got = got_all[b, h, big_i]
         bad = np.abs(got - ref) > score_tol(ref)
-        assert not bad.any(), (h, big_i, np.nonzero(bad)[0][:5], np.abs(got - ref).max())
+        assert not bad.any(), (b, h, big_i, np.nonzero(bad)[0][:5], np.abs(got - ref).max())
     print(f"[persistent] {_ids(case)}: {len(rows)} rows within tolerance", flush=True)
